@@ -1,0 +1,360 @@
+"""Pins for the CPU oracle (CPU only, no GPU).
+
+The oracle is the plain definition of the SwiGLU gated-MLP product
+Y = SiLU(A x W1) (.) (A x W2) ("Tile-Level Activation Overlap for Efficient LLM
+Inference", gist.science technical summary, "Problem Statement"), accumulated
+in fp32 and rounded once to bf16.  None of these checks compares the oracle with
+a retyped copy of itself: they compare it with fp64 brute force under a
+closed-form rounding-error bound, with exact integer arithmetic, with closed
+forms of SiLU, with a hand-derived rounding table, with an independent library
+rounding routine, and with invariants that follow from the definition.
+``test_oracle_mutants.py`` plants plausible mistakes in a copy of the oracle and
+shows that these pins catch each one.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from swiglu_gated_mlp_amd import inputs
+
+U32 = 2.0 ** -24          # unit roundoff of fp32
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bits(t):
+    return inputs.as_bits(t)
+
+
+def f32(b):
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def gamma(n):
+    """Higham's gamma_n = n u / (1 - n u): bound on the relative error of a
+    recursive sum of n+1 terms in fp32 (Higham, Accuracy and Stability of
+    Numerical Algorithms, 2nd ed., eq. 3.4 / Lemma 3.1)."""
+    return n * U32 / (1.0 - n * U32)
+
+
+def silu64(x):
+    return x / (1.0 + np.exp(-x))
+
+
+# ---------------------------------------------------------------------------
+# Rounding to bf16
+# ---------------------------------------------------------------------------
+
+def load_rne_table():
+    rows = []
+    with open(os.path.join(GOLDEN, "bf16_rne_table.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            a, b = line.split()[:2]
+            rows.append((int(a, 16), int(b, 16)))
+    return rows
+
+
+def check_rne_table(orc):
+    rows = load_rne_table()
+    src = np.array([r[0] for r in rows], dtype=np.uint32).view(np.float32)
+    got = orc.bf16_rne(src)
+    want = np.array([r[1] for r in rows], dtype=np.uint16)
+    bad = [(hex(r[0]), hex(int(g)), hex(r[1])) for r, g in zip(rows, got) if int(g) != r[1]]
+    assert not bad, "rounding table mismatches (fp32, got, want): %s" % bad
+    return got, want
+
+
+def test_rne_hand_table(orc):
+    check_rne_table(orc)
+
+
+def check_rne_vs_torch(orc, n=200000, seed=5):
+    """torch's float->bfloat16 conversion is an independent round-to-nearest-even
+    implementation; agree on random finite values and on constructed ties."""
+    rng = np.random.default_rng(seed)
+    raw = rng.integers(0, 2 ** 32, size=n, dtype=np.uint64).astype(np.uint32)
+    ties = (rng.integers(0, 2 ** 16, size=n // 4, dtype=np.uint64).astype(np.uint32) << 16) | 0x8000
+    allb = np.concatenate([raw, ties])
+    vals = allb.view(np.float32)
+    finite = np.isfinite(vals)
+    vals = vals[finite]
+    got = orc.bf16_rne(vals)
+    want = torch.from_numpy(vals.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    mism = np.nonzero(got != want)[0]
+    assert mism.size == 0, "disagrees with torch on %d values, e.g. %s" % (
+        mism.size, [hex(int(v)) for v in vals[mism[:5]].view(np.uint32)])
+
+
+def test_rne_matches_independent_library(orc):
+    check_rne_vs_torch(orc)
+
+
+def test_rne_nan_never_inf(orc):
+    rng = np.random.default_rng(1)
+    frac = rng.integers(1, 2 ** 23, size=5000, dtype=np.uint64).astype(np.uint32)
+    sign = rng.integers(0, 2, size=5000, dtype=np.uint64).astype(np.uint32) << 31
+    nans = (sign | 0x7F800000 | frac).view(np.float32)
+    y = orc.bf16_rne(nans)
+    assert np.all((y & 0x7F80) == 0x7F80) and np.all((y & 0x007F) != 0), "NaN rounded to a non-NaN"
+    assert np.all((y & 0x0040) != 0), "NaN not quiet"
+    assert np.all((y >> 15) == (nans.view(np.uint32) >> 31)), "NaN sign lost"
+
+
+# ---------------------------------------------------------------------------
+# SiLU closed forms
+# ---------------------------------------------------------------------------
+
+def silu_min_point():
+    """x* with x + 1 + e^x = 0 (Newton in fp64), where SiLU has its minimum
+    and SiLU(x*) = x* + 1 because sigmoid(x*) = (x* + 1) / x*."""
+    x = -1.3
+    for _ in range(60):
+        f = x + 1.0 + math.exp(x)
+        x -= f / (1.0 + math.exp(x))
+    return x
+
+
+def check_silu_closed_forms(orc):
+    s0 = orc.silu(np.array([0.0, -0.0], dtype=np.float32))
+    assert s0[0] == 0.0 and s0[1] == 0.0, "SiLU(0) != 0"
+    # odd part: SiLU(x) - SiLU(-x) = x
+    x = np.linspace(1e-3, 60.0, 20001, dtype=np.float32)
+    d = orc.silu(x).astype(np.float64) - orc.silu(-x).astype(np.float64)
+    assert np.all(np.abs(d - x) <= 4 * 2.0 ** -23 * np.abs(x) + 1e-37), "SiLU(x)-SiLU(-x) != x"
+    # minimum
+    xs = silu_min_point()
+    assert abs(xs - (-1.2784645427610738)) < 1e-12
+    smin = float(orc.silu(np.array([xs], dtype=np.float32))[0])
+    assert abs(smin - (xs + 1.0)) <= 2 * 2.0 ** -24 * 2 + 1e-9
+    grid = np.linspace(-20.0, 20.0, 400001, dtype=np.float32)
+    assert orc.silu(grid).min() >= (xs + 1.0) - 4 * 2.0 ** -24, "SiLU dips below its minimum"
+    # saturation: 1 + e^-x rounds to 1 for x >= 17, so SiLU(x) == x
+    big = np.concatenate([np.linspace(17.0, 1000.0, 5000, dtype=np.float32),
+                          np.array([1e10, 3e38], dtype=np.float32)])
+    assert np.array_equal(orc.silu(big), big), "SiLU(x) != x for x >= 17"
+    # overflow of e^-x: SiLU(x) == -0 for x < -88.8
+    neg = np.linspace(-1e4, -88.8, 5000, dtype=np.float32)
+    sn = orc.silu(neg)
+    assert np.all(sn.view(np.uint32) == 0x80000000), "SiLU(x) != -0 for x < -88.8"
+    # against fp64 in the normal range
+    g = np.linspace(-60.0, 60.0, 240001, dtype=np.float32)
+    ref = silu64(g.astype(np.float64))
+    got = orc.silu(g).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 6 * U32 * np.abs(ref) + 1e-38), "SiLU off by > 6 ulp"
+
+
+def test_silu_closed_forms(orc):
+    check_silu_closed_forms(orc)
+
+
+# ---------------------------------------------------------------------------
+# fp64 brute force with a rounding-error bound
+# ---------------------------------------------------------------------------
+
+TINY_MN = (1, 2, 3, 7, 16, 33)
+TINY_K = (1, 2, 8, 64, 100, 257)
+
+
+def bound_check(Ab, W1b, W2b, Y, G, U, unfused_rounding=False):
+    """Assert the oracle's fp32 G, U and bf16 Y lie within the closed-form
+    rounding-error bound of the exact (fp64) values.
+
+    |g32 - g| <= gamma_{K-1} * sum_k |a_k w_k| (recursive summation), SiLU' is
+    at most 1.0999 in magnitude, SiLU in fp32 is within 8u relative, the fp32
+    product adds u, and the final RNE to bf16 adds at most 2^-8 relative."""
+    a = f32(Ab).astype(np.float64)
+    w1 = f32(W1b).astype(np.float64)
+    w2 = f32(W2b).astype(np.float64)
+    K = a.shape[1]
+    g64 = a @ w1
+    u64 = a @ w2
+    ag = np.abs(a) @ np.abs(w1)
+    au = np.abs(a) @ np.abs(w2)
+    dg = gamma(max(K - 1, 0)) * ag + 1e-300
+    du = gamma(max(K - 1, 0)) * au + 1e-300
+    if G is not None:
+        assert np.all(np.abs(G.astype(np.float64) - g64) <= dg), "Gate outside the summation bound"
+        assert np.all(np.abs(U.astype(np.float64) - u64) <= du), "Up outside the summation bound"
+    if unfused_rounding:
+        dg = dg + 2.0 ** -8 * (np.abs(g64) + dg)
+        du = du + 2.0 ** -8 * (np.abs(u64) + du)
+    s64 = silu64(g64)
+    y64 = s64 * u64
+    E = (1.0999 * dg + 8 * U32 * np.abs(s64)) * (np.abs(u64) + du) + np.abs(s64) * du \
+        + 2 * U32 * np.abs(y64) + 1e-38
+    y = f32(Y).astype(np.float64)
+    err = np.abs(y - y64)
+    lim = 2.0 ** -8 * (np.abs(y64) + E) + E + 1e-38
+    bad = np.argwhere(err > lim)
+    assert bad.size == 0, "Y outside the bound at %s: got %r want %r lim %r" % (
+        bad[:3].tolist(), y[tuple(bad[0])], y64[tuple(bad[0])], lim[tuple(bad[0])])
+
+
+def check_bruteforce(orc, shapes=None):
+    shapes = shapes or [(m, k, n) for m in TINY_MN for k in TINY_K for n in (1, 7, 33)]
+    for idx, (m, k, n) in enumerate(shapes):
+        A, W1, W2 = inputs.gaussian_case(m, k, n, seed=idx)
+        Y, P, G, U = orc.swiglu(A, W1, W2, want_p=True, want_gu=True)
+        bound_check(bits(A), bits(W1), bits(W2), Y, G, U)
+        assert np.array_equal(orc.bf16_rne(P), Y)
+
+
+def test_bruteforce_fp64_bound(orc):
+    check_bruteforce(orc)
+
+
+def test_bruteforce_fp64_bound_rectangular(orc):
+    shapes = [(m, k, n) for m in (1, 16, 33) for k in (8, 257) for n in TINY_MN]
+    check_bruteforce(orc, shapes)
+
+
+def test_accumulation_order_is_increasing_k(orc):
+    """The oracle documents a sequential increasing-k fp32 sum; cross-check it
+    against an explicit numpy fp32 running sum on a shape where order matters
+    (large-magnitude cancellation)."""
+    A, W1, W2 = inputs.gaussian_case(3, 64, 5, seed=3)
+    a, w = f32(bits(A)), f32(bits(W1))
+    G = orc.gemm_f32(bits(A), bits(W1))
+    ref = np.zeros((3, 5), dtype=np.float32)
+    for k in range(64):
+        ref = (ref + (a[:, k:k + 1] * w[k:k + 1, :]).astype(np.float32)).astype(np.float32)
+    assert np.array_equal(G, ref)
+
+
+# ---------------------------------------------------------------------------
+# Exact regimes
+# ---------------------------------------------------------------------------
+
+def check_integer_regime(orc, M=9, K=200, N=13, seed=0):
+    """Integer inputs: Gate and Up are exact integers (every partial sum is far
+    below 2^24), Gate >= K >= 17 so SiLU(Gate) == Gate exactly, and Y is the
+    RNE of fp32(Gate*Up).  The expected value comes from Python integers and
+    torch's independent bf16 conversion."""
+    A, W1, W2 = inputs.integer_case(M, K, N, seed)
+    a = f32(bits(A)).astype(np.int64)
+    w1 = f32(bits(W1)).astype(np.int64)
+    w2 = f32(bits(W2)).astype(np.int64)
+    g = a @ w1
+    u = a @ w2
+    assert g.min() >= 17
+    p = (g * u).astype(np.float64).astype(np.float32)     # exact int -> fp64 -> fp32 RNE
+    want = torch.from_numpy(p).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    Y, G, U = orc.swiglu(A, W1, W2, want_gu=True)
+    assert np.array_equal(G, g.astype(np.float32)) and np.array_equal(U, u.astype(np.float32))
+    assert np.array_equal(Y, want)
+
+
+def test_integer_regime_exact(orc):
+    for s, (m, k, n) in enumerate([(9, 200, 13), (1, 17, 8), (33, 96, 40)]):
+        check_integer_regime(orc, m, k, n, seed=s)
+
+
+def test_overflow_regime_all_zero(orc):
+    """Gate <= -K <= -96 makes e^-Gate overflow: SiLU(Gate) = -0, so Y = +-0."""
+    A, W1, W2 = inputs.integer_case(7, 96, 11, seed=4, w1_vals=(-3, -2, -1))
+    Y = orc.swiglu(A, W1, W2)
+    assert np.all((Y & 0x7FFF) == 0)
+
+
+# ---------------------------------------------------------------------------
+# Invariants of the definition
+# ---------------------------------------------------------------------------
+
+def check_invariants(orc, M=6, K=40, N=24):
+    A, W1, W2 = inputs.gaussian_case(M, K, N, seed=21)
+    Ab, W1b, W2b = bits(A), bits(W1), bits(W2)
+    Y = orc.swiglu(Ab, W1b, W2b)
+    # W1 = 0 -> Gate = 0 -> SiLU = 0 -> Y = 0
+    z = np.zeros_like(W1b)
+    assert np.all(f32(orc.swiglu(Ab, z, W2b)) == 0.0), "W1 = 0 must give Y = 0"
+    # a zero column of W2 gives a zero output column
+    W2z = W2b.copy()
+    W2z[:, 5] = 0
+    Yz = orc.swiglu(Ab, W1b, W2z)
+    assert np.all(f32(Yz[:, 5]) == 0.0), "zero W2 column must give zero Y column"
+    assert np.array_equal(np.delete(Yz, 5, axis=1), np.delete(Y, 5, axis=1))
+    # one-hot row of A selects the weight rows exactly
+    Ah = Ab.copy()
+    Ah[2, :] = 0
+    Ah[2, 17] = 0x3F80      # 1.0
+    Yh, G, U = orc.swiglu(Ah, W1b, W2b, want_gu=True)
+    assert np.array_equal(G[2], f32(W1b[17])) and np.array_equal(U[2], f32(W2b[17])), \
+        "one-hot row must select W1[k,:], W2[k,:]"
+    # joint column permutation permutes the output columns (bitwise)
+    perm = np.random.default_rng(3).permutation(N)
+    assert np.array_equal(orc.swiglu(Ab, W1b[:, perm], W2b[:, perm]), Y[:, perm])
+    # row independence: a prefix of rows gives the prefix of the output
+    assert np.array_equal(orc.swiglu(Ab[:3], W1b, W2b), Y[:3])
+    # W2 -> 2 W2 doubles Y exactly (power-of-two scaling commutes with rounding)
+    W2d = orc.bf16_rne(2.0 * f32(W2b))
+    assert np.array_equal(f32(orc.swiglu(Ab, W1b, W2d)), 2.0 * f32(Y))
+    # Gate and Up are not interchangeable
+    assert not np.array_equal(orc.swiglu(Ab, W2b, W1b), Y), "swapping W1 and W2 must change Y"
+
+
+def test_invariants(orc):
+    check_invariants(orc)
+
+
+def test_empty_shapes(orc):
+    A, W1, W2 = inputs.gaussian_case(0, 16, 8, seed=0)
+    assert orc.swiglu(A, W1, W2).shape == (0, 8)
+    Y = orc.swiglu(*inputs.gaussian_case(3, 0, 8, seed=0))      # K = 0: empty sums
+    assert np.all(f32(Y) == 0.0)
+
+
+# ---------------------------------------------------------------------------
+# The unfused pipeline
+# ---------------------------------------------------------------------------
+
+def check_unfused(orc):
+    for idx, (m, k, n) in enumerate([(5, 64, 9), (16, 257, 33), (1, 8, 7)]):
+        A, W1, W2 = inputs.gaussian_case(m, k, n, seed=100 + idx)
+        Gb, Ub, Y = orc.unfused(A, W1, W2)
+        # each stored intermediate is the RNE of the fp32 accumulator
+        assert np.array_equal(Gb, orc.bf16_rne(orc.gemm_f32(bits(A), bits(W1))))
+        assert np.array_equal(Ub, orc.bf16_rne(orc.gemm_f32(bits(A), bits(W2))))
+        bound_check(bits(A), bits(W1), bits(W2), Y, None, None, unfused_rounding=True)
+    # when Gate and Up are exact in bf16 the two pipelines agree bitwise
+    A, W1, W2 = inputs.integer_case(12, 8, 10, seed=9, a_vals=(0, 1), w1_vals=(-1, 0, 1),
+                                    w2_vals=(-2, -1, 0, 1, 2))
+    assert np.array_equal(orc.unfused(A, W1, W2)[2], orc.swiglu(A, W1, W2))
+
+
+def test_unfused_pipeline(orc):
+    check_unfused(orc)
+
+
+def test_activation_before_reduction_matters(orc):
+    """SiLU is nonlinear, so partial sums over K must be reduced before it:
+    SiLU(g1) u1 + SiLU(g2) u2 differs from SiLU(g1 + g2)(u1 + u2)."""
+    A, W1, W2 = inputs.gaussian_case(4, 64, 16, seed=44)
+    Ab, W1b, W2b = bits(A), bits(W1), bits(W2)
+    full = f32(orc.swiglu(Ab, W1b, W2b)).astype(np.float64)
+    halves = sum(f32(orc.swiglu(np.ascontiguousarray(Ab[:, s]), np.ascontiguousarray(W1b[s]),
+                                np.ascontiguousarray(W2b[s]))).astype(np.float64)
+                 for s in (slice(0, 32), slice(32, 64)))
+    assert np.max(np.abs(full - halves)) > 0.1
+
+
+# ---------------------------------------------------------------------------
+# Input recipe
+# ---------------------------------------------------------------------------
+
+def test_input_recipe_statistics():
+    w = inputs.WORKLOADS[0]
+    A, W1, W2 = inputs.workload_tensors(w)
+    assert A.dtype == torch.bfloat16 and A.shape == (64, 896) and W1.shape == (896, 4864)
+    assert abs(float(A.float().std()) - 1.0) < 0.02
+    assert abs(float(W1.float().std()) * math.sqrt(896) - 1.0) < 0.01
+    A2, _, _ = inputs.workload_tensors(w)
+    assert torch.equal(A.view(torch.int16), A2.view(torch.int16)), "inputs must be seeded"
+    d = inputs.WORKLOADS[2]
+    a16, _, _ = inputs.workload_tensors(d, 16)
+    a1, _, _ = inputs.workload_tensors(d, 1)
+    assert torch.equal(a16[:1].view(torch.int16), a1.view(torch.int16)), "decode rows share a prefix"
