@@ -1,0 +1,240 @@
+"""Benchmark of the fused SwiGLU gated-MLP product on one MI355X.
+
+One step = one call of the whole hot path (swiglu_fused_packed: the fused
+Gate/Up MFMA GEMM with the SiLU * Up epilogue) over one batch of synthetic,
+seeded input already resident in HBM.  The weights are packed once before the
+timed region, as a model-load step.
+
+Prints ONE JSON line (metric, value, ..., roofline, cpu_baseline).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--m M]
+                    [--variant auto|data_parallel|split_k] [--no-cpu] [--all]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 (256 CU x 4096 flop/clk x 2.4 GHz)
+HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
+MALL_BYTES = 256 << 20
+DEFAULT_WORKLOAD = "qwen2.5-0.5B-prefill"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def flops(M, K, N):
+    return 4.0 * M * K * N
+
+
+def fused_bytes(M, K, N):
+    """Algorithmic HBM bytes of the fused product: read A and both weights once,
+    write Y once (bf16)."""
+    return 2.0 * (M * K + 2 * K * N + M * N)
+
+
+def unfused_extra_bytes(M, K, N):
+    """Extra bytes of the unfused pipeline: write+read Gate and Up, re-read A."""
+    return 8.0 * M * N + 2.0 * M * K
+
+
+def bound_of(M, K, N):
+    ai = flops(M, K, N) / fused_bytes(M, K, N)
+    return "mfma" if ai >= MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
+
+
+def rotation_count(M, K, N):
+    """Rotated input/output sets so consecutive launches never hit in the
+    256 MiB last-level cache: twice its size in total."""
+    return max(1, math.ceil(2 * MALL_BYTES / fused_bytes(M, K, N)))
+
+
+def time_gpu(fn_list, steps, warmup, stream):
+    """Run fn_list[i % R]() for warmup + steps; time the steps with HIP events
+    recorded on the launch stream.  Returns total seconds for `steps`."""
+    import torch
+    R = len(fn_list)
+    for i in range(warmup):
+        fn_list[i % R]()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        fn_list[i % R]()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / 1e3
+
+
+def cpu_baseline(w, M, target_s=12.0):
+    """Time the CPU oracle (as it stands) on the first rows of the same workload:
+    a few rows first to estimate the rate, then enough rows for ~target_s."""
+    import oracle
+    from swiglu_gated_mlp_amd import inputs
+    threads = min(len(os.sched_getaffinity(0)), 16)
+    oracle.set_threads(threads)
+    A, W1, W2 = inputs.workload_tensors(w, M)
+    Ab, W1b, W2b = inputs.as_bits(A), inputs.as_bits(W1), inputs.as_bits(W2)
+    m0 = min(M, max(1, threads))
+    t0 = time.perf_counter()
+    oracle.swiglu(Ab[:m0], W1b, W2b)
+    dt = time.perf_counter() - t0
+    m = int(min(M, max(m0, m0 * target_s / max(dt, 1e-6))))
+    m = max(threads, (m // threads) * threads) if m >= threads else m
+    m = min(m, M)
+    t0 = time.perf_counter()
+    oracle.swiglu(Ab[:m], W1b, W2b)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(flops(m, w.K, w.N) / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(oracle.max_threads()),
+        "kind": "oracle",
+        "sample": "first %d of %d rows of A, all %d columns (K=%d); %.1f s" % (m, M, w.N, w.K, dt),
+    }
+
+
+def bench_point(w, M, steps, warmup, variant, stream):
+    import torch
+    import swiglu_gated_mlp_amd as sw
+    from swiglu_gated_mlp_amd import inputs
+    dev = torch.device("cuda:0")
+    K, N = w.K, w.N
+    A, W1, W2 = inputs.workload_tensors(w, M)
+    W1d, W2d = W1.to(dev), W2.to(dev)
+    R = rotation_count(M, K, N)
+    sets = []
+    for r in range(R):
+        Wp = sw.swiglu_pack_weights(W1d, W2d)
+        Ad = A.to(dev)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = sw.Workspace(dev)
+        sets.append((Ad, Wp, Y, ws))
+    del W1d, W2d
+    torch.cuda.synchronize()
+    v = sw.VARIANTS[variant]
+    fns = [(lambda s=s: sw.swiglu_fused_packed(s[0], s[1], N, Y=s[2], workspace=s[3], variant=v))
+           for s in sets]
+    sec = time_gpu(fns, steps, warmup, stream)
+    per = sec / steps
+    return {
+        "M": M, "K": K, "N": N, "rotation": R, "seconds": sec, "per_launch_s": per,
+        "tflops": flops(M, K, N) / per / 1e12,
+        "gbs": fused_bytes(M, K, N) / per / 1e9,
+        "variant": variant, "resolved_variant": sw.swiglu_choose_variant(M, K, N) if v == 0 else v,
+    }
+
+
+def bench_unfused(w, M, steps, warmup, stream):
+    import torch
+    import swiglu_gated_mlp_amd as sw
+    from swiglu_gated_mlp_amd import inputs
+    dev = torch.device("cuda:0")
+    K, N = w.K, w.N
+    A, W1, W2 = inputs.workload_tensors(w, M)
+    Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
+    G = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    U = torch.empty_like(G)
+    Y = torch.empty_like(G)
+    fn = lambda: sw.swiglu_unfused(Ad, W1d, W2d, G, U, Y)  # noqa: E731
+    sec = time_gpu([fn], steps, warmup, stream)
+    return sec / steps
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--m", type=int, default=None, help="token count (default: the workload's largest)")
+    ap.add_argument("--variant", default="auto", choices=["auto", "data_parallel", "split_k"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--all", action="store_true",
+                    help="also time every workload point and the unfused pipeline (stderr)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build runs the fused SwiGLU product on a "
+              "single MI355X (no multi-GPU path); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import swiglu_gated_mlp_amd as sw
+    from swiglu_gated_mlp_amd import inputs
+    from swiglu_gated_mlp_amd import build as hip_build
+    if not os.path.exists(hip_build.LIB_PATH):
+        hip_build.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sw.lib()
+    stream = torch.cuda.current_stream()
+    w = inputs.BY_NAME[args.workload]
+    M = args.m or w.m_max
+
+    res = bench_point(w, M, args.steps, args.warmup, args.variant, stream)
+    per = res["per_launch_s"]
+    bound = bound_of(M, w.K, w.N)
+    if bound == "mfma":
+        achieved, peak, unit = res["tflops"], MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = res["gbs"], HBM_PEAK_GBS, "GB/s"
+
+    extra = {}
+    if args.all:
+        for ww in inputs.WORKLOADS:
+            for mm in ww.ms:
+                r = bench_point(ww, mm, max(10, args.steps // 2), 5, args.variant, stream)
+                tu = bench_unfused(ww, mm, max(5, args.steps // 4), 3, stream)
+                b = bound_of(mm, ww.K, ww.N)
+                frac = r["tflops"] / MFMA_BF16_PEAK_TFLOPS if b == "mfma" else r["gbs"] / HBM_PEAK_GBS
+                line = {"workload": ww.name, "M": mm, "K": ww.K, "N": ww.N, "bound": b,
+                        "us": round(r["per_launch_s"] * 1e6, 2), "tflops": round(r["tflops"], 2),
+                        "gbs": round(r["gbs"], 1), "frac": round(frac, 4),
+                        "unfused_us": round(tu * 1e6, 2),
+                        "speedup_vs_unfused": round(tu / r["per_launch_s"], 3),
+                        "resolved_variant": r["resolved_variant"]}
+                log("POINT " + json.dumps(line))
+                extra.setdefault("points", []).append(line)
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle on a sample of the workload ...")
+        cpu = cpu_baseline(w, M)
+
+    out = {
+        "metric": "fused SwiGLU TFLOP/s (bf16) at Qwen-2.5 shapes; % of MFMA/HBM roofline",
+        "value": round(res["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(per * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/K) weights)",
+        "config": {"workload": "%s M=%d K=%d N=%d" % (w.name, M, w.K, w.N), "M": M, "K": w.K,
+                   "N": w.N, "variant": args.variant, "rotation_sets": res["rotation"]},
+        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 5), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+/*
+ * swiglu.h -- C ABI of libswiglu.so, the fused SwiGLU gated-MLP product for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Citations name the pages about "Tile-Level Activation Overlap for Efficient
+ * LLM Inference": [Abstract] is the paper's abstract (paper-with-me page);
+ * [Summary: X] is section X of the gist.science technical summary.
+ *
+ * The operation ([Summary: Problem Statement]):
+ *
+ *     Y = SiLU(A x W1) (.) (A x W2),   SiLU(x) = x / (1 + e^-x)
+ *
+ * A [M,K], W1 [K,N], W2 [K,N], Y [M,N]; Gate = A x W1 is the operand SiLU is
+ * applied to, Up = A x W2 multiplies it.  Gate and Up are accumulated in fp32
+ * and never written to memory ([Abstract]; [Summary: Key Contributions],
+ * tile-level fusion); SiLU and the product are fp32; Y is rounded once to bf16,
+ * round-to-nearest-even.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Element type: swiglu_bf16 holds raw bf16 bit patterns.  Every matrix is
+ *    row-major and contiguous (leading dimension = number of columns).
+ *  - Pointers: all matrix pointers are DEVICE pointers (hipMalloc'd or torch
+ *    CUDA tensors) of the current HIP device, 16-byte aligned.
+ *  - Ownership: the caller owns every buffer.  The library allocates no memory
+ *    on any path and keeps no pointer after a call returns.
+ *  - Streams: `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *    enqueued and the call returns without synchronising; device-side faults
+ *    surface at the caller's next synchronisation.
+ *  - Shapes: M >= 0; K > 0 and N > 0 must be multiples of 8 (16-byte rows).
+ *    M == 0 is a valid empty call: SWIGLU_OK, nothing is launched.
+ *  - Aliasing: inputs may alias each other (W1 == W2 is legal).  Outputs must
+ *    not overlap any input or each other.
+ *  - Errors: argument errors are detected on the host before any HIP call and
+ *    leave every output untouched.  A failed launch returns SWIGLU_ERR_HIP and
+ *    swiglu_last_hip_error() gives the hipError_t (per calling thread).
+ *  - Thread safety: every entry point is re-entrant.  Calls on different
+ *    streams may overlap as long as their outputs and workspaces differ.
+ */
+#ifndef SWIGLU_H_
+#define SWIGLU_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SWIGLU_ABI_VERSION 1
+
+typedef uint16_t swiglu_bf16;
+
+typedef enum {
+    SWIGLU_OK = 0,
+    SWIGLU_ERR_NULL_POINTER = 1,      /* a required pointer is NULL (with M > 0)      */
+    SWIGLU_ERR_BAD_SHAPE = 2,         /* M < 0, K <= 0, N <= 0, or sizes overflow     */
+    SWIGLU_ERR_UNSUPPORTED_SHAPE = 3, /* K or N not a multiple of 8                   */
+    SWIGLU_ERR_MISALIGNED = 4,        /* a pointer is not 16-byte aligned             */
+    SWIGLU_ERR_ALIASING = 5,          /* an output overlaps an input or other output  */
+    SWIGLU_ERR_WORKSPACE = 6,         /* workspace missing or too small               */
+    SWIGLU_ERR_BAD_VARIANT = 7,       /* unknown variant, or one the shape can't use  */
+    SWIGLU_ERR_HIP = 8                /* a HIP call failed; see swiglu_last_hip_error */
+} swiglu_status;
+
+/* Schedules of the fused packed entry point.
+ *  DATA_PARALLEL: one workgroup per output tile, full K per tile; for large M
+ *                 (the pages' Kernel-1 regime, [Summary: Methodology] Kernel-1).
+ *  SPLIT_K:       the K range is split across workgroups; fp32 Gate/Up partials
+ *                 go through the workspace and are summed in fixed split order
+ *                 BEFORE SiLU; for small M, where output tiles alone cannot fill
+ *                 the GPU (the occupancy problem of [Summary: Methodology]
+ *                 Kernel-2, "Optimization").
+ *  DECODE:        M <= 64 only.  Weight streaming: one workgroup per 16 output
+ *                 columns reads their Gate and Up weight rows once, its waves
+ *                 split K and add their fp32 partials in LDS in fixed order
+ *                 BEFORE SiLU; needs no workspace.  The product is then bound
+ *                 by reading the weights from HBM.
+ *  AUTO:          the library picks from M, K, N and the device's CU count. */
+typedef enum {
+    SWIGLU_VARIANT_AUTO = 0,
+    SWIGLU_VARIANT_DATA_PARALLEL = 1,
+    SWIGLU_VARIANT_SPLIT_K = 2,
+    SWIGLU_VARIANT_DECODE = 3
+} swiglu_variant;
+
+/* Returns SWIGLU_ABI_VERSION. */
+int swiglu_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *swiglu_status_str(int status);
+
+/* hipError_t of the most recent SWIGLU_ERR_HIP on the calling thread (0 if none). */
+int swiglu_last_hip_error(void);
+
+/* Number of compute units of the current device as the library sees it
+ * (0 if it cannot be queried).  Host call; used by the schedule heuristic. */
+int swiglu_device_cu_count(void);
+
+/* ------------------------------------------------------------------------
+ * swiglu_fused -- Y = SiLU(A W1) (.) (A W2) from unpacked row-major weights.
+ * [Summary: Problem Statement] (definition); [Abstract] (tile-level fusion:
+ * Gate and Up stay in registers, only Y is written).
+ *   A  [M,K] bf16, W1 [K,N] bf16, W2 [K,N] bf16 (inputs, device)
+ *   Y  [M,N] bf16 (output, device; must not overlap A, W1, W2)
+ * Needs no workspace; always uses the data-parallel schedule.  The weights are
+ * transposed to K-contiguous order on the fly, tile by tile, in registers.
+ * ---------------------------------------------------------------------- */
+swiglu_status swiglu_fused(const swiglu_bf16 *A, const swiglu_bf16 *W1,
+                           const swiglu_bf16 *W2, swiglu_bf16 *Y, int64_t M,
+                           int64_t K, int64_t N, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Packed weights.  The pages build one fused weight matrix holding W1 and W2
+ * side by side before the GEMM runs ([Summary: Methodology] Kernel-2,
+ * "Strategy": W_fused in R^{K x 2N}).  Here the two are interleaved per tile
+ * of 128 output columns instead of per column, and stored K-contiguous:
+ *
+ *   Wp = for jt in 0 .. ceil(N/128)-1:            (output-column tile)
+ *          for kb in 0 .. ceil(K/64)-1:           (64-deep K block)
+ *            block[256][64]:                      (32 KiB)
+ *              row r <  128: W1[kb*64 + c, jt*128 + r]        for c in 0..63
+ *              row r >= 128: W2[kb*64 + c, jt*128 + r - 128]  for c in 0..63
+ *   Entries with k >= K or column >= N are zero.
+ *
+ * swiglu_packed_bytes: size of Wp in bytes for a K x N weight pair (0 if the
+ *   shape is invalid).
+ * swiglu_pack_weights: W1, W2 [K,N] -> Wp (device, swiglu_packed_bytes bytes).
+ *   One-time transform (model-load time); not part of the fused call.
+ * swiglu_unpack_weights: the inverse, Wp -> W1, W2 (for tests).
+ * ---------------------------------------------------------------------- */
+size_t swiglu_packed_bytes(int64_t K, int64_t N);
+swiglu_status swiglu_pack_weights(const swiglu_bf16 *W1, const swiglu_bf16 *W2,
+                                  swiglu_bf16 *Wp, int64_t K, int64_t N,
+                                  void *stream);
+swiglu_status swiglu_unpack_weights(const swiglu_bf16 *Wp, swiglu_bf16 *W1,
+                                    swiglu_bf16 *W2, int64_t K, int64_t N,
+                                    void *stream);
+
+/* ------------------------------------------------------------------------
+ * swiglu_fused_packed -- the same product from packed weights (the fast path).
+ * [Summary: Problem Statement] (definition); [Summary: Methodology] Kernel-2
+ * (one GEMM over the fused weight, SiLU(Gate) (.) Up applied to each pair of
+ * accumulators before the store).
+ *   A [M,K] bf16, Wp (swiglu_packed_bytes(K,N) bytes), Y [M,N] bf16 (device).
+ *   workspace: device scratch for SWIGLU_VARIANT_SPLIT_K (fp32 partials and
+ *     per-tile counters); may be NULL when swiglu_workspace_bytes() returns 0
+ *     for the chosen variant.  The counters must be zero before the FIRST use of
+ *     a workspace (hipMemset it once); every call leaves them zero again, so no
+ *     per-call clearing is needed.  Concurrent calls must not share a
+ *     workspace.
+ *   variant: a swiglu_variant; AUTO lets the library choose.
+ * swiglu_workspace_bytes: bytes of workspace the call needs for (M,K,N,variant)
+ *   (for AUTO: the requirement of the variant AUTO would pick).
+ * ---------------------------------------------------------------------- */
+size_t swiglu_workspace_bytes(int64_t M, int64_t K, int64_t N, int variant);
+swiglu_status swiglu_fused_packed(const swiglu_bf16 *A, const swiglu_bf16 *Wp,
+                                  swiglu_bf16 *Y, int64_t M, int64_t K, int64_t N,
+                                  void *workspace, size_t workspace_bytes,
+                                  int variant, void *stream);
+
+/* Variant AUTO resolves to for this shape on the current device. */
+int swiglu_choose_variant(int64_t M, int64_t K, int64_t N);
+
+/* ------------------------------------------------------------------------
+ * The unfused pipeline the pages measure against ([Summary: Problem
+ * Statement]: two GEMMs materialise Gate and Up in memory, then a separate
+ * element-wise activation reads them back; [Summary: Results]: "PyTorch
+ * eager" baseline), built from this library's own kernels.
+ *
+ * swiglu_gemm_bf16: C[M,N] = bf16_RNE(A[M,K] x W[K,N]), fp32 accumulation,
+ *   W row-major.  C must not overlap A or W.
+ * swiglu_silu_mul:  Y[i] = bf16_RNE(SiLU(G[i]) * U[i]) for i < count, fp32 math
+ *   from bf16 inputs; Y must not overlap G or U.  count >= 0, any value.
+ * swiglu_unfused:   G = gemm(A, W1); U = gemm(A, W2); Y = silu_mul(G, U).
+ *   G_scratch and U_scratch are caller-owned [M,N] bf16 device buffers.
+ * ---------------------------------------------------------------------- */
+swiglu_status swiglu_gemm_bf16(const swiglu_bf16 *A, const swiglu_bf16 *W,
+                               swiglu_bf16 *C, int64_t M, int64_t K, int64_t N,
+                               void *stream);
+swiglu_status swiglu_silu_mul(const swiglu_bf16 *G, const swiglu_bf16 *U,
+                              swiglu_bf16 *Y, int64_t count, void *stream);
+swiglu_status swiglu_unfused(const swiglu_bf16 *A, const swiglu_bf16 *W1,
+                             const swiglu_bf16 *W2, swiglu_bf16 *G_scratch,
+                             swiglu_bf16 *U_scratch, swiglu_bf16 *Y, int64_t M,
+                             int64_t K, int64_t N, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWIGLU_H_ */

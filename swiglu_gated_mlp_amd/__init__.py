@@ -1,0 +1,282 @@
+"""Python binding of libswiglu (the fused SwiGLU gated-MLP product on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libswiglu.so``; this module checks tensor types, allocates
+outputs with torch (device memory) and passes raw pointers plus the current
+torch stream through the C ABI declared in ``include/swiglu.h``.  The function
+names are the C entry points' names.  There is no fallback: if the library is
+missing or the device is not a GPU, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from . import inputs  # noqa: F401  (seeded input generators)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libswiglu.so")
+
+SWIGLU_OK = 0
+SWIGLU_ERR_HIP = 8
+VARIANT_AUTO = 0
+VARIANT_DATA_PARALLEL = 1
+VARIANT_SPLIT_K = 2
+VARIANT_DECODE = 3
+VARIANTS = {"auto": VARIANT_AUTO, "data_parallel": VARIANT_DATA_PARALLEL, "split_k": VARIANT_SPLIT_K,
+            "decode": VARIANT_DECODE}
+
+# Every entry point of include/swiglu.h with its ctypes signature.
+_I64 = ctypes.c_int64
+_P = ctypes.c_void_p
+SIGNATURES = {
+    "swiglu_abi_version": ([], ctypes.c_int),
+    "swiglu_status_str": ([ctypes.c_int], ctypes.c_char_p),
+    "swiglu_last_hip_error": ([], ctypes.c_int),
+    "swiglu_device_cu_count": ([], ctypes.c_int),
+    "swiglu_fused": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "swiglu_packed_bytes": ([_I64, _I64], ctypes.c_size_t),
+    "swiglu_pack_weights": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
+    "swiglu_unpack_weights": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
+    "swiglu_workspace_bytes": ([_I64, _I64, _I64, ctypes.c_int], ctypes.c_size_t),
+    "swiglu_fused_packed": ([_P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, ctypes.c_int, _P],
+                            ctypes.c_int),
+    "swiglu_choose_variant": ([_I64, _I64, _I64], ctypes.c_int),
+    "swiglu_gemm_bf16": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "swiglu_silu_mul": ([_P, _P, _P, _I64, _P], ctypes.c_int),
+    "swiglu_unfused": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class SwigluError(RuntimeError):
+    def __init__(self, fn: str, status: int, hip_error: int = 0):
+        msg = "%s failed: %s (status %d)" % (fn, status_str(status), status)
+        if status == SWIGLU_ERR_HIP:
+            msg += ", hipError_t %d" % hip_error
+        super().__init__(msg)
+        self.status = status
+        self.hip_error = hip_error
+
+
+def lib():
+    """The loaded libswiglu (ctypes.CDLL).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError("libswiglu.so is not built (%s); run "
+                                   "`python -m swiglu_gated_mlp_amd.build`" % LIB_PATH)
+            handle = ctypes.CDLL(LIB_PATH)
+            for name, (argt, rest) in SIGNATURES.items():
+                fn = getattr(handle, name)
+                fn.argtypes = argt
+                fn.restype = rest
+            _lib = handle
+        return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().swiglu_status_str(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != SWIGLU_OK:
+        raise SwigluError(fn, status, lib().swiglu_last_hip_error() if status == SWIGLU_ERR_HIP else 0)
+
+
+def _dev_bf16(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if t.dtype != torch.bfloat16:
+        raise TypeError("%s must be bfloat16 (got %s)" % (name, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def swiglu_abi_version() -> int:
+    return int(lib().swiglu_abi_version())
+
+
+def swiglu_device_cu_count() -> int:
+    return int(lib().swiglu_device_cu_count())
+
+
+def swiglu_fused(A: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor, Y: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """Y = SiLU(A @ W1) * (A @ W2) from row-major weights; returns Y [M,N] bf16."""
+    M, K = A.shape
+    N = W1.shape[1]
+    if W1.shape != (K, N) or W2.shape != (K, N):
+        raise ValueError("W1, W2 must be [K,N] = [%d,%d]" % (K, N))
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    st = lib().swiglu_fused(_dev_bf16(A, "A"), _dev_bf16(W1, "W1"), _dev_bf16(W2, "W2"),
+                            _dev_bf16(Y, "Y"), M, K, N, _stream(stream))
+    _check("swiglu_fused", st)
+    return Y
+
+
+def swiglu_packed_bytes(K: int, N: int) -> int:
+    return int(lib().swiglu_packed_bytes(K, N))
+
+
+def swiglu_pack_weights(W1: torch.Tensor, W2: torch.Tensor, Wp: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+    """Pack W1, W2 [K,N] into the per-128-column-tile interleaved layout."""
+    K, N = W1.shape
+    nbytes = swiglu_packed_bytes(K, N)
+    if nbytes == 0:
+        raise ValueError("invalid weight shape [%d,%d]" % (K, N))
+    if Wp is None:
+        Wp = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=W1.device)
+    elif Wp.numel() * Wp.element_size() < nbytes:
+        raise ValueError("Wp too small: need %d bytes" % nbytes)
+    st = lib().swiglu_pack_weights(_dev_bf16(W1, "W1"), _dev_bf16(W2, "W2"), _dev_bf16(Wp, "Wp"),
+                                   K, N, _stream(stream))
+    _check("swiglu_pack_weights", st)
+    return Wp
+
+
+def swiglu_unpack_weights(Wp: torch.Tensor, K: int, N: int, stream=None):
+    """Inverse of swiglu_pack_weights; returns (W1, W2)."""
+    W1 = torch.empty((K, N), dtype=torch.bfloat16, device=Wp.device)
+    W2 = torch.empty((K, N), dtype=torch.bfloat16, device=Wp.device)
+    st = lib().swiglu_unpack_weights(_dev_bf16(Wp, "Wp"), _dev_bf16(W1, "W1"), _dev_bf16(W2, "W2"),
+                                     K, N, _stream(stream))
+    _check("swiglu_unpack_weights", st)
+    return W1, W2
+
+
+def swiglu_workspace_bytes(M: int, K: int, N: int, variant: int = VARIANT_AUTO) -> int:
+    return int(lib().swiglu_workspace_bytes(M, K, N, int(variant)))
+
+
+def swiglu_choose_variant(M: int, K: int, N: int) -> int:
+    return int(lib().swiglu_choose_variant(M, K, N))
+
+
+class Workspace:
+    """Zero-initialised device scratch for the split-K schedule, grown on demand.
+
+    The library leaves its arrival counters at zero after every call, so a
+    workspace only needs clearing when it is (re)allocated.  One Workspace must
+    not be shared by calls that may run concurrently."""
+
+    def __init__(self, device=None):
+        self.device = torch.device(device or "cuda")
+        self.buf: torch.Tensor | None = None
+
+    def get(self, nbytes: int) -> torch.Tensor | None:
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+_default_ws: dict = {}
+
+
+def _workspace_for(device: torch.device, stream_handle: int) -> Workspace:
+    key = (device.index, stream_handle)
+    ws = _default_ws.get(key)
+    if ws is None:
+        ws = _default_ws[key] = Workspace(device)
+    return ws
+
+
+def swiglu_fused_packed(A: torch.Tensor, Wp: torch.Tensor, N: int, Y: torch.Tensor | None = None,
+                        workspace: torch.Tensor | Workspace | None = None, variant: int = VARIANT_AUTO,
+                        stream=None) -> torch.Tensor:
+    """Y = SiLU(A W1) * (A W2) from packed weights; returns Y [M,N] bf16.
+
+    ``workspace`` may be a zero-initialised uint8 tensor, a Workspace, or None
+    (a cached per-stream Workspace is used)."""
+    M, K = A.shape
+    if isinstance(variant, str):
+        variant = VARIANTS[variant]
+    s = _stream(stream)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    need = swiglu_workspace_bytes(M, K, N, variant)
+    if isinstance(workspace, Workspace):
+        ws = workspace.get(need)
+    elif workspace is None:
+        ws = _workspace_for(A.device, s).get(need)
+    else:
+        ws = workspace
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    if ws is not None and ws.device.type != "cuda":
+        raise ValueError("workspace must be a GPU tensor")
+    st = lib().swiglu_fused_packed(_dev_bf16(A, "A"), _dev_bf16(Wp, "Wp"), _dev_bf16(Y, "Y"), M, K, N,
+                                   _ptr(ws), ws_bytes, int(variant), s)
+    _check("swiglu_fused_packed", st)
+    return Y
+
+
+def swiglu_gemm_bf16(A: torch.Tensor, W: torch.Tensor, C: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """C = bf16(A @ W) with fp32 accumulation (one GEMM of the unfused pipeline)."""
+    M, K = A.shape
+    N = W.shape[1]
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    st = lib().swiglu_gemm_bf16(_dev_bf16(A, "A"), _dev_bf16(W, "W"), _dev_bf16(C, "C"), M, K, N,
+                                _stream(stream))
+    _check("swiglu_gemm_bf16", st)
+    return C
+
+
+def swiglu_silu_mul(G: torch.Tensor, U: torch.Tensor, Y: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """Y = bf16(SiLU(G) * U), element-wise (the unfused pipeline's activation)."""
+    if G.shape != U.shape:
+        raise ValueError("G and U shapes differ")
+    if Y is None:
+        Y = torch.empty_like(G)
+    st = lib().swiglu_silu_mul(_dev_bf16(G, "G"), _dev_bf16(U, "U"), _dev_bf16(Y, "Y"), G.numel(),
+                               _stream(stream))
+    _check("swiglu_silu_mul", st)
+    return Y
+
+
+def swiglu_unfused(A: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor, G: torch.Tensor | None = None,
+                   U: torch.Tensor | None = None, Y: torch.Tensor | None = None, stream=None):
+    """The unfused pipeline: G = A@W1, U = A@W2 (bf16, in memory), Y = SiLU(G)*U.
+    Returns (G, U, Y)."""
+    M, K = A.shape
+    N = W1.shape[1]
+    mk = lambda: torch.empty((M, N), dtype=torch.bfloat16, device=A.device)  # noqa: E731
+    G = mk() if G is None else G
+    U = mk() if U is None else U
+    Y = mk() if Y is None else Y
+    st = lib().swiglu_unfused(_dev_bf16(A, "A"), _dev_bf16(W1, "W1"), _dev_bf16(W2, "W2"),
+                              _dev_bf16(G, "G"), _dev_bf16(U, "U"), _dev_bf16(Y, "Y"), M, K, N,
+                              _stream(stream))
+    _check("swiglu_unfused", st)
+    return G, U, Y

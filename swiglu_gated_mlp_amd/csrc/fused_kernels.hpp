@@ -1,0 +1,592 @@
+// Device kernels of libswiglu: the fused SwiGLU GEMM, its split-K form, the
+// weight pack, and the unfused baseline's GEMM and element-wise SwiGLU.
+//
+// Citations name the pages about "Tile-Level Activation Overlap for Efficient
+// LLM Inference": [Abstract] is the paper's abstract (paper-with-me page);
+// [Summary: X] is section X of the gist.science technical summary.
+//
+// What is computed ([Summary: Problem Statement]):
+//     Y = SiLU(A x W1) (.) (A x W2)
+// Gate = A x W1 and Up = A x W2 are accumulated in fp32 registers, side by
+// side, for the SAME output positions of the same lanes, so SiLU(Gate) * Up is
+// a lane-local epilogue and neither intermediate is ever stored ([Abstract]:
+// tile-level fusion; [Summary: Key Contributions]: the four Gate/Up memory
+// operations disappear).
+//
+// gfx950 mapping (CDNA4, 64-wide wavefronts):
+//  * Matrix core op: v_mfma_f32_32x32x16_bf16.  The weight fragment is the
+//    first operand and the activation fragment the second, so the 32x32 fp32
+//    result holds rows = output columns n and columns = tokens m; each lane
+//    then owns four consecutive n of one token, which makes the Y store a
+//    single 8-byte write.
+//  * One LDS-staged A tile [BM x 64] is shared by the Gate and the Up weight
+//    tiles of the same K step (the Kernel-2 idea of one GEMM over a fused
+//    weight, [Summary: Methodology]); two LDS stages are double-buffered with
+//    a register prefetch of the next K step issued before the MFMAs of the
+//    current one.
+//  * LDS rows are 128 bytes (64 bf16 of K); 16-byte chunks are XOR-swizzled
+//    by swz(row) so the 16-byte-per-lane fragment reads of 8 or 16
+//    consecutive rows hit distinct banks.
+//  * Workgroup ids are remapped so each XCD (own L2) gets a contiguous run of
+//    output tiles, grouped along M so neighbours share weight panels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int BK = 64;             // K depth of one LDS stage (one 128-byte row)
+constexpr int PACK_BN = 128;       // output columns per packed weight tile
+constexpr int PACK_BK = 64;        // K depth per packed block
+constexpr int PACK_ROWS = 2 * PACK_BN;   // Gate rows then Up rows
+constexpr int NUM_XCD = 8;
+constexpr float LOG2E = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// element offset of 16-byte chunk c (0..7) of row r in an LDS tile [rows][64]
+__device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 3); }
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+// SiLU(g) = g * sigmoid(g) = g / (1 + 2^(-g log2 e)); v_exp_f32 and v_rcp_f32.
+// g -> -inf: the exponential overflows to +inf, rcp gives 0, result -0.
+// g >= 17: the exponential is below 2^-24, 1 + e rounds to 1, result g.
+__device__ __forceinline__ float silu_f(float g) {
+    const float e = __builtin_amdgcn_exp2f(-g * LOG2E);
+    return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+__device__ __forceinline__ unsigned bf16_bits(float x) {
+    __bf16 h = (__bf16)x;   // v_cvt_pk_bf16_f32: round to nearest even
+    return (unsigned)__builtin_bit_cast(unsigned short, h);
+}
+
+__device__ __forceinline__ unsigned pack2(float lo, float hi) {
+    return bf16_bits(lo) | (bf16_bits(hi) << 16);
+}
+
+// Map the hardware workgroup id to a logical id such that XCD x (which gets
+// ids x, x+8, x+16, ...) owns one contiguous range of logical ids.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+    const int q = total / NUM_XCD, r = total % NUM_XCD;
+    const int x = bid % NUM_XCD, j = bid / NUM_XCD;
+    return x * q + (x < r ? x : r) + j;
+}
+
+// 8x8 bf16 transpose: in[i] holds W[k+i][n..n+7]; out[j] gets W[k..k+7][n+j].
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int d = j >> 1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const unsigned lo = in[2 * q][d], hi = in[2 * q + 1][d];
+            out[j][q] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u))
+                                : ((lo & 0xFFFFu) | (hi << 16));
+        }
+    }
+}
+
+struct FusedArgs {
+    const uint16_t* A;    // [M,K]
+    const uint16_t* W1;   // [K,N] row-major, or the packed weights
+    const uint16_t* W2;   // [K,N] row-major (unused when packed)
+    uint16_t* Y;          // [M,N]
+    float* part;          // split-K partials (fp32)
+    unsigned* counters;   // split-K arrival counters, one per output tile
+    int M, K, N;
+    int tiles_m, tiles_n;
+    int splits;           // number of K splits (1 = none)
+    int kb_per_split;     // K blocks (of 64) per split
+    int KB;               // ceil(K / 64)
+};
+
+// ---------------------------------------------------------------------------
+// The fused (DUAL) / single-GEMM (!DUAL) tile kernel.
+//   BM x BN output tile per workgroup, WM x WN waves, each wave owning a
+//   (BM/WM) x (BN/WN) sub-tile as (BM/WM/32) x (BN/WN/32) MFMA 32x32 blocks,
+//   for Gate and for Up when DUAL.
+//   PACKED: weights come from the packed layout (K-contiguous rows), else from
+//   row-major [K,N] W1/W2 and are transposed in registers on the way to LDS.
+//   SPLIT: the workgroup covers kb_per_split K blocks; partial Gate/Up go to
+//   `part`, and the last workgroup of a tile to arrive sums the partials in
+//   split order 0..S-1 (before SiLU) and runs the epilogue.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, bool DUAL, bool PACKED, bool SPLIT>
+__global__ __launch_bounds__(64 * WM * WN) void fused_tile_kernel(FusedArgs p) {
+    constexpr int NT = 64 * WM * WN;
+    constexpr int NG = DUAL ? 2 : 1;          // accumulator groups (Gate, Up)
+    constexpr int NB = NG * BN;               // weight rows (n) per stage
+    constexpr int TM = BM / WM / 32;
+    constexpr int TN = BN / WN / 32;
+    constexpr int A_LD = BM * 8 / NT;         // 16-byte A chunks per thread per stage
+    constexpr int B_LD = NB * 8 / NT;         // 16-byte packed-weight chunks per thread
+    constexpr int B_BLK = NB / NT;            // 8x8 row-major weight blocks per thread
+    constexpr int GROUP_M = 8;
+    static_assert(TM >= 1 && TN >= 1, "tile too small for the wave grid");
+    static_assert(BM % (WM * 32) == 0 && BN % (WN * 32) == 0, "tile/wave mismatch");
+    static_assert(A_LD >= 1 && (BM * 8) % NT == 0, "A tile not evenly split");
+    static_assert(!PACKED || ((NB * 8) % NT == 0 && B_LD >= 1), "B tile not evenly split");
+    static_assert(PACKED || (NB % NT == 0 && B_BLK >= 1), "B tile not evenly split");
+    static_assert(!PACKED || DUAL, "packed weights hold a Gate/Up pair");
+    static_assert(!PACKED || (PACK_BN % BN == 0), "tile must divide the packed tile");
+
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + NB) * BK];
+    uint16_t* const sA0 = smem;
+    uint16_t* const sB0 = smem + BM * BK;
+    constexpr int STAGE = (BM + NB) * BK;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave % WM, wn = wave / WM;
+    const int wrow0 = wm * (BM / WM);
+    const int wcol0 = wn * (BN / WN);
+
+    // ---- which tile / split -----------------------------------------------
+    const int S = SPLIT ? p.splits : 1;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int tile = logical / S;
+    const int split = logical - tile * S;
+    int tm, tn;
+    {
+        const int per_group = GROUP_M * p.tiles_n;
+        const int group = tile / per_group;
+        const int first_m = group * GROUP_M;
+        const int gsize = min(p.tiles_m - first_m, GROUP_M);
+        const int in_group = tile - group * per_group;
+        tm = first_m + in_group % gsize;
+        tn = in_group / gsize;
+    }
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const int M = p.M, K = p.K, N = p.N;
+    const int kb_begin = SPLIT ? split * p.kb_per_split : 0;
+    const int kb_end = SPLIT ? min(p.KB, kb_begin + p.kb_per_split) : p.KB;
+
+    // ---- global -> register loaders ------------------------------------------
+    u32x4 ra[A_LD];
+    u32x4 rb[PACKED ? B_LD : 8 * B_BLK];
+
+    auto load_stage = [&](int kb) {
+        const int k0 = kb * BK;
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i) {
+            const int q = tid + i * NT;
+            const int row = q >> 3, c = q & 7;
+            const int grow = min(m0 + row, M - 1);
+            const int gk = k0 + c * 8;
+            ra[i] = gk < K ? ld16(p.A + (size_t)grow * K + gk) : u32x4{0u, 0u, 0u, 0u};
+        }
+        if constexpr (PACKED) {
+            const int jp = n0 / PACK_BN, ro = n0 % PACK_BN;
+            const uint16_t* blk = p.W1 + ((size_t)jp * p.KB + kb) * (PACK_ROWS * PACK_BK);
+#pragma unroll
+            for (int i = 0; i < B_LD; ++i) {
+                const int q = tid + i * NT;
+                const int row = q >> 3, c = q & 7;
+                const int prow = row < BN ? ro + row : PACK_BN + ro + (row - BN);
+                rb[i] = ld16(blk + prow * PACK_BK + c * 8);
+            }
+        } else {
+            constexpr int NGRP = NB / 8;
+#pragma unroll
+            for (int b = 0; b < B_BLK; ++b) {
+                const int blkid = tid + b * NT;
+                const int ng = blkid % NGRP, kc = blkid / NGRP;
+                const int nl = ng * 8;
+                const bool up = DUAL && nl >= BN;
+                const uint16_t* W = up ? p.W2 : p.W1;
+                const int ncol = min(n0 + (up ? nl - BN : nl), N - 8);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int gk = k0 + kc * 8 + i;
+                    rb[b * 8 + i] = gk < K ? ld16(W + (size_t)gk * N + ncol) : u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+        }
+    };
+
+    auto store_stage = [&](int buf) {
+        uint16_t* sA = sA0 + buf * STAGE;
+        uint16_t* sB = sB0 + buf * STAGE;
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i) {
+            const int q = tid + i * NT;
+            *reinterpret_cast<u32x4*>(sA + lds_off(q >> 3, q & 7)) = ra[i];
+        }
+        if constexpr (PACKED) {
+#pragma unroll
+            for (int i = 0; i < B_LD; ++i) {
+                const int q = tid + i * NT;
+                *reinterpret_cast<u32x4*>(sB + lds_off(q >> 3, q & 7)) = rb[i];
+            }
+        } else {
+            constexpr int NGRP = NB / 8;
+#pragma unroll
+            for (int b = 0; b < B_BLK; ++b) {
+                const int blkid = tid + b * NT;
+                const int ng = blkid % NGRP, kc = blkid / NGRP;
+                u32x4 in[8], out[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) in[i] = rb[b * 8 + i];
+                transpose8x8(in, out);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    *reinterpret_cast<u32x4*>(sB + lds_off(ng * 8 + j, kc)) = out[j];
+            }
+        }
+    };
+
+    // ---- accumulators -----------------------------------------------------------
+    f32x16 acc[NG][TM][TN];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[g][i][j][r] = 0.0f;
+
+    auto compute_stage = [&](int buf) {
+        const uint16_t* sA = sA0 + buf * STAGE;
+        const uint16_t* sB = sB0 + buf * STAGE;
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            const int c = 2 * kk + (lane >> 5);
+            bf16x8 af[TM];
+            bf16x8 bfr[NG][TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                af[i] = *reinterpret_cast<const bf16x8*>(sA + lds_off(wrow0 + i * 32 + (lane & 31), c));
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    bfr[g][j] = *reinterpret_cast<const bf16x8*>(
+                        sB + lds_off(g * BN + wcol0 + j * 32 + (lane & 31), c));
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[g][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[g][j], af[i],
+                                                                               acc[g][i][j], 0, 0, 0);
+        }
+    };
+
+    // ---- main loop: double-buffered LDS, register prefetch ------------------------
+    if (kb_begin < kb_end) {
+        load_stage(kb_begin);
+        store_stage(0);
+        __syncthreads();
+        for (int kb = kb_begin; kb < kb_end; ++kb) {
+            const int buf = (kb - kb_begin) & 1;
+            const bool more = kb + 1 < kb_end;
+            if (more) load_stage(kb + 1);
+            compute_stage(buf);
+            if (more) store_stage(buf ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // ---- split-K: publish partials, last arrival reduces ------------------------
+    if constexpr (SPLIT) {
+        constexpr int ACC = NG * TM * TN * 16;
+        if (S > 1) {
+            float* base = p.part + (size_t)tile * S * (ACC * NT);
+            float* mine = base + (size_t)split * (ACC * NT);
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const bool row_ok = m0 + wrow0 + i * 32 + (lane & 31) < M;
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int idx = ((g * TM + i) * TN + j) * 16 + r;
+                            if (row_ok) mine[(size_t)idx * NT + tid] = acc[g][i][j][r];
+                        }
+                }
+            __threadfence();
+            __syncthreads();
+            __shared__ unsigned s_last;
+            if (tid == 0) {
+                const unsigned prev = atomicAdd(p.counters + tile, 1u);
+                s_last = (prev == (unsigned)(S - 1)) ? 1u : 0u;
+            }
+            __syncthreads();
+            if (!s_last) return;
+            __threadfence();
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const bool row_ok = m0 + wrow0 + i * 32 + (lane & 31) < M;
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int idx = ((g * TM + i) * TN + j) * 16 + r;
+                            float v = 0.0f;
+                            if (row_ok) {
+                                for (int s = 0; s < S; ++s)
+                                    v += base[((size_t)s * ACC + idx) * NT + tid];
+                            }
+                            acc[g][i][j][r] = v;
+                        }
+                }
+            if (tid == 0) atomicExch(p.counters + tile, 0u);   // ready for the next call
+        }
+    }
+
+    // ---- epilogue: SiLU(Gate) * Up (or the plain GEMM value), bf16, store ---------
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int m = m0 + wrow0 + i * 32 + (lane & 31);
+        if (m >= M) continue;
+        uint16_t* yrow = p.Y + (size_t)m * N;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wcol0 + j * 32 + 8 * q + 4 * (lane >> 5);
+                if (n >= N) continue;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float g = acc[0][i][j][4 * q + e];
+                    if constexpr (DUAL) {
+                        const float u = acc[NG - 1][i][j][4 * q + e];
+                        v[e] = silu_f(g) * u;
+                    } else {
+                        v[e] = g;
+                    }
+                }
+                u32x2 out;
+                out[0] = pack2(v[0], v[1]);
+                out[1] = pack2(v[2], v[3]);
+                *reinterpret_cast<u32x2*>(yrow + n) = out;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode (small M): weight streaming.
+//   The product is bound by reading the packed weights once from HBM, so the
+//   kernel is shaped around keeping many 16-byte loads in flight, not around
+//   the matrix cores: each workgroup owns a group of 16 output columns (its 16
+//   Gate rows and 16 Up rows of every packed block), and its 4 waves take the
+//   K blocks round-robin (wave w: kb = w, w+4, ...).  Weight fragments go
+//   straight from HBM to registers -- every weight element is used once, so
+//   there is nothing to share through LDS -- and an MFMA 16x16x32 per
+//   (Gate|Up, 16-token tile) does the dot products (its cost is negligible
+//   next to the loads).  The four per-wave fp32 partial sums of Gate and Up
+//   are then added in LDS in wave order 0..3 (fixed order, BEFORE SiLU) and
+//   the epilogue applies SiLU(Gate) * Up.
+//   MT 16-token tiles cover M <= 16 * MT.
+// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct DecodeArgs {
+    const uint16_t* A;    // [M,K]
+    const uint16_t* Wp;   // packed weights
+    uint16_t* Y;          // [M,N]
+    int M, K, N;
+    int KB;               // ceil(K / 64)
+};
+
+template <int MT, int UNROLL>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
+    constexpr int WAVES = 4;
+    __shared__ f32x4 red[WAVES][MT][2][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int r16 = lane & 15;          // weight row within the group / token within a tile
+    const int kq = lane >> 4;           // which 8-wide K slice of a 32-deep step
+    const int n0 = blockIdx.x * 16;
+    const int jt = n0 / PACK_BN, ro = n0 % PACK_BN;
+    const int M = p.M, K = p.K, N = p.N, KB = p.KB;
+
+    const uint16_t* wg_base = p.Wp + (size_t)jt * KB * (PACK_ROWS * PACK_BK)
+                              + (size_t)(ro + r16) * PACK_BK + 8 * kq;
+    const uint16_t* wu_base = wg_base + (size_t)PACK_BN * PACK_BK;
+    const uint16_t* a_row[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) a_row[t] = p.A + (size_t)min(t * 16 + r16, M - 1) * K + 8 * kq;
+
+    f32x4 accg[MT], accu[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        accg[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accu[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    for (int kb0 = wave; kb0 < KB; kb0 += WAVES * UNROLL) {
+        u32x4 wg[UNROLL][2], wu[UNROLL][2], av[UNROLL][2][MT];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int kb = kb0 + u * WAVES;
+            if (kb < KB) {
+                const size_t boff = (size_t)kb * (PACK_ROWS * PACK_BK);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    wg[u][h] = ld16(wg_base + boff + 32 * h);
+                    wu[u][h] = ld16(wu_base + boff + 32 * h);
+                    const int k = kb * PACK_BK + 32 * h + 8 * kq;
+#pragma unroll
+                    for (int t = 0; t < MT; ++t)
+                        av[u][h][t] = k < K ? ld16(a_row[t] + (size_t)kb * PACK_BK + 32 * h)
+                                            : u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int kb = kb0 + u * WAVES;
+            if (kb < KB) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const bf16x8 g8 = __builtin_bit_cast(bf16x8, wg[u][h]);
+                    const bf16x8 u8 = __builtin_bit_cast(bf16x8, wu[u][h]);
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) {
+                        const bf16x8 a8 = __builtin_bit_cast(bf16x8, av[u][h][t]);
+                        accg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g8, a8, accg[t], 0, 0, 0);
+                        accu[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(u8, a8, accu[t], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        red[wave][t][0][lane] = accg[t];
+        red[wave][t][1][lane] = accu[t];
+    }
+    __syncthreads();
+    // epilogue: wave w finishes token tiles t = w, w+4, ...
+    for (int t = wave; t < MT; t += WAVES) {
+        f32x4 g = red[0][t][0][lane], u = red[0][t][1][lane];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) {
+            g += red[w][t][0][lane];
+            u += red[w][t][1][lane];
+        }
+        const int m = t * 16 + r16;
+        const int n = n0 + 4 * kq;
+        if (m < M && n < N) {
+            u32x2 out;
+            out[0] = pack2(silu_f(g[0]) * u[0], silu_f(g[1]) * u[1]);
+            out[1] = pack2(silu_f(g[2]) * u[2], silu_f(g[3]) * u[3]);
+            *reinterpret_cast<u32x2*>(p.Y + (size_t)m * N + n) = out;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Weight pack / unpack (one-time transforms; see the packed layout in swiglu.h).
+// One thread per 16-byte packed chunk (8 consecutive k of one packed row).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ W1,
+                                                   const uint16_t* __restrict__ W2,
+                                                   uint16_t* __restrict__ Wp, int K, int N,
+                                                   int KB, long long nchunks) {
+    const long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= nchunks) return;
+    const int c = (int)(q & 7);
+    const long long rowid = q >> 3;                 // packed row over all blocks
+    const int prow = (int)(rowid % PACK_ROWS);
+    const long long blk = rowid / PACK_ROWS;        // jt * KB + kb
+    const int kb = (int)(blk % KB);
+    const int jt = (int)(blk / KB);
+    const bool up = prow >= PACK_BN;
+    const int n = jt * PACK_BN + (up ? prow - PACK_BN : prow);
+    const uint16_t* W = up ? W2 : W1;
+    unsigned short v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int k = kb * PACK_BK + c * 8 + i;
+        v[i] = (n < N && k < K) ? W[(size_t)k * N + n] : (unsigned short)0;
+    }
+    u32x4 out;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) out[d] = (unsigned)v[2 * d] | ((unsigned)v[2 * d + 1] << 16);
+    *reinterpret_cast<u32x4*>(Wp + q * 8) = out;
+}
+
+__global__ __launch_bounds__(256) void unpack_kernel(const uint16_t* __restrict__ Wp,
+                                                     uint16_t* __restrict__ W1,
+                                                     uint16_t* __restrict__ W2, int K, int N,
+                                                     int KB, long long nchunks) {
+    const long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= nchunks) return;
+    const int c = (int)(q & 7);
+    const long long rowid = q >> 3;
+    const int prow = (int)(rowid % PACK_ROWS);
+    const long long blk = rowid / PACK_ROWS;
+    const int kb = (int)(blk % KB);
+    const int jt = (int)(blk / KB);
+    const bool up = prow >= PACK_BN;
+    const int n = jt * PACK_BN + (up ? prow - PACK_BN : prow);
+    if (n >= N) return;
+    uint16_t* W = up ? W2 : W1;
+    const u32x4 in = *reinterpret_cast<const u32x4*>(Wp + q * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int k = kb * PACK_BK + c * 8 + i;
+        if (k < K) W[(size_t)k * N + n] = (uint16_t)((in[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Element-wise SwiGLU of the unfused pipeline: Y = bf16(SiLU(G) * U), fp32 math.
+// 8 elements (16 bytes) per thread per step, grid-stride; scalar tail.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restrict__ G,
+                                                       const uint16_t* __restrict__ U,
+                                                       uint16_t* __restrict__ Y, long long count) {
+    const long long nvec = count / 8;
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    for (long long v = (long long)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
+        const u32x4 g = *reinterpret_cast<const u32x4*>(G + v * 8);
+        const u32x4 u = *reinterpret_cast<const u32x4*>(U + v * 8);
+        u32x4 y;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const float g0 = __builtin_bit_cast(float, g[d] << 16);
+            const float g1 = __builtin_bit_cast(float, g[d] & 0xFFFF0000u);
+            const float u0 = __builtin_bit_cast(float, u[d] << 16);
+            const float u1 = __builtin_bit_cast(float, u[d] & 0xFFFF0000u);
+            y[d] = pack2(silu_f(g0) * u0, silu_f(g1) * u1);
+        }
+        *reinterpret_cast<u32x4*>(Y + v * 8) = y;
+    }
+    const long long t = nvec * 8 + (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < count && blockIdx.x == 0 && (long long)threadIdx.x < count - nvec * 8) {
+        const float g0 = __builtin_bit_cast(float, (unsigned)G[t] << 16);
+        const float u0 = __builtin_bit_cast(float, (unsigned)U[t] << 16);
+        Y[t] = (uint16_t)bf16_bits(silu_f(g0) * u0);
+    }
+}
+
+}  // namespace swk

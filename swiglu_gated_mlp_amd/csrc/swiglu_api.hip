@@ -1,0 +1,433 @@
+// Host side of libswiglu: argument validation, schedule choice and kernel
+// launches behind the C ABI declared in include/swiglu.h.
+//
+// Every argument check runs before the first HIP call, so a rejected call has
+// no effect on the device and the checks work on a machine without a GPU.
+#include "swiglu.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+
+#include "fused_kernels.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+swiglu_status hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return SWIGLU_ERR_HIP;
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;   // every dimension fits int32 with room
+
+bool log_enabled() {
+    static int on = -1;
+    if (on < 0) {
+        const char* s = std::getenv("SWIGLU_LOG");
+        on = (s && s[0] && s[0] != '0') ? 1 : 0;
+    }
+    return on == 1;
+}
+
+// ---------------------------------------------------------------------------
+// argument checks (host only, no HIP calls)
+// ---------------------------------------------------------------------------
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+    return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes};
+}
+
+bool overlap(Range a, Range b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+swiglu_status check_shape(int64_t M, int64_t K, int64_t N) {
+    if (M < 0 || K <= 0 || N <= 0) return SWIGLU_ERR_BAD_SHAPE;
+    if (M > kMaxDim || K > kMaxDim || N > kMaxDim) return SWIGLU_ERR_BAD_SHAPE;
+    if (M * N > ((int64_t)1 << 40) || K * N > ((int64_t)1 << 40) || M * K > ((int64_t)1 << 40))
+        return SWIGLU_ERR_BAD_SHAPE;
+    if ((K % 8) != 0 || (N % 8) != 0) return SWIGLU_ERR_UNSUPPORTED_SHAPE;
+    return SWIGLU_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t packed_elems(int64_t K, int64_t N) {
+    return ceil_div(N, swk::PACK_BN) * ceil_div(K, swk::PACK_BK) * swk::PACK_ROWS * swk::PACK_BK;
+}
+
+// ---------------------------------------------------------------------------
+// device facts
+// ---------------------------------------------------------------------------
+int cu_count_now() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// ---------------------------------------------------------------------------
+// kernel configurations
+// ---------------------------------------------------------------------------
+struct TileCfg {
+    int BM, BN;
+};
+
+// Output tile height for a token count.  Small M keeps the MFMA waste and the
+// clamped-row reads low; large M takes the biggest tile the register file and
+// LDS allow (BM 256: each wave holds 128 rows x 64 columns of Gate and Up).
+TileCfg packed_tile_for(int64_t M) {
+    if (M <= 32) return {32, 128};
+    if (M <= 64) return {64, 128};
+    if (M <= 2048) return {128, 128};
+    return {256, 128};
+}
+
+// Split-K workspace = a fixed-size counter region, then the fp32 partials.
+// The counter region has the same size and place for every shape, so a
+// workspace that served one shape can serve another: each call leaves every
+// counter it used at zero, and no call ever writes partials over a counter.
+constexpr size_t kCounterBytes = 64 * 1024;
+constexpr int kMaxSplitTiles = (int)(kCounterBytes / sizeof(unsigned));
+
+struct Plan {
+    TileCfg t;
+    int tiles_m, tiles_n, tiles;
+    int splits, kb_per_split, KB;
+    int variant;   // resolved: DATA_PARALLEL, SPLIT_K or DECODE
+    int decode_mt; // DECODE: 16-token tiles per workgroup
+};
+
+constexpr int kDecodeMaxM = 64;
+bool variant_known(int v) { return v >= SWIGLU_VARIANT_AUTO && v <= SWIGLU_VARIANT_DECODE; }
+
+Plan make_plan(int64_t M, int64_t K, int64_t N, int variant, int cus) {
+    Plan p{};
+    p.t = packed_tile_for(M);
+    p.tiles_m = (int)ceil_div(M, p.t.BM);
+    p.tiles_n = (int)ceil_div(N, p.t.BN);
+    p.tiles = p.tiles_m * p.tiles_n;
+    p.KB = (int)ceil_div(K, swk::BK);
+    if (cus <= 0) cus = 256;
+    int v = variant;
+    if (v == SWIGLU_VARIANT_AUTO) {
+        if (M <= kDecodeMaxM)
+            v = SWIGLU_VARIANT_DECODE;
+        else
+            v = (p.tiles >= cus || p.KB < 4) ? SWIGLU_VARIANT_DATA_PARALLEL : SWIGLU_VARIANT_SPLIT_K;
+    }
+    p.variant = v;
+    p.decode_mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    if (v == SWIGLU_VARIANT_SPLIT_K && p.tiles <= kMaxSplitTiles) {
+        // about two workgroups per CU, at least two K blocks per split
+        int s = (int)ceil_div(2 * cus, p.tiles);
+        s = std::max(1, std::min(s, p.KB / 2 > 0 ? p.KB / 2 : 1));
+        p.kb_per_split = (int)ceil_div(p.KB, s);
+        p.splits = (int)ceil_div(p.KB, p.kb_per_split);
+    } else {
+        p.splits = 1;
+        p.kb_per_split = p.KB;
+    }
+    return p;
+}
+
+size_t split_workspace_bytes(const Plan& p) {
+    if (p.variant != SWIGLU_VARIANT_SPLIT_K || p.splits <= 1) return 0;
+    const size_t partials = (size_t)p.tiles * p.splits * 2 * p.t.BM * p.t.BN * sizeof(float);
+    return kCounterBytes + partials;
+}
+
+template <int BM, int BN, int WM, int WN, bool DUAL, bool PACKED, bool SPLIT>
+hipError_t launch_tile(const swk::FusedArgs& a, int grid, hipStream_t s) {
+    const void* fn = reinterpret_cast<const void*>(&swk::fused_tile_kernel<BM, BN, WM, WN, DUAL, PACKED, SPLIT>);
+    swk::FusedArgs args = a;
+    void* kargs[] = {&args};
+    return hipLaunchKernel(fn, dim3(grid), dim3(64 * WM * WN), kargs, 0, s);
+}
+
+template <int MT>
+hipError_t launch_decode(const swk::DecodeArgs& a, int groups, hipStream_t s) {
+    // K blocks per wave in flight: 4 for one token tile, 2 for more (their
+    // activation fragments take registers too)
+    constexpr int UNROLL = MT == 1 ? 4 : 2;
+    const void* fn = reinterpret_cast<const void*>(&swk::decode_kernel<MT, UNROLL>);
+    swk::DecodeArgs args = a;
+    void* kargs[] = {&args};
+    return hipLaunchKernel(fn, dim3(groups), dim3(256), kargs, 0, s);
+}
+
+hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) {
+    if (p.variant == SWIGLU_VARIANT_DECODE) {
+        swk::DecodeArgs d{};
+        d.A = a.A; d.Wp = a.W1; d.Y = a.Y;
+        d.M = a.M; d.K = a.K; d.N = a.N; d.KB = a.KB;
+        const int groups = (int)ceil_div(a.N, 16);
+        switch (p.decode_mt) {
+            case 1: return launch_decode<1>(d, groups, s);
+            case 2: return launch_decode<2>(d, groups, s);
+            default: return launch_decode<4>(d, groups, s);
+        }
+    }
+    const int grid = p.tiles * p.splits;
+    const bool split = p.splits > 1;
+    switch (p.t.BM) {
+        case 32:
+            return split ? launch_tile<32, 128, 1, 4, true, true, true>(a, grid, s)
+                         : launch_tile<32, 128, 1, 4, true, true, false>(a, grid, s);
+        case 64:
+            return split ? launch_tile<64, 128, 2, 2, true, true, true>(a, grid, s)
+                         : launch_tile<64, 128, 2, 2, true, true, false>(a, grid, s);
+        case 128:
+            return split ? launch_tile<128, 128, 2, 2, true, true, true>(a, grid, s)
+                         : launch_tile<128, 128, 2, 2, true, true, false>(a, grid, s);
+        default:
+            return split ? launch_tile<256, 128, 2, 2, true, true, true>(a, grid, s)
+                         : launch_tile<256, 128, 2, 2, true, true, false>(a, grid, s);
+    }
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+int swiglu_abi_version(void) { return SWIGLU_ABI_VERSION; }
+
+const char* swiglu_status_str(int s) {
+    switch (s) {
+        case SWIGLU_OK: return "ok";
+        case SWIGLU_ERR_NULL_POINTER: return "null pointer";
+        case SWIGLU_ERR_BAD_SHAPE: return "bad shape";
+        case SWIGLU_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (K and N must be multiples of 8)";
+        case SWIGLU_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+        case SWIGLU_ERR_ALIASING: return "output overlaps another operand";
+        case SWIGLU_ERR_WORKSPACE: return "workspace missing or too small";
+        case SWIGLU_ERR_BAD_VARIANT: return "unknown variant";
+        case SWIGLU_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+int swiglu_last_hip_error(void) { return g_last_hip_error; }
+
+int swiglu_device_cu_count(void) { return cu_count_now(); }
+
+size_t swiglu_packed_bytes(int64_t K, int64_t N) {
+    if (check_shape(0, K, N) != SWIGLU_OK) return 0;
+    return (size_t)packed_elems(K, N) * sizeof(swiglu_bf16);
+}
+
+swiglu_status swiglu_pack_weights(const swiglu_bf16* W1, const swiglu_bf16* W2, swiglu_bf16* Wp,
+                                  int64_t K, int64_t N, void* stream) {
+    swiglu_status st = check_shape(0, K, N);
+    if (st != SWIGLU_OK) return st;
+    if (!W1 || !W2 || !Wp) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(W1) || !aligned16(W2) || !aligned16(Wp)) return SWIGLU_ERR_MISALIGNED;
+    const Range out = range_of(Wp, packed_elems(K, N) * 2);
+    if (overlap(out, range_of(W1, K * N * 2)) || overlap(out, range_of(W2, K * N * 2)))
+        return SWIGLU_ERR_ALIASING;
+    const long long nchunks = (long long)packed_elems(K, N) / 8;
+    const int KB = (int)ceil_div(K, swk::PACK_BK);
+    int Ki = (int)K, Ni = (int)N;
+    void* args[] = {(void*)&W1, (void*)&W2, (void*)&Wp, &Ki, &Ni, (void*)&KB, (void*)&nchunks};
+    const dim3 grid((unsigned)ceil_div(nchunks, 256));
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&swk::pack_kernel), grid, dim3(256),
+                                   args, 0, (hipStream_t)stream);
+    return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
+}
+
+swiglu_status swiglu_unpack_weights(const swiglu_bf16* Wp, swiglu_bf16* W1, swiglu_bf16* W2,
+                                    int64_t K, int64_t N, void* stream) {
+    swiglu_status st = check_shape(0, K, N);
+    if (st != SWIGLU_OK) return st;
+    if (!W1 || !W2 || !Wp) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(W1) || !aligned16(W2) || !aligned16(Wp)) return SWIGLU_ERR_MISALIGNED;
+    const Range in = range_of(Wp, packed_elems(K, N) * 2);
+    const Range o1 = range_of(W1, K * N * 2), o2 = range_of(W2, K * N * 2);
+    if (overlap(in, o1) || overlap(in, o2) || overlap(o1, o2)) return SWIGLU_ERR_ALIASING;
+    const long long nchunks = (long long)packed_elems(K, N) / 8;
+    const int KB = (int)ceil_div(K, swk::PACK_BK);
+    int Ki = (int)K, Ni = (int)N;
+    void* args[] = {(void*)&Wp, (void*)&W1, (void*)&W2, &Ki, &Ni, (void*)&KB, (void*)&nchunks};
+    const dim3 grid((unsigned)ceil_div(nchunks, 256));
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&swk::unpack_kernel), grid, dim3(256),
+                                   args, 0, (hipStream_t)stream);
+    return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
+}
+
+swiglu_status swiglu_fused(const swiglu_bf16* A, const swiglu_bf16* W1, const swiglu_bf16* W2,
+                           swiglu_bf16* Y, int64_t M, int64_t K, int64_t N, void* stream) {
+    swiglu_status st = check_shape(M, K, N);
+    if (st != SWIGLU_OK) return st;
+    if (M == 0) return SWIGLU_OK;
+    if (!A || !W1 || !W2 || !Y) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(A) || !aligned16(W1) || !aligned16(W2) || !aligned16(Y)) return SWIGLU_ERR_MISALIGNED;
+    const Range y = range_of(Y, M * N * 2);
+    if (overlap(y, range_of(A, M * K * 2)) || overlap(y, range_of(W1, K * N * 2)) ||
+        overlap(y, range_of(W2, K * N * 2)))
+        return SWIGLU_ERR_ALIASING;
+
+    swk::FusedArgs a{};
+    a.A = A; a.W1 = W1; a.W2 = W2; a.Y = Y;
+    a.M = (int)M; a.K = (int)K; a.N = (int)N;
+    a.KB = (int)ceil_div(K, swk::BK);
+    a.splits = 1; a.kb_per_split = a.KB;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (M <= 32) {
+        a.tiles_m = (int)ceil_div(M, 32); a.tiles_n = (int)ceil_div(N, 128);
+        e = launch_tile<32, 128, 1, 4, true, false, false>(a, a.tiles_m * a.tiles_n, s);
+    } else if (M <= 2048) {
+        a.tiles_m = (int)ceil_div(M, 128); a.tiles_n = (int)ceil_div(N, 128);
+        e = launch_tile<128, 128, 2, 2, true, false, false>(a, a.tiles_m * a.tiles_n, s);
+    } else {
+        a.tiles_m = (int)ceil_div(M, 256); a.tiles_n = (int)ceil_div(N, 128);
+        e = launch_tile<256, 128, 2, 2, true, false, false>(a, a.tiles_m * a.tiles_n, s);
+    }
+    if (log_enabled()) std::fprintf(stderr, "[swiglu] fused M=%lld K=%lld N=%lld\n", (long long)M, (long long)K, (long long)N);
+    return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
+}
+
+int swiglu_choose_variant(int64_t M, int64_t K, int64_t N) {
+    if (check_shape(M, K, N) != SWIGLU_OK) return SWIGLU_VARIANT_AUTO;
+    return make_plan(M, K, N, SWIGLU_VARIANT_AUTO, cu_count_now()).variant;
+}
+
+size_t swiglu_workspace_bytes(int64_t M, int64_t K, int64_t N, int variant) {
+    if (check_shape(M, K, N) != SWIGLU_OK || M == 0) return 0;
+    if (!variant_known(variant)) return 0;
+    return split_workspace_bytes(make_plan(M, K, N, variant, cu_count_now()));
+}
+
+swiglu_status swiglu_fused_packed(const swiglu_bf16* A, const swiglu_bf16* Wp, swiglu_bf16* Y,
+                                  int64_t M, int64_t K, int64_t N, void* workspace,
+                                  size_t workspace_bytes, int variant, void* stream) {
+    swiglu_status st = check_shape(M, K, N);
+    if (st != SWIGLU_OK) return st;
+    if (!variant_known(variant)) return SWIGLU_ERR_BAD_VARIANT;
+    if (variant == SWIGLU_VARIANT_DECODE && M > kDecodeMaxM) return SWIGLU_ERR_BAD_VARIANT;
+    if (M == 0) return SWIGLU_OK;
+    if (!A || !Wp || !Y) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(A) || !aligned16(Wp) || !aligned16(Y)) return SWIGLU_ERR_MISALIGNED;
+    const Range y = range_of(Y, M * N * 2);
+    if (overlap(y, range_of(A, M * K * 2)) || overlap(y, range_of(Wp, packed_elems(K, N) * 2)))
+        return SWIGLU_ERR_ALIASING;
+
+    const Plan p = make_plan(M, K, N, variant, cu_count_now());
+    const size_t need = split_workspace_bytes(p);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return SWIGLU_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return SWIGLU_ERR_MISALIGNED;
+        const Range w = range_of(workspace, (int64_t)need);
+        if (overlap(w, y) || overlap(w, range_of(A, M * K * 2)) ||
+            overlap(w, range_of(Wp, packed_elems(K, N) * 2)))
+            return SWIGLU_ERR_ALIASING;
+    }
+
+    swk::FusedArgs a{};
+    a.A = A; a.W1 = Wp; a.W2 = nullptr; a.Y = Y;
+    a.M = (int)M; a.K = (int)K; a.N = (int)N;
+    a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n;
+    a.splits = p.splits; a.kb_per_split = p.kb_per_split; a.KB = p.KB;
+    if (need > 0) {
+        a.counters = reinterpret_cast<unsigned*>(workspace);
+        a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + kCounterBytes);
+    }
+    if (log_enabled())
+        std::fprintf(stderr, "[swiglu] fused_packed M=%lld K=%lld N=%lld variant=%d tile=%dx%d tiles=%d splits=%d\n",
+                     (long long)M, (long long)K, (long long)N, p.variant, p.t.BM, p.t.BN, p.tiles, p.splits);
+    hipError_t e = launch_packed(a, p, (hipStream_t)stream);
+    return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
+}
+
+swiglu_status swiglu_gemm_bf16(const swiglu_bf16* A, const swiglu_bf16* W, swiglu_bf16* C,
+                               int64_t M, int64_t K, int64_t N, void* stream) {
+    swiglu_status st = check_shape(M, K, N);
+    if (st != SWIGLU_OK) return st;
+    if (M == 0) return SWIGLU_OK;
+    if (!A || !W || !C) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(A) || !aligned16(W) || !aligned16(C)) return SWIGLU_ERR_MISALIGNED;
+    const Range c = range_of(C, M * N * 2);
+    if (overlap(c, range_of(A, M * K * 2)) || overlap(c, range_of(W, K * N * 2))) return SWIGLU_ERR_ALIASING;
+    swk::FusedArgs a{};
+    a.A = A; a.W1 = W; a.W2 = W; a.Y = C;
+    a.M = (int)M; a.K = (int)K; a.N = (int)N;
+    a.KB = (int)ceil_div(K, swk::BK);
+    a.splits = 1; a.kb_per_split = a.KB;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (M <= 32) {
+        a.tiles_m = (int)ceil_div(M, 32); a.tiles_n = (int)ceil_div(N, 256);
+        e = launch_tile<32, 256, 1, 4, false, false, false>(a, a.tiles_m * a.tiles_n, s);
+    } else if (M <= 2048) {
+        a.tiles_m = (int)ceil_div(M, 128); a.tiles_n = (int)ceil_div(N, 256);
+        e = launch_tile<128, 256, 2, 2, false, false, false>(a, a.tiles_m * a.tiles_n, s);
+    } else {
+        a.tiles_m = (int)ceil_div(M, 256); a.tiles_n = (int)ceil_div(N, 256);
+        e = launch_tile<256, 256, 2, 2, false, false, false>(a, a.tiles_m * a.tiles_n, s);
+    }
+    return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
+}
+
+swiglu_status swiglu_silu_mul(const swiglu_bf16* G, const swiglu_bf16* U, swiglu_bf16* Y,
+                              int64_t count, void* stream) {
+    if (count < 0) return SWIGLU_ERR_BAD_SHAPE;
+    if (count == 0) return SWIGLU_OK;
+    if (!G || !U || !Y) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(G) || !aligned16(U) || !aligned16(Y)) return SWIGLU_ERR_MISALIGNED;
+    const Range y = range_of(Y, count * 2);
+    if (overlap(y, range_of(G, count * 2)) || overlap(y, range_of(U, count * 2))) return SWIGLU_ERR_ALIASING;
+    const int cus = std::max(1, cu_count_now());
+    const long long nvec = (count + 7) / 8;
+    const int grid = (int)std::max<long long>(1, std::min<long long>(ceil_div(nvec, 256), (long long)cus * 8));
+    long long cnt = count;
+    void* args[] = {(void*)&G, (void*)&U, (void*)&Y, &cnt};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&swk::silu_mul_kernel), dim3(grid),
+                                   dim3(256), args, 0, (hipStream_t)stream);
+    return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
+}
+
+swiglu_status swiglu_unfused(const swiglu_bf16* A, const swiglu_bf16* W1, const swiglu_bf16* W2,
+                             swiglu_bf16* G_scratch, swiglu_bf16* U_scratch, swiglu_bf16* Y,
+                             int64_t M, int64_t K, int64_t N, void* stream) {
+    swiglu_status st = check_shape(M, K, N);
+    if (st != SWIGLU_OK) return st;
+    if (M == 0) return SWIGLU_OK;
+    if (!A || !W1 || !W2 || !G_scratch || !U_scratch || !Y) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(G_scratch) || !aligned16(U_scratch) || !aligned16(Y)) return SWIGLU_ERR_MISALIGNED;
+    const Range g = range_of(G_scratch, M * N * 2), u = range_of(U_scratch, M * N * 2),
+                y = range_of(Y, M * N * 2);
+    const Range ins[3] = {range_of(A, M * K * 2), range_of(W1, K * N * 2), range_of(W2, K * N * 2)};
+    for (const Range& r : ins)
+        if (overlap(g, r) || overlap(u, r) || overlap(y, r)) return SWIGLU_ERR_ALIASING;
+    if (overlap(g, u) || overlap(g, y) || overlap(u, y)) return SWIGLU_ERR_ALIASING;
+    st = swiglu_gemm_bf16(A, W1, G_scratch, M, K, N, stream);
+    if (st != SWIGLU_OK) return st;
+    st = swiglu_gemm_bf16(A, W2, U_scratch, M, K, N, stream);
+    if (st != SWIGLU_OK) return st;
+    return swiglu_silu_mul(G_scratch, U_scratch, Y, M * N, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/swiglu.h declares, and rejects bad arguments on the host before any
+HIP call (so these calls are safe on a machine with no device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import swiglu_gated_mlp_amd as sw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swiglu.h")
+
+OK, NULLP, SHAPE, UNSUP, MISAL, ALIAS, WS, VARIANT = 0, 1, 2, 3, 4, 5, 6, 7
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swiglu_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_set():
+    assert set(declared_functions()) == set(sw.SIGNATURES), \
+        "header and binding disagree: %s" % (set(declared_functions()) ^ set(sw.SIGNATURES))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(sw.LIB_PATH)
+    missing = [f for f in declared_functions() if not hasattr(lib, f)]
+    assert not missing, "not exported: %s" % missing
+
+
+def test_abi_version_and_status_strings():
+    assert sw.swiglu_abi_version() == 1
+    for s in range(9):
+        assert sw.status_str(s) and sw.status_str(s) != "unknown status"
+    assert sw.status_str(99) == "unknown status"
+
+
+def test_packed_bytes():
+    L = sw.lib()
+    # ceil(N/128) tiles x ceil(K/64) blocks x 256 rows x 64 k x 2 bytes
+    assert L.swiglu_packed_bytes(896, 4864) == 38 * 14 * 256 * 64 * 2
+    assert L.swiglu_packed_bytes(896, 4864) == 2 * 896 * 4864 * 2   # exact when tiles divide
+    assert L.swiglu_packed_bytes(72, 136) == 2 * 2 * 256 * 64 * 2   # padded tail tiles
+    assert L.swiglu_packed_bytes(8192, 29568) == 968884224
+    assert L.swiglu_packed_bytes(0, 8) == 0 and L.swiglu_packed_bytes(12, 8) == 0
+
+
+# fake, never-dereferenced device addresses: validation returns before any use
+A_, W1_, W2_, Y_, WP_, WS_ = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000, 0x60000000
+
+
+@pytest.mark.parametrize("M,K,N,want", [
+    (-1, 64, 64, SHAPE), (4, 0, 64, SHAPE), (4, 64, 0, SHAPE), (4, -8, 64, SHAPE),
+    (4, 60, 64, UNSUP), (4, 64, 60, UNSUP), (1 << 31, 64, 64, SHAPE),
+])
+def test_fused_shape_errors(M, K, N, want):
+    assert sw.lib().swiglu_fused(A_, W1_, W2_, Y_, M, K, N, None) == want
+
+
+def test_fused_pointer_errors():
+    L = sw.lib()
+    assert L.swiglu_fused(None, W1_, W2_, Y_, 4, 64, 64, None) == NULLP
+    assert L.swiglu_fused(A_, W1_, W2_, None, 4, 64, 64, None) == NULLP
+    assert L.swiglu_fused(A_ + 2, W1_, W2_, Y_, 4, 64, 64, None) == MISAL
+    assert L.swiglu_fused(A_, W1_, W2_, Y_ + 8, 4, 64, 64, None) == MISAL
+    # Y overlapping A, W1 or W2
+    assert L.swiglu_fused(A_, W1_, W2_, A_ + 64, 4, 64, 64, None) == ALIAS
+    assert L.swiglu_fused(A_, W1_, W2_, W2_ + 1024, 4, 64, 64, None) == ALIAS
+    # W1 == W2 is allowed (inputs may alias): validation passes; M == 0 then returns OK
+    assert L.swiglu_fused(A_, W1_, W1_, Y_, 0, 64, 64, None) == OK
+    # M == 0 is a valid empty call even with null pointers
+    assert L.swiglu_fused(None, None, None, None, 0, 64, 64, None) == OK
+
+
+def test_packed_errors():
+    L = sw.lib()
+    assert L.swiglu_fused_packed(A_, WP_, Y_, 4, 64, 64, None, 0, 9, None) == VARIANT
+    # the decode schedule serves M <= 64 only
+    assert L.swiglu_fused_packed(A_, WP_, Y_, 65, 64, 64, None, 0, 3, None) == VARIANT
+    assert L.swiglu_workspace_bytes(16, 3584, 18944, 3) == 0
+    assert L.swiglu_fused_packed(A_, WP_, Y_, 4, 64, 64, None, 0, -1, None) == VARIANT
+    assert L.swiglu_fused_packed(A_, None, Y_, 4, 64, 64, None, 0, 0, None) == NULLP
+    assert L.swiglu_fused_packed(A_, WP_, WP_ + 16, 4, 64, 64, None, 0, 1, None) == ALIAS
+    # split-K needs a workspace
+    need = L.swiglu_workspace_bytes(4, 4096, 1024, 2)
+    assert need > 0
+    assert L.swiglu_fused_packed(A_, WP_, Y_, 4, 4096, 1024, None, 0, 2, None) == WS
+    assert L.swiglu_fused_packed(A_, WP_, Y_, 4, 4096, 1024, WS_, need - 1, 2, None) == WS
+    assert L.swiglu_fused_packed(A_, WP_, Y_, 4, 4096, 1024, WS_ + 4, need, 2, None) == MISAL
+    assert L.swiglu_fused_packed(A_, WP_, Y_, 4, 4096, 1024, Y_, need, 2, None) == ALIAS
+    # the data-parallel schedule needs none
+    assert L.swiglu_workspace_bytes(4, 4096, 1024, 1) == 0
+    assert L.swiglu_pack_weights(W1_, W2_, W1_ + 16, 64, 64, None) == ALIAS
+    assert L.swiglu_pack_weights(W1_, W2_, WP_, 63, 64, None) == UNSUP
+    assert L.swiglu_unpack_weights(WP_, W1_, W1_, 64, 64, None) == ALIAS
+
+
+def test_unfused_errors():
+    L = sw.lib()
+    assert L.swiglu_silu_mul(A_, W1_, Y_, -1, None) == SHAPE
+    assert L.swiglu_silu_mul(A_, W1_, A_, 16, None) == ALIAS
+    assert L.swiglu_silu_mul(None, None, None, 0, None) == OK
+    assert L.swiglu_gemm_bf16(A_, W1_, A_ + 16, 4, 64, 64, None) == ALIAS
+    assert L.swiglu_unfused(A_, W1_, W2_, Y_, Y_, WS_, 4, 64, 64, None) == ALIAS
+    assert L.swiglu_unfused(A_, W1_, W2_, None, WP_, WS_, 4, 64, 64, None) == NULLP
+
+
+def test_workspace_counts_partials_and_counters():
+    L = sw.lib()
+    # split-K workspace covers fp32 Gate+Up partials of every (tile, split) plus
+    # one counter per tile; it is zero for the data-parallel schedule
+    for M, K, N in [(1, 3584, 18944), (16, 3584, 18944), (128, 3584, 18944), (32, 8192, 29568)]:
+        b = L.swiglu_workspace_bytes(M, K, N, 2)
+        assert b % 4 == 0 and b > 0
+        assert L.swiglu_workspace_bytes(M, K, N, 1) == 0

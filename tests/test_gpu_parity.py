@@ -1,0 +1,267 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Acceptance rule (tolerance written here, used everywhere): for every compared
+element |y - ref| <= 1e-3 + 8e-3 |ref|, y = GPU bf16, ref = oracle bf16.
+Bitwise equality is required where the arithmetic fixes the result exactly
+(integer regime, invariants, determinism, packed == unpacked).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import swiglu_gated_mlp_amd as sw
+from swiglu_gated_mlp_amd import inputs
+
+from _util import (check_close, f32, gpu_bits, mismatch_rates, oracle_cols, oracle_rows,
+                   sample_cols, sample_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+DP, SPLIT, AUTO, DECODE = (sw.VARIANT_DATA_PARALLEL, sw.VARIANT_SPLIT_K, sw.VARIANT_AUTO,
+                           sw.VARIANT_DECODE)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    sw.lib()
+    oracle.set_threads(16)
+    return torch.device("cuda:0")
+
+
+def run_all_variants(dev, A, W1, W2, label):
+    """Y from swiglu_fused and swiglu_fused_packed under every schedule."""
+    M, K = A.shape
+    N = W1.shape[1]
+    Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
+    Wp = sw.swiglu_pack_weights(W1d, W2d)
+    out = {}
+    say("[%s] M=%d K=%d N=%d fused" % (label, M, K, N))
+    out["fused"] = sw.swiglu_fused(Ad, W1d, W2d)
+    variants = [("dp", DP), ("split", SPLIT), ("auto", AUTO)]
+    if M <= 64:
+        variants.append(("decode", DECODE))
+    for name, v in variants:
+        say("[%s] M=%d K=%d N=%d packed/%s" % (label, M, K, N, name))
+        out[name] = sw.swiglu_fused_packed(Ad, Wp, N, variant=v)
+    torch.cuda.synchronize()
+    return {k: gpu_bits(v) for k, v in out.items()}
+
+
+SMALL_SHAPES = [
+    (1, 64, 128), (3, 72, 136), (17, 200, 256), (32, 128, 128), (33, 64, 264), (63, 128, 384),
+    (65, 896, 512), (128, 512, 256), (130, 256, 264), (255, 192, 128), (257, 512, 640),
+    (300, 136, 520), (2049, 128, 256), (2100, 64, 136),
+]
+
+
+@pytest.mark.parametrize("M,K,N", SMALL_SHAPES)
+def test_small_shapes_every_variant(dev, M, K, N):
+    A, W1, W2 = inputs.gaussian_case(M, K, N, seed=M * 7 + K + N)
+    outs = run_all_variants(dev, A, W1, W2, "small")
+    ref = oracle.swiglu(A, W1, W2)
+    for name, y in outs.items():
+        check_close(y, ref, "%s M=%d K=%d N=%d" % (name, M, K, N))
+    # same MFMA chain per element: unpacked and packed data-parallel agree bitwise
+    assert np.array_equal(outs["fused"], outs["dp"]), "fused != fused_packed(dp) bitwise"
+
+
+def test_pack_roundtrip_and_layout(dev):
+    for K, N in [(64, 128), (72, 136), (896, 4864), (200, 520)]:
+        _, W1, W2 = inputs.gaussian_case(1, K, N, seed=K + N)
+        W1d, W2d = W1.to(dev), W2.to(dev)
+        Wp = sw.swiglu_pack_weights(W1d, W2d)
+        V1, V2 = sw.swiglu_unpack_weights(Wp, K, N)
+        torch.cuda.synchronize()
+        assert torch.equal(V1.view(torch.int16), W1d.view(torch.int16))
+        assert torch.equal(V2.view(torch.int16), W2d.view(torch.int16))
+        # layout as documented: tile jt, block kb, row r, k offset c
+        P = inputs.as_bits(Wp.cpu())
+        KB = (K + 63) // 64
+        w1, w2 = inputs.as_bits(W1), inputs.as_bits(W2)
+        rng = np.random.default_rng(K)
+        for _ in range(200):
+            n = int(rng.integers(0, N))
+            k = int(rng.integers(0, K))
+            jt, r, kb, c = n // 128, n % 128, k // 64, k % 64
+            base = ((jt * KB + kb) * 256) * 64
+            assert P[base + r * 64 + c] == w1[k, n]
+            assert P[base + (128 + r) * 64 + c] == w2[k, n]
+        # padding is zero
+        if N % 128:
+            jt = N // 128
+            r = N % 128
+            assert np.all(P[((jt * KB) * 256 + r) * 64:((jt * KB) * 256 + 128) * 64] == 0)
+
+
+# The five Qwen-2.5-shaped workloads, eight (workload, M) points.
+POINTS = [(w.index, m) for w in inputs.WORKLOADS for m in w.ms]
+
+
+def _points_id(p):
+    return "%s-M%d" % (inputs.WORKLOADS[p[0]].name, p[1])
+
+
+@pytest.mark.parametrize("point", POINTS, ids=[_points_id(p) for p in POINTS])
+def test_integer_regime_bitwise_at_workload_shapes(dev, point):
+    """Integer inputs: Gate/Up exact in any order, SiLU(Gate) == Gate, so every
+    schedule must reproduce the oracle bit for bit."""
+    w = inputs.WORKLOADS[point[0]]
+    M = point[1]
+    A, W1, W2 = inputs.integer_case(M, w.K, w.N, seed=w.index * 10 + 1)
+    outs = run_all_variants(dev, A, W1, W2, "int-" + _points_id(point))
+    rows, cols = sample_rows(M), sample_cols(w.N)
+    ref_r = oracle_rows(A, W1, W2, rows)
+    ref_c = oracle_cols(A, W1, W2, cols)
+    for name, y in outs.items():
+        assert np.array_equal(y[rows], ref_r), "%s: sampled rows differ bitwise" % name
+        assert np.array_equal(y[:, cols], ref_c), "%s: sampled columns differ bitwise" % name
+        assert np.array_equal(y, outs["fused"]), "%s differs from fused" % name
+
+
+@pytest.mark.parametrize("point", POINTS, ids=[_points_id(p) for p in POINTS])
+def test_gaussian_workloads(dev, point):
+    """Seeded N(0,1) activations, N(0,1/K) weights at the workload shapes; the
+    oracle is evaluated on sampled rows (all columns, so every N tile) and on
+    sampled columns (all rows, so every M tile)."""
+    w = inputs.WORKLOADS[point[0]]
+    M = point[1]
+    A, W1, W2 = inputs.workload_tensors(w, M)
+    outs = run_all_variants(dev, A, W1, W2, "gauss-" + _points_id(point))
+    if M * w.K * w.N <= 64 * 896 * 4864:
+        ref, P = oracle.swiglu(A, W1, W2, want_p=True)
+        for name, y in outs.items():
+            check_close(y, ref, name)
+            b, pg = mismatch_rates(y, ref, P)
+            say("  %s: bitwise mismatch %.5f%%, >1%% rel err vs fp32 %.5f%%" % (name, 100 * b, 100 * pg))
+        return
+    rows, cols = sample_rows(M), sample_cols(w.N)
+    ref_r, P_r = oracle_rows(A, W1, W2, rows, want_p=True)
+    ref_c = oracle_cols(A, W1, W2, cols)
+    for name, y in outs.items():
+        check_close(y[rows], ref_r, name + " rows")
+        check_close(y[:, cols], ref_c, name + " cols")
+        b, pg = mismatch_rates(y[rows], ref_r, P_r)
+        say("  %s: bitwise mismatch %.5f%%, >1%% rel err vs fp32 %.5f%% (sampled rows)"
+            % (name, 100 * b, 100 * pg))
+
+
+def test_unfused_pipeline(dev):
+    M, K, N = 64, 896, 4864
+    A, W1, W2 = inputs.workload_tensors(inputs.WORKLOADS[0])
+    Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
+    G, U, Y = sw.swiglu_unfused(Ad, W1d, W2d)
+    torch.cuda.synchronize()
+    Gb, Ub, Yb = gpu_bits(G), gpu_bits(U), gpu_bits(Y)
+    # each GEMM: the fp32 sums differ only in order, so bf16 results are within 1 ulp
+    # (plus an absolute floor for sums that cancel to near zero)
+    for name, got, w in (("G", Gb, W1), ("U", Ub, W2)):
+        ref = oracle.gemm_bf16(A, w)
+        g, r = f32(got).astype(np.float64), f32(ref).astype(np.float64)
+        bad = np.argwhere(np.abs(g - r) > 2.0 ** -7 * np.abs(r) + 1e-3)
+        assert bad.size == 0, "%s: %d elements beyond 1 ulp, e.g. %s got %r want %r" % (
+            name, len(bad), bad[0].tolist(), g[tuple(bad[0])], r[tuple(bad[0])])
+    # the element-wise step on the GPU's own G and U
+    check_close(Yb, oracle.silu_mul(Gb, Ub), "silu_mul")
+    # the whole pipeline against the oracle's fused result: double rounding of
+    # Gate and Up adds error, report it
+    ref, P = oracle.swiglu(A, W1, W2, want_p=True)
+    b, pg = mismatch_rates(Yb, ref, P)
+    say("  unfused vs fused oracle: bitwise mismatch %.4f%%, >1%% rel err %.4f%%" % (100 * b, 100 * pg))
+    # stand-alone silu_mul with an odd count (vector body + scalar tail)
+    cnt = 1000003
+    g = torch.randn(cnt, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    u = torch.randn(cnt, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16)
+    y = sw.swiglu_silu_mul(g.to(dev), u.to(dev))
+    torch.cuda.synchronize()
+    check_close(gpu_bits(y), oracle.silu_mul(inputs.as_bits(g), inputs.as_bits(u)), "silu_mul odd")
+
+
+def test_invariants_at_decode_shape(dev):
+    K, N = 3584, 18944
+    A, W1, W2 = inputs.workload_tensors(inputs.WORKLOADS[2], 16)
+    Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
+    Wp = sw.swiglu_pack_weights(W1d, W2d)
+    for v in (DP, SPLIT, DECODE):
+        base = sw.swiglu_fused_packed(Ad, Wp, N, variant=v)
+        again = sw.swiglu_fused_packed(Ad, Wp, N, variant=v)
+        torch.cuda.synchronize()
+        assert torch.equal(base.view(torch.int16), again.view(torch.int16)), "not deterministic"
+        # W1 = 0 -> Y = 0
+        Z = sw.swiglu_pack_weights(torch.zeros_like(W1d), W2d)
+        assert torch.all(sw.swiglu_fused_packed(Ad, Z, N, variant=v).float() == 0)
+        # zero W2 column -> zero Y column, others unchanged
+        W2z = W2d.clone()
+        W2z[:, 777] = 0
+        Yz = sw.swiglu_fused_packed(Ad, sw.swiglu_pack_weights(W1d, W2z), N, variant=v)
+        assert torch.all(Yz[:, 777].float() == 0)
+        keep = [c for c in range(N) if c != 777]
+        assert torch.equal(Yz[:, keep].view(torch.int16), base[:, keep].view(torch.int16))
+        # W2 -> 2 W2 doubles Y exactly
+        Y2 = sw.swiglu_fused_packed(Ad, sw.swiglu_pack_weights(W1d, W2d * 2), N, variant=v)
+        assert torch.equal(Y2.float(), 2 * base.float())
+        # joint column permutation
+        perm = torch.randperm(N, generator=torch.Generator().manual_seed(5)).to(dev)
+        Yp = sw.swiglu_fused_packed(Ad, sw.swiglu_pack_weights(W1d[:, perm].contiguous(),
+                                                               W2d[:, perm].contiguous()), N, variant=v)
+        assert torch.equal(Yp.view(torch.int16), base[:, perm].view(torch.int16))
+        # swapping Gate and Up changes the result
+        Ys = sw.swiglu_fused_packed(Ad, sw.swiglu_pack_weights(W2d, W1d), N, variant=v)
+        assert not torch.equal(Ys.view(torch.int16), base.view(torch.int16))
+    # one-hot rows select weight rows: Gate = W1[k], Up = W2[k] exactly
+    Ah = A.clone()
+    ks = [0, 1234, 3583]
+    for i, k in enumerate(ks):
+        Ah[i] = 0
+        Ah[i, k] = 1.0
+    Yh = gpu_bits(sw.swiglu_fused_packed(Ah.to(dev), Wp, N))
+    torch.cuda.synchronize()
+    refh = oracle_rows(Ah, W1, W2, list(range(len(ks))))
+    check_close(Yh[:len(ks)], refh, "one-hot rows")
+    # prefix: the M=1 call equals row 0 of the M=16 call (same schedule class)
+    Y1 = gpu_bits(sw.swiglu_fused_packed(Ad[:1].contiguous(), Wp, N))
+    Y16 = gpu_bits(sw.swiglu_fused_packed(Ad, Wp, N))
+    check_close(Y1, Y16[:1], "prefix M=1 vs M=16")
+
+
+def test_edge_cases(dev):
+    K, N = 128, 256
+    A, W1, W2 = inputs.gaussian_case(5, K, N, seed=77)
+    Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
+    # M = 0
+    y0 = sw.swiglu_fused(Ad[:0], W1d, W2d)
+    assert y0.shape == (0, N)
+    Wp = sw.swiglu_pack_weights(W1d, W2d)
+    assert sw.swiglu_fused_packed(Ad[:0], Wp, N).shape == (0, N)
+    # W1 == W2 is legal: Y = SiLU(G) * G
+    ys = gpu_bits(sw.swiglu_fused(Ad, W1d, W1d))
+    check_close(ys, oracle.swiglu(A, W1, W1), "W1 == W2")
+    # misaligned operand is rejected before launch
+    buf = torch.empty(5 * K + 1, dtype=torch.bfloat16, device=dev)
+    Amis = buf[1:].view(5, K)
+    with pytest.raises(sw.SwigluError) as ei:
+        sw.swiglu_fused(Amis, W1d, W2d)
+    assert ei.value.status == 4
+    # overflow regime: Gate <= -K -> SiLU = -0 -> Y = +-0
+    A2, W12, W22 = inputs.integer_case(64, 896, 512, seed=3, w1_vals=(-3, -2, -1))
+    Y = sw.swiglu_fused(A2.to(dev), W12.to(dev), W22.to(dev))
+    torch.cuda.synchronize()
+    assert np.all((gpu_bits(Y) & 0x7FFF) == 0)
+
+
+def test_split_workspace_reused_across_shapes(dev):
+    """One workspace serves split-K calls of different tile counts in a row:
+    the arrival counters live in a fixed region that partials never touch, and
+    every call leaves them at zero."""
+    ws = sw.Workspace(dev)
+    shapes = [(128, 2048, 1024), (128, 2048, 18944), (128, 1024, 4864), (128, 2048, 18944), (96, 512, 8192)]
+    for i, (M, K, N) in enumerate(shapes):
+        A, W1, W2 = inputs.gaussian_case(M, K, N, seed=300 + i)
+        Wp = sw.swiglu_pack_weights(W1.to(dev), W2.to(dev))
+        Y = sw.swiglu_fused_packed(A.to(dev), Wp, N, workspace=ws, variant=SPLIT)
+        torch.cuda.synchronize()
+        rows = sample_rows(M, 4)
+        check_close(gpu_bits(Y)[rows], oracle_rows(A, W1, W2, rows), "split reuse %s" % ((M, K, N),))
+        head = ws.buf[:64 * 1024].view(torch.int32)
+        assert int(head.abs().sum()) == 0, "arrival counters not left at zero"
