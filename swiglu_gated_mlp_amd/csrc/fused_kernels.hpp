@@ -388,6 +388,187 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_tile_kernel(FusedArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Prefill (large M) fused kernel on packed weights.
+//   Same math and lane layout as fused_tile_kernel, but the global -> LDS copy
+//   uses the direct LDS load (global_load_lds_dwordx4): each wave instruction
+//   writes 64 x 16 bytes to consecutive LDS chunks, so the bank swizzle is
+//   applied by choosing which global chunk each lane fetches.  No staging
+//   registers and no LDS-write instructions: the next K step streams into the
+//   other LDS stage while the MFMAs run on this one, and the only wait per
+//   step is the final vmcnt + barrier.  Fragments are double-buffered in
+//   registers across the four 16-deep K sub-steps.
+//   A ragged last K block (K % 64 != 0) goes through registers so the
+//   activation columns beyond K are zero-filled (the packed weights are
+//   already zero there).
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+__device__ __forceinline__ void dma16(const uint16_t* gsrc, uint16_t* lds_dst) {
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gsrc),
+                                     (lds_void_ptr)(lds_dst), 16, 0, 0);
+}
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p) {
+    constexpr int NT = 64 * WM * WN;
+    constexpr int NW = WM * WN;
+    constexpr int NB = 2 * BN;                // Gate rows then Up rows
+    constexpr int TM = BM / WM / 32;
+    constexpr int TN = BN / WN / 32;
+    constexpr int A_INS = BM / 8 / NW;        // 1 KiB direct loads per wave per stage (A)
+    constexpr int B_INS = NB / 8 / NW;        // ... (weights)
+    constexpr int STAGE = (BM + NB) * BK;     // elements per LDS stage
+    constexpr int GROUP_M = 8;
+    static_assert(TM >= 1 && TN >= 1, "tile too small for the wave grid");
+    static_assert(A_INS >= 1 && B_INS >= 1 && (BM / 8) % NW == 0 && (NB / 8) % NW == 0, "load split");
+    static_assert(PACK_BN % BN == 0, "tile must divide the packed tile");
+
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave % WM, wn = wave / WM;
+    const int wrow0 = wm * (BM / WM);
+    const int wcol0 = wn * (BN / WN);
+
+    const int tile = xcd_remap(blockIdx.x, gridDim.x);
+    int tm, tn;
+    {
+        const int per_group = GROUP_M * p.tiles_n;
+        const int group = tile / per_group;
+        const int first_m = group * GROUP_M;
+        const int gsize = min(p.tiles_m - first_m, GROUP_M);
+        const int in_group = tile - group * per_group;
+        tm = first_m + in_group % gsize;
+        tn = in_group / gsize;
+    }
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const int M = p.M, K = p.K, N = p.N, KB = p.KB;
+    const int jp = n0 / PACK_BN, ro = n0 % PACK_BN;
+    const bool ragged_k = (K % BK) != 0;
+
+    // per-lane source offsets (elements), constant over K steps
+    const int lrow = lane >> 3, lpc = lane & 7;
+    const uint16_t* a_src[A_INS];
+    int b_off[B_INS];
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) {
+        const int r = (wave * A_INS + i) * 8 + lrow;
+        const int grow = min(m0 + r, M - 1);
+        a_src[i] = p.A + (size_t)grow * K + 8 * (lpc ^ swz(r));
+    }
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) {
+        const int r = (wave * B_INS + i) * 8 + lrow;
+        const int prow = r < BN ? ro + r : PACK_BN + ro + (r - BN);
+        b_off[i] = prow * PACK_BK + 8 * (lpc ^ swz(r));
+    }
+    const uint16_t* wtile = p.W1 + (size_t)jp * KB * (PACK_ROWS * PACK_BK);
+
+    auto issue_stage = [&](int kb, int buf) {
+        uint16_t* sA = smem + buf * STAGE;
+        uint16_t* sB = sA + BM * BK;
+        const int k0 = kb * BK;
+        if (ragged_k && kb == KB - 1) {
+            // zero-filled activation columns beyond K, through registers
+#pragma unroll
+            for (int i = 0; i < A_INS; ++i) {
+                const int r = (wave * A_INS + i) * 8 + lrow;
+                const int kc = k0 + 8 * (lpc ^ swz(r));
+                u32x4 v = u32x4{0u, 0u, 0u, 0u};
+                if (kc < K) v = ld16(a_src[i] + k0);
+                *reinterpret_cast<u32x4*>(sA + ((wave * A_INS + i) * 64 + lane) * 8) = v;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < A_INS; ++i)
+                dma16(a_src[i] + k0, sA + (wave * A_INS + i) * 512);
+        }
+        const uint16_t* blk = wtile + (size_t)kb * (PACK_ROWS * PACK_BK);
+#pragma unroll
+        for (int i = 0; i < B_INS; ++i) dma16(blk + b_off[i], sB + (wave * B_INS + i) * 512);
+    };
+
+    f32x16 acc[2][TM][TN];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[g][i][j][r] = 0.0f;
+
+    bf16x8 fa[2][TM], fb[2][2][TN];
+    auto read_frags = [&](int buf, int kk, int set) {
+        const uint16_t* sA = smem + buf * STAGE;
+        const uint16_t* sB = sA + BM * BK;
+        const int c = 2 * kk + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            fa[set][i] = *reinterpret_cast<const bf16x8*>(sA + lds_off(wrow0 + i * 32 + (lane & 31), c));
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                fb[set][g][j] = *reinterpret_cast<const bf16x8*>(
+                    sB + lds_off(g * BN + wcol0 + j * 32 + (lane & 31), c));
+    };
+    auto mfmas = [&](int set) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[g][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][g][j], fa[set][i],
+                                                                           acc[g][i][j], 0, 0, 0);
+    };
+
+    issue_stage(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kb = 0; kb < KB; ++kb) {
+        const int buf = kb & 1;
+        if (kb + 1 < KB) issue_stage(kb + 1, buf ^ 1);
+        read_frags(buf, 0, 0);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            if (kk + 1 < BK / 16) read_frags(buf, kk + 1, (kk + 1) & 1);
+            mfmas(kk & 1);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // epilogue: SiLU(Gate) * Up, bf16, 8-byte stores
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int m = m0 + wrow0 + i * 32 + (lane & 31);
+        if (m >= M) continue;
+        uint16_t* yrow = p.Y + (size_t)m * N;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wcol0 + j * 32 + 8 * q + 4 * (lane >> 5);
+                if (n >= N) continue;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = silu_f(acc[0][i][j][4 * q + e]) * acc[1][i][j][4 * q + e];
+                u32x2 out;
+                out[0] = pack2(v[0], v[1]);
+                out[1] = pack2(v[2], v[3]);
+                *reinterpret_cast<u32x2*>(yrow + n) = out;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Decode (small M): weight streaming.
 //   The product is bound by reading the packed weights once from HBM, so the
 //   kernel is shaped around keeping many 16-byte loads in flight, not around

@@ -176,6 +176,14 @@ hipError_t launch_decode(const swk::DecodeArgs& a, int groups, hipStream_t s) {
     return hipLaunchKernel(fn, dim3(groups), dim3(256), kargs, 0, s);
 }
 
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_prefill(const swk::FusedArgs& a, int grid, hipStream_t s) {
+    const void* fn = reinterpret_cast<const void*>(&swk::fused_prefill_kernel<BM, BN, WM, WN>);
+    swk::FusedArgs args = a;
+    void* kargs[] = {&args};
+    return hipLaunchKernel(fn, dim3(grid), dim3(64 * WM * WN), kargs, 0, s);
+}
+
 hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) {
     if (p.variant == SWIGLU_VARIANT_DECODE) {
         swk::DecodeArgs d{};
@@ -199,10 +207,10 @@ hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) 
                          : launch_tile<64, 128, 2, 2, true, true, false>(a, grid, s);
         case 128:
             return split ? launch_tile<128, 128, 2, 2, true, true, true>(a, grid, s)
-                         : launch_tile<128, 128, 2, 2, true, true, false>(a, grid, s);
+                         : launch_prefill<128, 128, 2, 2>(a, grid, s);
         default:
             return split ? launch_tile<256, 128, 2, 2, true, true, true>(a, grid, s)
-                         : launch_tile<256, 128, 2, 2, true, true, false>(a, grid, s);
+                         : launch_prefill<256, 128, 2, 2>(a, grid, s);
     }
 }
 
