@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace swk {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -427,7 +429,7 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wm = wave % WM, wn = wave / WM;
     const int wrow0 = wm * (BM / WM);
     const int wcol0 = wn * (BN / WN);
@@ -467,25 +469,28 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
     }
     const uint16_t* wtile = p.W1 + (size_t)jp * KB * (PACK_ROWS * PACK_BK);
 
-    auto issue_stage = [&](int kb, int buf) {
+    // activation columns beyond K (ragged last block) are zero-filled through
+    // registers; every other stage is a direct load
+    auto issue_a_regs = [&](int kb, int buf) {
         uint16_t* sA = smem + buf * STAGE;
-        uint16_t* sB = sA + BM * BK;
         const int k0 = kb * BK;
-        if (ragged_k && kb == KB - 1) {
-            // zero-filled activation columns beyond K, through registers
 #pragma unroll
-            for (int i = 0; i < A_INS; ++i) {
-                const int r = (wave * A_INS + i) * 8 + lrow;
-                const int kc = k0 + 8 * (lpc ^ swz(r));
-                u32x4 v = u32x4{0u, 0u, 0u, 0u};
-                if (kc < K) v = ld16(a_src[i] + k0);
-                *reinterpret_cast<u32x4*>(sA + ((wave * A_INS + i) * 64 + lane) * 8) = v;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < A_INS; ++i)
-                dma16(a_src[i] + k0, sA + (wave * A_INS + i) * 512);
+        for (int i = 0; i < A_INS; ++i) {
+            const int r = (wave * A_INS + i) * 8 + lrow;
+            const int kc = k0 + 8 * (lpc ^ swz(r));
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (kc < K) v = ld16(a_src[i] + k0);
+            *reinterpret_cast<u32x4*>(sA + ((wave * A_INS + i) * 64 + lane) * 8) = v;
         }
+    };
+    auto issue_a = [&](int kb, int buf) {
+        uint16_t* sA = smem + buf * STAGE;
+        const int k0 = kb * BK;
+#pragma unroll
+        for (int i = 0; i < A_INS; ++i) dma16(a_src[i] + k0, sA + (wave * A_INS + i) * 512);
+    };
+    auto issue_b = [&](int kb, int buf) {
+        uint16_t* sB = smem + buf * STAGE + BM * BK;
         const uint16_t* blk = wtile + (size_t)kb * (PACK_ROWS * PACK_BK);
 #pragma unroll
         for (int i = 0; i < B_INS; ++i) dma16(blk + b_off[i], sB + (wave * B_INS + i) * 512);
@@ -527,21 +532,82 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
                                                                            acc[g][i][j], 0, 0, 0);
     };
 
-    issue_stage(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int kb = 0; kb < KB; ++kb) {
-        const int buf = kb & 1;
-        if (kb + 1 < KB) issue_stage(kb + 1, buf ^ 1);
-        read_frags(buf, 0, 0);
+    // Software pipeline over the four 16-deep sub-steps of a 64-deep stage:
+    // the fragments of sub-step kk+1 are read while the MFMAs of kk run
+    // (each read slotted between MFMAs), and the one barrier per stage sits
+    // before the last sub-step's MFMAs, so the first reads of the next stage
+    // overlap those 16 MFMAs instead of stalling the matrix pipe.
+    constexpr int NFRAG = TM + 2 * TN;          // ds_read_b128 per sub-step
+    constexpr int NMFMA = 2 * TM * TN;          // MFMAs per sub-step
+    static_assert(NMFMA >= NFRAG, "sub-step needs at least one MFMA per fragment read");
+    // [MFMA, LDS read] x NFRAG, then the remaining MFMAs: the sub-step opens
+    // with an MFMA (its operands were read a whole sub-step earlier) and its
+    // last read is issued well before the next sub-step needs it.
+    auto interleave = [&](auto ndma) {
+        constexpr int ND = decltype(ndma)::value;
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            if (kk + 1 < BK / 16) read_frags(buf, kk + 1, (kk + 1) & 1);
-            mfmas(kk & 1);
+        for (int t = 0; t < NFRAG; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+            if (t < ND) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // direct load
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NFRAG, 0);
+    };
+    using Z = std::integral_constant<int, 0>;
+    using NA = std::integral_constant<int, A_INS>;
+    using NB_ = std::integral_constant<int, B_INS>;
+
+    // One 64-deep stage.  PREFETCH: stage kb+1 is loaded into the other LDS
+    // buffer during this one (the activation part through registers when
+    // RAGGED_NEXT, i.e. stage kb+1 is a ragged last block).
+    auto stage = [&](auto prefetch, auto ragged_next, int kb) {
+        constexpr bool PF = decltype(prefetch)::value;
+        constexpr bool RN = decltype(ragged_next)::value;
+        const int buf = kb & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (PF) {
+            if constexpr (RN) issue_a_regs(kb + 1, buf ^ 1);
+            else issue_a(kb + 1, buf ^ 1);
+        }
+        read_frags(buf, 1, 1);
+        mfmas(0);
+        if constexpr (PF && !RN) interleave(NA{});
+        else interleave(Z{});
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (PF) issue_b(kb + 1, buf ^ 1);
+        read_frags(buf, 2, 0);
+        mfmas(1);
+        if constexpr (PF) interleave(NB_{});
+        else interleave(Z{});
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(buf, 3, 1);
+        mfmas(0);
+        interleave(Z{});
+        __builtin_amdgcn_sched_barrier(0);
+        // stage kb+1 has landed in LDS for every wave, and every wave is done
+        // reading stage kb (its last fragments are in registers)
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-    }
+        if constexpr (PF) {
+            read_frags(buf ^ 1, 0, 0);
+            mfmas(1);
+            interleave(Z{});
+        } else {
+            mfmas(1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    if (ragged_k && KB == 1) issue_a_regs(0, 0);
+    else issue_a(0, 0);
+    issue_b(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    read_frags(0, 0, 0);
+    const int steady = KB - 1 - (ragged_k && KB >= 2 ? 1 : 0);
+    for (int kb = 0; kb < steady; ++kb) stage(std::true_type{}, std::false_type{}, kb);
+    if (ragged_k && KB >= 2) stage(std::true_type{}, std::true_type{}, KB - 2);
+    stage(std::false_type{}, std::false_type{}, KB - 1);
 
     // epilogue: SiLU(Gate) * Up, bf16, 8-byte stores
 #pragma unroll
