@@ -77,6 +77,30 @@ def time_gpu(fn_list, steps, warmup, stream):
     return start.elapsed_time(stop) / 1e3
 
 
+def kernel_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("swiglu_gated_mlp_amd/csrc/fused_kernels.hpp", "swiglu_gated_mlp_amd/csrc/swiglu_api.hip"):
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_label):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs (profiles/traffic.json, copy-calibrated), or None when they were taken
+    on another workload or on kernel sources that have changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload_label or t.get("source_sha256") != kernel_source_sha256():
+        return None
+    return t.get("traffic_bytes_per_dispatch")
+
+
 def cpu_baseline(w, M, target_s=12.0):
     """Time the CPU oracle (as it stands) on the first rows of the same workload:
     a few rows first to estimate the rate, then enough rows for ~target_s."""
@@ -152,6 +176,55 @@ def bench_unfused(w, M, steps, warmup, stream):
     return sec / steps
 
 
+def ceilings(stream):
+    """What the device sustains: MFMA-only loop, streaming read, and the vendor
+    library's bf16 GEMM on the same [M,K]x[K,2N] shapes (context only)."""
+    import torch
+    import swiglu_gated_mlp_amd as sw
+    from swiglu_gated_mlp_amd import inputs
+    dev = torch.device("cuda:0")
+    out = {}
+    blocks, iters = 2048, 1000
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    sec = time_gpu([lambda: sw.swiglu_probe_mfma(sink, blocks, iters)], 5, 2, stream)
+    out["mfma_bf16_tflops"] = round(blocks * 4 * iters * 8 * 32768 / (sec / 5) / 1e12, 1)
+    nbytes = 4 << 30
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    src.fill_(1.0)
+    isink = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
+    for b in (1024, 2048, 4096):
+        sec = time_gpu([lambda b=b: sw.swiglu_probe_read(src, isink, b)], 5, 2, stream)
+        out["hbm_read_gbs_blocks%d" % b] = round(nbytes / (sec / 5) / 1e9, 1)
+    del src
+    dst = torch.empty(nbytes // 4, dtype=torch.bfloat16, device=dev)
+    srcc = torch.ones(nbytes // 4, dtype=torch.bfloat16, device=dev)
+    sec = time_gpu([lambda: dst.copy_(srcc)], 5, 2, stream)
+    out["copy_gbs_read_plus_write"] = round(2 * (nbytes // 2) / (sec / 5) / 1e9, 1)
+    del dst, srcc
+    for name, m in (("qwen2.5-0.5B-prefill", 4096), ("qwen2.5-7B-prefill", 8192), ("qwen2.5-72B", 4096)):
+        w = inputs.BY_NAME[name]
+        A = torch.randn(m, w.K, device=dev).to(torch.bfloat16)
+        W = (torch.randn(w.K, 2 * w.N, device=dev) * w.K ** -0.5).to(torch.bfloat16)
+        sec = time_gpu([lambda: torch.matmul(A, W)], 10, 3, stream)
+        out["torch_matmul_%s_tflops" % name] = round(flops(m, w.K, w.N) / (sec / 10) / 1e12, 1)
+        del A, W
+    log("CEIL " + json.dumps(out))
+    return out
+
+
+def copy_probe(mib):
+    """A plain device copy of a known size (the byte-counter calibration run)."""
+    import torch
+    n = (mib << 20) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy probe: 3 copies of %d MiB" % mib)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +236,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload point and the unfused pipeline (stderr)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="also measure the MFMA / HBM / vendor-GEMM ceilings (stderr)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (byte-counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -180,7 +257,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     sw.lib()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     stream = torch.cuda.current_stream()
+    if args.ceilings:
+        ceilings(stream)
     w = inputs.BY_NAME[args.workload]
     M = args.m or w.m_max
 
@@ -230,7 +312,8 @@ def main():
         "config": {"workload": "%s M=%d K=%d N=%d" % (w.name, M, w.K, w.N), "M": M, "K": w.K,
                    "N": w.N, "variant": args.variant, "rotation_sets": res["rotation"]},
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 5), "traffic": None},
+                     "frac": round(achieved / peak, 5),
+                     "traffic": measured_traffic("%s M=%d K=%d N=%d" % (w.name, M, w.K, w.N))},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -48,6 +48,9 @@ SIGNATURES = {
     "swiglu_gemm_bf16": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "swiglu_silu_mul": ([_P, _P, _P, _I64, _P], ctypes.c_int),
     "swiglu_unfused": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    # include/swiglu_probe.h (diagnostic ceilings)
+    "swiglu_probe_mfma": ([_P, ctypes.c_int, ctypes.c_int, _P], ctypes.c_int),
+    "swiglu_probe_read": ([_P, ctypes.c_size_t, _P, ctypes.c_int, _P], ctypes.c_int),
 }
 
 _lock = threading.Lock()
@@ -280,3 +283,25 @@ def swiglu_unfused(A: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor, G: torch
                               _stream(stream))
     _check("swiglu_unfused", st)
     return G, U, Y
+
+
+# ---------------------------------------------------------------------------
+# diagnostic ceilings (include/swiglu_probe.h)
+# ---------------------------------------------------------------------------
+
+def swiglu_probe_mfma(sink: torch.Tensor, blocks: int, iters: int, stream=None) -> None:
+    """MFMA-only loop: blocks x 4 waves x iters x 8 v_mfma_f32_32x32x16_bf16."""
+    if sink.dtype != torch.float32 or sink.numel() < blocks * 256 or sink.device.type != "cuda":
+        raise ValueError("sink must be a GPU float32 tensor of >= blocks*256 elements")
+    _check("swiglu_probe_mfma", lib().swiglu_probe_mfma(sink.data_ptr(), blocks, iters, _stream(stream)))
+
+
+def swiglu_probe_read(src: torch.Tensor, sink: torch.Tensor, blocks: int, stream=None) -> None:
+    """Stream every byte of ``src`` through 16-byte loads."""
+    nbytes = src.numel() * src.element_size()
+    if src.device.type != "cuda" or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    if sink.dtype != torch.int32 or sink.numel() < blocks * 256 or sink.device.type != "cuda":
+        raise ValueError("sink must be a GPU int32 tensor of >= blocks*256 elements")
+    _check("swiglu_probe_read", lib().swiglu_probe_read(src.data_ptr(), nbytes, sink.data_ptr(), blocks,
+                                                        _stream(stream)))

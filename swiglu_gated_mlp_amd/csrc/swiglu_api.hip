@@ -4,6 +4,7 @@
 // Every argument check runs before the first HIP call, so a rejected call has
 // no effect on the device and the checks work on a machine without a GPU.
 #include "swiglu.h"
+#include "swiglu_probe.h"
 
 #include <hip/hip_runtime.h>
 
@@ -15,6 +16,7 @@
 #include <mutex>
 
 #include "fused_kernels.hpp"
+#include "probe_kernels.hpp"
 
 namespace {
 
@@ -436,6 +438,26 @@ swiglu_status swiglu_unfused(const swiglu_bf16* A, const swiglu_bf16* W1, const 
     st = swiglu_gemm_bf16(A, W2, U_scratch, M, K, N, stream);
     if (st != SWIGLU_OK) return st;
     return swiglu_silu_mul(G_scratch, U_scratch, Y, M * N, stream);
+}
+
+swiglu_status swiglu_probe_mfma(float* sink, int blocks, int iters, void* stream) {
+    if (!sink) return SWIGLU_ERR_NULL_POINTER;
+    if (blocks < 1 || iters < 1) return SWIGLU_ERR_BAD_SHAPE;
+    void* args[] = {(void*)&sink, &iters};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&swk::probe_mfma_kernel), dim3(blocks),
+                                   dim3(256), args, 0, (hipStream_t)stream);
+    return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
+}
+
+swiglu_status swiglu_probe_read(const void* src, size_t bytes, uint32_t* sink, int blocks, void* stream) {
+    if (!src || !sink) return SWIGLU_ERR_NULL_POINTER;
+    if (blocks < 1 || bytes < 16 || (bytes % 16) != 0) return SWIGLU_ERR_BAD_SHAPE;
+    if (!aligned16(src)) return SWIGLU_ERR_MISALIGNED;
+    long long n16 = (long long)(bytes / 16);
+    void* args[] = {(void*)&src, &n16, (void*)&sink};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&swk::probe_read_kernel), dim3(blocks),
+                                   dim3(256), args, 0, (hipStream_t)stream);
+    return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
 }
 
 }  // extern "C"

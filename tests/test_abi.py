@@ -10,13 +10,13 @@ import pytest
 import swiglu_gated_mlp_amd as sw
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "swiglu.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("swiglu.h", "swiglu_probe.h")]
 
 OK, NULLP, SHAPE, UNSUP, MISAL, ALIAS, WS, VARIANT = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(swiglu_[a-z0-9_]+)\s*\(", text)))
 
@@ -117,3 +117,11 @@ def test_workspace_counts_partials_and_counters():
         b = L.swiglu_workspace_bytes(M, K, N, 2)
         assert b % 4 == 0 and b > 0
         assert L.swiglu_workspace_bytes(M, K, N, 1) == 0
+
+
+def test_probe_argument_errors():
+    L = sw.lib()
+    assert L.swiglu_probe_mfma(None, 1, 1, None) == NULLP
+    assert L.swiglu_probe_mfma(Y_, 0, 1, None) == SHAPE
+    assert L.swiglu_probe_read(A_, 15, Y_, 1, None) == SHAPE
+    assert L.swiglu_probe_read(A_ + 4, 64, Y_, 1, None) == MISAL
