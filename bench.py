@@ -228,8 +228,8 @@ def copy_probe(mib):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--m", type=int, default=None, help="token count (default: the workload's largest)")
     ap.add_argument("--variant", default="auto", choices=["auto", "data_parallel", "split_k"])

@@ -609,18 +609,22 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
     if (ragged_k && KB >= 2) stage(std::true_type{}, std::true_type{}, KB - 2);
     stage(std::false_type{}, std::false_type{}, KB - 1);
 
-    // epilogue: SiLU(Gate) * Up, bf16, 8-byte stores
+    // Epilogue: SiLU(Gate) * Up -> bf16, staged through LDS so the global
+    // stores are 16 bytes per lane over whole 128-byte row segments.  Every
+    // wave has finished reading the stage buffers (the last barrier came
+    // before the final sub-step, whose operands were already in registers),
+    // so buffer 0 holds the Y tile: each wave owns a disjoint
+    // (BM/WM) x (BN/WN) region, rows of 64 columns, chunks swizzled like the
+    // operand stages.
+    static_assert(BN / WN == 64, "epilogue staging assumes 64 columns per wave");
+    uint16_t* sY = smem + wave * (BM / WM) * 64;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-        const int m = m0 + wrow0 + i * 32 + (lane & 31);
-        if (m >= M) continue;
-        uint16_t* yrow = p.Y + (size_t)m * N;
+        const int r = i * 32 + (lane & 31);
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wcol0 + j * 32 + 8 * q + 4 * (lane >> 5);
-                if (n >= N) continue;
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -628,9 +632,20 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
                 u32x2 out;
                 out[0] = pack2(v[0], v[1]);
                 out[1] = pack2(v[2], v[3]);
-                *reinterpret_cast<u32x2*>(yrow + n) = out;
+                *reinterpret_cast<u32x2*>(sY + lds_off(r, q + 4 * j) + 4 * (lane >> 5)) = out;
             }
         }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < (BM / WM) / 8; ++t) {
+        const int r = t * 8 + (lane >> 3);
+        const int pc = lane & 7;
+        const int c = pc ^ swz(r);
+        const int m = m0 + wrow0 + r;
+        const int n = n0 + wcol0 + 8 * c;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sY + r * 64 + pc * 8);
+        if (m < M && n < N) *reinterpret_cast<u32x4*>(p.Y + (size_t)m * N + n) = v;
     }
 }
 
