@@ -66,11 +66,12 @@ typedef enum {
 /* Schedules of the fused packed entry point.
  *  DATA_PARALLEL: one workgroup per output tile, full K per tile; for large M
  *                 (the pages' Kernel-1 regime, [Summary: Methodology] Kernel-1).
- *  SPLIT_K:       the K range is split across workgroups; fp32 Gate/Up partials
- *                 go through the workspace and are summed in fixed split order
- *                 BEFORE SiLU; for small M, where output tiles alone cannot fill
- *                 the GPU (the occupancy problem of [Summary: Methodology]
- *                 Kernel-2, "Optimization").
+ *  SPLIT_K:       the K range is split across workgroups; each split writes
+ *                 its fp32 Gate/Up partial sums to the workspace and a second
+ *                 kernel adds them in fixed split order 0..S-1 BEFORE SiLU,
+ *                 then applies the epilogue; for small M, where output tiles
+ *                 alone cannot fill the GPU (the occupancy problem of
+ *                 [Summary: Methodology] Kernel-2, "Optimization").
  *  DECODE:        M <= 64 only.  Weight streaming: one workgroup per 16 output
  *                 columns reads their Gate and Up weight rows once, its waves
  *                 split K and add their fp32 partials in LDS in fixed order
@@ -143,12 +144,11 @@ swiglu_status swiglu_unpack_weights(const swiglu_bf16 *Wp, swiglu_bf16 *W1,
  * (one GEMM over the fused weight, SiLU(Gate) (.) Up applied to each pair of
  * accumulators before the store).
  *   A [M,K] bf16, Wp (swiglu_packed_bytes(K,N) bytes), Y [M,N] bf16 (device).
- *   workspace: device scratch for SWIGLU_VARIANT_SPLIT_K (fp32 partials and
- *     per-tile counters); may be NULL when swiglu_workspace_bytes() returns 0
- *     for the chosen variant.  The counters must be zero before the FIRST use of
- *     a workspace (hipMemset it once); every call leaves them zero again, so no
- *     per-call clearing is needed.  Concurrent calls must not share a
- *     workspace.
+ *   workspace: device scratch for SWIGLU_VARIANT_SPLIT_K: fp32 partial sums,
+ *     splits x M x 2N floats (Gate at column n, Up at column N + n of each
+ *     split's [M, 2N] slab).  May be NULL when swiglu_workspace_bytes() returns
+ *     0 for the chosen variant.  Its contents on entry do not matter (no
+ *     clearing needed); calls that may run concurrently must not share one.
  *   variant: a swiglu_variant; AUTO lets the library choose.
  * swiglu_workspace_bytes: bytes of workspace the call needs for (M,K,N,variant)
  *   (for AUTO: the requirement of the variant AUTO would pick).

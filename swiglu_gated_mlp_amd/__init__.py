@@ -184,11 +184,9 @@ def swiglu_choose_variant(M: int, K: int, N: int) -> int:
 
 
 class Workspace:
-    """Zero-initialised device scratch for the split-K schedule, grown on demand.
-
-    The library leaves its arrival counters at zero after every call, so a
-    workspace only needs clearing when it is (re)allocated.  One Workspace must
-    not be shared by calls that may run concurrently."""
+    """Device scratch for the split-K schedule (fp32 partial sums), grown on
+    demand.  Its contents never need clearing.  One Workspace must not be
+    shared by calls that may run concurrently."""
 
     def __init__(self, device=None):
         self.device = torch.device(device or "cuda")
@@ -198,7 +196,7 @@ class Workspace:
         if nbytes == 0:
             return None
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         return self.buf
 
 
@@ -218,8 +216,8 @@ def swiglu_fused_packed(A: torch.Tensor, Wp: torch.Tensor, N: int, Y: torch.Tens
                         stream=None) -> torch.Tensor:
     """Y = SiLU(A W1) * (A W2) from packed weights; returns Y [M,N] bf16.
 
-    ``workspace`` may be a zero-initialised uint8 tensor, a Workspace, or None
-    (a cached per-stream Workspace is used)."""
+    ``workspace`` may be a uint8 tensor of at least swiglu_workspace_bytes()
+    bytes, a Workspace, or None (a cached per-stream Workspace is used)."""
     M, K = A.shape
     if isinstance(variant, str):
         variant = VARIANTS[variant]

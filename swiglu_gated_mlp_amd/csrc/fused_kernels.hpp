@@ -40,6 +40,7 @@ namespace swk {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -106,14 +107,72 @@ struct FusedArgs {
     const uint16_t* W1;   // [K,N] row-major, or the packed weights
     const uint16_t* W2;   // [K,N] row-major (unused when packed)
     uint16_t* Y;          // [M,N]
-    float* part;          // split-K partials (fp32)
-    unsigned* counters;   // split-K arrival counters, one per output tile
+    float* part;          // split-K partials (fp32, [split][M][2N])
     int M, K, N;
     int tiles_m, tiles_n;
     int splits;           // number of K splits (1 = none)
     int kb_per_split;     // K blocks (of 64) per split
     int KB;               // ceil(K / 64)
 };
+
+// ---------------------------------------------------------------------------
+// Split-K partials.  Layout [split][M][2N] fp32: the Gate sum of (m, n) at
+// column n, the Up sum at column N + n.  Each lane owns four consecutive
+// columns of one token per 32x32 accumulator block, so it writes 16 bytes of
+// Gate and 16 bytes of Up per block.  Rows >= M and columns >= N are skipped.
+// ---------------------------------------------------------------------------
+template <int TM, int TN>
+__device__ __forceinline__ void store_partials(const f32x16 (&acc)[2][TM][TN], float* part, int split,
+                                               int M, int N, int row0, int col0, int lane) {
+    float* base = part + (size_t)split * M * (2 * (size_t)N);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int m = row0 + i * 32 + (lane & 31);
+        if (m >= M) continue;
+        float* prow = base + (size_t)m * (2 * (size_t)N);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = col0 + j * 32 + 8 * q + 4 * (lane >> 5);
+                if (n >= N) continue;
+                f32x4 g, u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    g[e] = acc[0][i][j][4 * q + e];
+                    u[e] = acc[1][i][j][4 * q + e];
+                }
+                *reinterpret_cast<f32x4*>(prow + n) = g;
+                *reinterpret_cast<f32x4*>(prow + N + n) = u;
+            }
+    }
+}
+
+// Y[m, n..n+3] = bf16(SiLU(sum_s G_s) * sum_s U_s), splits added in order
+// 0..S-1 (so the result does not depend on which workgroup finished first).
+// One thread per 4 outputs, grid-stride.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                            uint16_t* __restrict__ Y, int M, int N,
+                                                            int S) {
+    const long long groups = (long long)M * (N / 4);
+    const size_t split_stride = (size_t)M * 2 * (size_t)N;
+    for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < groups;
+         t += (long long)gridDim.x * blockDim.x) {
+        const int m = (int)(t / (N / 4));
+        const int n = (int)(t % (N / 4)) * 4;
+        const float* src = part + (size_t)m * 2 * (size_t)N + n;
+        f32x4 g = *reinterpret_cast<const f32x4*>(src);
+        f32x4 u = *reinterpret_cast<const f32x4*>(src + N);
+        for (int s2 = 1; s2 < S; ++s2) {
+            g += *reinterpret_cast<const f32x4*>(src + s2 * split_stride);
+            u += *reinterpret_cast<const f32x4*>(src + s2 * split_stride + N);
+        }
+        u32x2 out;
+        out[0] = pack2(silu_f(g[0]) * u[0], silu_f(g[1]) * u[1]);
+        out[1] = pack2(silu_f(g[2]) * u[2], silu_f(g[3]) * u[3]);
+        *reinterpret_cast<u32x2*>(Y + (size_t)m * N + n) = out;
+    }
+}
 
 // ---------------------------------------------------------------------------
 // The fused (DUAL) / single-GEMM (!DUAL) tile kernel.
@@ -306,55 +365,10 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_tile_kernel(FusedArgs p) {
         }
     }
 
-    // ---- split-K: publish partials, last arrival reduces ------------------------
+    // ---- split-K: fp32 partials to the workspace, reduced by splitk_reduce_kernel ---
     if constexpr (SPLIT) {
-        constexpr int ACC = NG * TM * TN * 16;
-        if (S > 1) {
-            float* base = p.part + (size_t)tile * S * (ACC * NT);
-            float* mine = base + (size_t)split * (ACC * NT);
-#pragma unroll
-            for (int g = 0; g < NG; ++g)
-#pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    const bool row_ok = m0 + wrow0 + i * 32 + (lane & 31) < M;
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int idx = ((g * TM + i) * TN + j) * 16 + r;
-                            if (row_ok) mine[(size_t)idx * NT + tid] = acc[g][i][j][r];
-                        }
-                }
-            __threadfence();
-            __syncthreads();
-            __shared__ unsigned s_last;
-            if (tid == 0) {
-                const unsigned prev = atomicAdd(p.counters + tile, 1u);
-                s_last = (prev == (unsigned)(S - 1)) ? 1u : 0u;
-            }
-            __syncthreads();
-            if (!s_last) return;
-            __threadfence();
-#pragma unroll
-            for (int g = 0; g < NG; ++g)
-#pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    const bool row_ok = m0 + wrow0 + i * 32 + (lane & 31) < M;
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int idx = ((g * TM + i) * TN + j) * 16 + r;
-                            float v = 0.0f;
-                            if (row_ok) {
-                                for (int s = 0; s < S; ++s)
-                                    v += base[((size_t)s * ACC + idx) * NT + tid];
-                            }
-                            acc[g][i][j][r] = v;
-                        }
-                }
-            if (tid == 0) atomicExch(p.counters + tile, 0u);   // ready for the next call
-        }
+        store_partials<TM, TN>(acc, p.part, split, M, N, m0 + wrow0, n0 + wcol0, lane);
+        return;
     }
 
     // ---- epilogue: SiLU(Gate) * Up (or the plain GEMM value), bf16, store ---------
@@ -410,9 +424,8 @@ __device__ __forceinline__ void dma16(const uint16_t* gsrc, uint16_t* lds_dst) {
                                      (lds_void_ptr)(lds_dst), 16, 0, 0);
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool SPLIT>
 __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p) {
-    constexpr int NT = 64 * WM * WN;
     constexpr int NW = WM * WN;
     constexpr int NB = 2 * BN;                // Gate rows then Up rows
     constexpr int TM = BM / WM / 32;
@@ -434,7 +447,12 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
     const int wrow0 = wm * (BM / WM);
     const int wcol0 = wn * (BN / WN);
 
-    const int tile = xcd_remap(blockIdx.x, gridDim.x);
+    // logical id -> (output tile, K split); the splits of a tile are
+    // consecutive, so they and their reduction stay on one XCD
+    const int S = SPLIT ? p.splits : 1;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int tile = SPLIT ? logical / S : logical;
+    const int split = SPLIT ? logical - tile * S : 0;
     int tm, tn;
     {
         const int per_group = GROUP_M * p.tiles_n;
@@ -450,6 +468,10 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
     const int M = p.M, K = p.K, N = p.N, KB = p.KB;
     const int jp = n0 / PACK_BN, ro = n0 % PACK_BN;
     const bool ragged_k = (K % BK) != 0;
+    // this workgroup's K blocks [kb_first, kb_last]; the host never makes an
+    // empty split
+    const int kb_first = SPLIT ? split * p.kb_per_split : 0;
+    const int kb_last = SPLIT ? min(KB, kb_first + p.kb_per_split) - 1 : KB - 1;
 
     // per-lane source offsets (elements), constant over K steps
     const int lrow = lane >> 3, lpc = lane & 7;
@@ -563,7 +585,7 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
     auto stage = [&](auto prefetch, auto ragged_next, int kb) {
         constexpr bool PF = decltype(prefetch)::value;
         constexpr bool RN = decltype(ragged_next)::value;
-        const int buf = kb & 1;
+        const int buf = (kb - kb_first) & 1;
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (PF) {
             if constexpr (RN) issue_a_regs(kb + 1, buf ^ 1);
@@ -598,26 +620,42 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    if (ragged_k && KB == 1) issue_a_regs(0, 0);
-    else issue_a(0, 0);
-    issue_b(0, 0);
+    const bool last_ragged = ragged_k && kb_last == KB - 1;
+    if (last_ragged && kb_first == kb_last) issue_a_regs(kb_first, 0);
+    else issue_a(kb_first, 0);
+    issue_b(kb_first, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     read_frags(0, 0, 0);
-    const int steady = KB - 1 - (ragged_k && KB >= 2 ? 1 : 0);
-    for (int kb = 0; kb < steady; ++kb) stage(std::true_type{}, std::false_type{}, kb);
-    if (ragged_k && KB >= 2) stage(std::true_type{}, std::true_type{}, KB - 2);
-    stage(std::false_type{}, std::false_type{}, KB - 1);
+    const bool rn = last_ragged && kb_last > kb_first;
+    const int steady_end = kb_last - (rn ? 1 : 0);
+    for (int kb = kb_first; kb < steady_end; ++kb) stage(std::true_type{}, std::false_type{}, kb);
+    if (rn) stage(std::true_type{}, std::true_type{}, kb_last - 1);
+    stage(std::false_type{}, std::false_type{}, kb_last);
+
+    // Split-K: this split's fp32 Gate/Up partial sums go to the workspace
+    // ([split][M][2N]: Gate at column n, Up at column N + n); splitk_reduce_kernel
+    // adds the splits in order 0..S-1 and applies the epilogue.
+    if constexpr (SPLIT) {
+        store_partials<TM, TN>(acc, p.part, split, M, N, m0 + wrow0, n0 + wcol0, lane);
+        return;
+    }
 
     // Epilogue: SiLU(Gate) * Up -> bf16, staged through LDS so the global
-    // stores are 16 bytes per lane over whole 128-byte row segments.  Every
-    // wave has finished reading the stage buffers (the last barrier came
-    // before the final sub-step, whose operands were already in registers),
-    // so buffer 0 holds the Y tile: each wave owns a disjoint
-    // (BM/WM) x (BN/WN) region, rows of 64 columns, chunks swizzled like the
-    // operand stages.
-    static_assert(BN / WN == 64, "epilogue staging assumes 64 columns per wave");
-    uint16_t* sY = smem + wave * (BM / WM) * 64;
+    // stores are 16 bytes per lane over whole row segments of the wave's
+    // sub-tile.  Every wave is done with the operand stages (the last barrier
+    // came before the final sub-step, whose operands were in registers, and a
+    // split's reduction reads only global memory), so the stage buffers hold
+    // the Y tile: each wave owns a disjoint (BM/WM) x CW region with rows
+    // padded by 16 bytes to spread the banks.
+    constexpr int CW = BN / WN;                 // columns per wave: 32 or 64
+    constexpr int PY = CW + 8;                  // padded row pitch (elements)
+    constexpr int CPR = CW / 8;                 // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;               // rows per wave-wide store
+    static_assert(CW == 32 || CW == 64, "epilogue handles 32 or 64 columns per wave");
+    static_assert(NW * (BM / WM) * PY <= 2 * STAGE, "epilogue staging fits the stage buffers");
+    __syncthreads();
+    uint16_t* sY = smem + wave * (BM / WM) * PY;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int r = i * 32 + (lane & 31);
@@ -632,19 +670,18 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
                 u32x2 out;
                 out[0] = pack2(v[0], v[1]);
                 out[1] = pack2(v[2], v[3]);
-                *reinterpret_cast<u32x2*>(sY + lds_off(r, q + 4 * j) + 4 * (lane >> 5)) = out;
+                *reinterpret_cast<u32x2*>(sY + r * PY + j * 32 + 8 * q + 4 * (lane >> 5)) = out;
             }
         }
     }
     __syncthreads();
 #pragma unroll
-    for (int t = 0; t < (BM / WM) / 8; ++t) {
-        const int r = t * 8 + (lane >> 3);
-        const int pc = lane & 7;
-        const int c = pc ^ swz(r);
+    for (int t = 0; t < (BM / WM) / RPI; ++t) {
+        const int r = t * RPI + lane / CPR;
+        const int c = lane % CPR;
         const int m = m0 + wrow0 + r;
         const int n = n0 + wcol0 + 8 * c;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(sY + r * 64 + pc * 8);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sY + r * PY + 8 * c);
         if (m < M && n < N) *reinterpret_cast<u32x4*>(p.Y + (size_t)m * N + n) = v;
     }
 }
@@ -664,8 +701,6 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
 //   the epilogue applies SiLU(Gate) * Up.
 //   MT 16-token tiles cover M <= 16 * MT.
 // ---------------------------------------------------------------------------
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
 struct DecodeArgs {
     const uint16_t* A;    // [M,K]
     const uint16_t* Wp;   // packed weights

@@ -91,26 +91,29 @@ int cu_count_now() {
 // ---------------------------------------------------------------------------
 // kernel configurations
 // ---------------------------------------------------------------------------
+// Output tile for a token count and schedule.  M <= 64 (forced data-parallel
+// or split-K; AUTO uses the decode kernel there): 32/64-row register-path
+// tiles.  Split-K above that: 128 x 64 tiles (two workgroups fit a CU, and a
+// narrow tile gives more tiles to split).  Data-parallel: 128 x 128 up to
+// 2048 tokens, then 256 x 128 (each wave 128 rows x 64 columns of Gate and Up).
 struct TileCfg {
     int BM, BN;
 };
 
-// Output tile height for a token count.  Small M keeps the MFMA waste and the
-// clamped-row reads low; large M takes the biggest tile the register file and
-// LDS allow (BM 256: each wave holds 128 rows x 64 columns of Gate and Up).
-TileCfg packed_tile_for(int64_t M) {
+TileCfg packed_tile_for(int64_t M, int variant) {
     if (M <= 32) return {32, 128};
     if (M <= 64) return {64, 128};
+    if (variant == SWIGLU_VARIANT_SPLIT_K) return {128, 64};
     if (M <= 2048) return {128, 128};
     return {256, 128};
 }
 
-// Split-K workspace = a fixed-size counter region, then the fp32 partials.
-// The counter region has the same size and place for every shape, so a
-// workspace that served one shape can serve another: each call leaves every
-// counter it used at zero, and no call ever writes partials over a counter.
-constexpr size_t kCounterBytes = 64 * 1024;
-constexpr int kMaxSplitTiles = (int)(kCounterBytes / sizeof(unsigned));
+// workgroups per CU the split count aims for
+constexpr int kSplitWavesPerCu = 2;
+
+// Split-K above this many output tiles is pointless (the tiles alone fill
+// the device many times over).
+constexpr int kMaxSplitTiles = 16384;
 
 struct Plan {
     TileCfg t;
@@ -125,24 +128,27 @@ bool variant_known(int v) { return v >= SWIGLU_VARIANT_AUTO && v <= SWIGLU_VARIA
 
 Plan make_plan(int64_t M, int64_t K, int64_t N, int variant, int cus) {
     Plan p{};
-    p.t = packed_tile_for(M);
-    p.tiles_m = (int)ceil_div(M, p.t.BM);
-    p.tiles_n = (int)ceil_div(N, p.t.BN);
-    p.tiles = p.tiles_m * p.tiles_n;
-    p.KB = (int)ceil_div(K, swk::BK);
     if (cus <= 0) cus = 256;
+    p.KB = (int)ceil_div(K, swk::BK);
     int v = variant;
     if (v == SWIGLU_VARIANT_AUTO) {
-        if (M <= kDecodeMaxM)
+        if (M <= kDecodeMaxM) {
             v = SWIGLU_VARIANT_DECODE;
-        else
-            v = (p.tiles >= cus || p.KB < 4) ? SWIGLU_VARIANT_DATA_PARALLEL : SWIGLU_VARIANT_SPLIT_K;
+        } else {
+            const TileCfg dp = packed_tile_for(M, SWIGLU_VARIANT_DATA_PARALLEL);
+            const int64_t dp_tiles = ceil_div(M, dp.BM) * ceil_div(N, dp.BN);
+            v = (dp_tiles >= cus || p.KB < 4) ? SWIGLU_VARIANT_DATA_PARALLEL : SWIGLU_VARIANT_SPLIT_K;
+        }
     }
     p.variant = v;
     p.decode_mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    p.t = packed_tile_for(M, v);
+    p.tiles_m = (int)ceil_div(M, p.t.BM);
+    p.tiles_n = (int)ceil_div(N, p.t.BN);
+    p.tiles = p.tiles_m * p.tiles_n;
     if (v == SWIGLU_VARIANT_SPLIT_K && p.tiles <= kMaxSplitTiles) {
-        // about two workgroups per CU, at least two K blocks per split
-        int s = (int)ceil_div(2 * cus, p.tiles);
+        // about kSplitWavesPerCu workgroups per CU, at least two K blocks per split
+        int s = (int)ceil_div((int64_t)kSplitWavesPerCu * cus, p.tiles);
         s = std::max(1, std::min(s, p.KB / 2 > 0 ? p.KB / 2 : 1));
         p.kb_per_split = (int)ceil_div(p.KB, s);
         p.splits = (int)ceil_div(p.KB, p.kb_per_split);
@@ -153,10 +159,10 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int variant, int cus) {
     return p;
 }
 
-size_t split_workspace_bytes(const Plan& p) {
+// Split-K workspace: fp32 Gate and Up partial sums, [split][M][2N].
+size_t split_workspace_bytes(const Plan& p, int64_t M, int64_t N) {
     if (p.variant != SWIGLU_VARIANT_SPLIT_K || p.splits <= 1) return 0;
-    const size_t partials = (size_t)p.tiles * p.splits * 2 * p.t.BM * p.t.BN * sizeof(float);
-    return kCounterBytes + partials;
+    return (size_t)p.splits * (size_t)M * 2 * (size_t)N * sizeof(float);
 }
 
 template <int BM, int BN, int WM, int WN, bool DUAL, bool PACKED, bool SPLIT>
@@ -178,9 +184,9 @@ hipError_t launch_decode(const swk::DecodeArgs& a, int groups, hipStream_t s) {
     return hipLaunchKernel(fn, dim3(groups), dim3(256), kargs, 0, s);
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool SPLIT>
 hipError_t launch_prefill(const swk::FusedArgs& a, int grid, hipStream_t s) {
-    const void* fn = reinterpret_cast<const void*>(&swk::fused_prefill_kernel<BM, BN, WM, WN>);
+    const void* fn = reinterpret_cast<const void*>(&swk::fused_prefill_kernel<BM, BN, WM, WN, SPLIT>);
     swk::FusedArgs args = a;
     void* kargs[] = {&args};
     return hipLaunchKernel(fn, dim3(grid), dim3(64 * WM * WN), kargs, 0, s);
@@ -208,11 +214,14 @@ hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) 
             return split ? launch_tile<64, 128, 2, 2, true, true, true>(a, grid, s)
                          : launch_tile<64, 128, 2, 2, true, true, false>(a, grid, s);
         case 128:
-            return split ? launch_tile<128, 128, 2, 2, true, true, true>(a, grid, s)
-                         : launch_prefill<128, 128, 2, 2>(a, grid, s);
+            if (p.t.BN == 64)
+                return split ? launch_prefill<128, 64, 2, 2, true>(a, grid, s)
+                             : launch_prefill<128, 64, 2, 2, false>(a, grid, s);
+            return split ? launch_prefill<128, 128, 2, 2, true>(a, grid, s)
+                         : launch_prefill<128, 128, 2, 2, false>(a, grid, s);
         default:
-            return split ? launch_tile<256, 128, 2, 2, true, true, true>(a, grid, s)
-                         : launch_prefill<256, 128, 2, 2>(a, grid, s);
+            return split ? launch_prefill<256, 128, 2, 2, true>(a, grid, s)
+                         : launch_prefill<256, 128, 2, 2, false>(a, grid, s);
     }
 }
 
@@ -328,7 +337,7 @@ int swiglu_choose_variant(int64_t M, int64_t K, int64_t N) {
 size_t swiglu_workspace_bytes(int64_t M, int64_t K, int64_t N, int variant) {
     if (check_shape(M, K, N) != SWIGLU_OK || M == 0) return 0;
     if (!variant_known(variant)) return 0;
-    return split_workspace_bytes(make_plan(M, K, N, variant, cu_count_now()));
+    return split_workspace_bytes(make_plan(M, K, N, variant, cu_count_now()), M, N);
 }
 
 swiglu_status swiglu_fused_packed(const swiglu_bf16* A, const swiglu_bf16* Wp, swiglu_bf16* Y,
@@ -346,7 +355,7 @@ swiglu_status swiglu_fused_packed(const swiglu_bf16* A, const swiglu_bf16* Wp, s
         return SWIGLU_ERR_ALIASING;
 
     const Plan p = make_plan(M, K, N, variant, cu_count_now());
-    const size_t need = split_workspace_bytes(p);
+    const size_t need = split_workspace_bytes(p, M, N);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return SWIGLU_ERR_WORKSPACE;
         if (!aligned16(workspace)) return SWIGLU_ERR_MISALIGNED;
@@ -361,14 +370,22 @@ swiglu_status swiglu_fused_packed(const swiglu_bf16* A, const swiglu_bf16* Wp, s
     a.M = (int)M; a.K = (int)K; a.N = (int)N;
     a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n;
     a.splits = p.splits; a.kb_per_split = p.kb_per_split; a.KB = p.KB;
-    if (need > 0) {
-        a.counters = reinterpret_cast<unsigned*>(workspace);
-        a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + kCounterBytes);
-    }
+    if (need > 0) a.part = reinterpret_cast<float*>(workspace);
     if (log_enabled())
         std::fprintf(stderr, "[swiglu] fused_packed M=%lld K=%lld N=%lld variant=%d tile=%dx%d tiles=%d splits=%d\n",
                      (long long)M, (long long)K, (long long)N, p.variant, p.t.BM, p.t.BN, p.tiles, p.splits);
     hipError_t e = launch_packed(a, p, (hipStream_t)stream);
+    if (e == hipSuccess && p.splits > 1) {
+        const int cus = std::max(1, cu_count_now());
+        const long long groups = (long long)M * (N / 4);
+        const int grid = (int)std::max<long long>(1, std::min<long long>(ceil_div(groups, 256), (long long)cus * 8));
+        int Mi = (int)M, Ni = (int)N, Si = p.splits;
+        const float* part = a.part;
+        uint16_t* yp = a.Y;
+        void* args[] = {(void*)&part, (void*)&yp, &Mi, &Ni, &Si};
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&swk::splitk_reduce_kernel), dim3(grid), dim3(256),
+                            args, 0, (hipStream_t)stream);
+    }
     return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
 }
 

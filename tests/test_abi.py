@@ -109,14 +109,16 @@ def test_unfused_errors():
     assert L.swiglu_unfused(A_, W1_, W2_, None, WP_, WS_, 4, 64, 64, None) == NULLP
 
 
-def test_workspace_counts_partials_and_counters():
+def test_workspace_holds_fp32_partials():
     L = sw.lib()
-    # split-K workspace covers fp32 Gate+Up partials of every (tile, split) plus
-    # one counter per tile; it is zero for the data-parallel schedule
+    # split-K workspace = splits x M x 2N fp32 partial sums; zero for the
+    # data-parallel and decode schedules
     for M, K, N in [(1, 3584, 18944), (16, 3584, 18944), (128, 3584, 18944), (32, 8192, 29568)]:
         b = L.swiglu_workspace_bytes(M, K, N, 2)
-        assert b % 4 == 0 and b > 0
+        per_split = M * 2 * N * 4
+        assert b > 0 and b % per_split == 0 and 2 <= b // per_split <= K // 128
         assert L.swiglu_workspace_bytes(M, K, N, 1) == 0
+        assert L.swiglu_workspace_bytes(M, K, N, 3) == 0
 
 
 def test_probe_argument_errors():

@@ -251,9 +251,9 @@ def test_edge_cases(dev):
 
 
 def test_split_workspace_reused_across_shapes(dev):
-    """One workspace serves split-K calls of different tile counts in a row:
-    the arrival counters live in a fixed region that partials never touch, and
-    every call leaves them at zero."""
+    """One workspace serves split-K calls of different shapes in a row, and
+    its earlier contents (partials of another shape, or garbage) never leak
+    into a result."""
     ws = sw.Workspace(dev)
     shapes = [(128, 2048, 1024), (128, 2048, 18944), (128, 1024, 4864), (128, 2048, 18944), (96, 512, 8192)]
     for i, (M, K, N) in enumerate(shapes):
@@ -263,5 +263,4 @@ def test_split_workspace_reused_across_shapes(dev):
         torch.cuda.synchronize()
         rows = sample_rows(M, 4)
         check_close(gpu_bits(Y)[rows], oracle_rows(A, W1, W2, rows), "split reuse %s" % ((M, K, N),))
-        head = ws.buf[:64 * 1024].view(torch.int32)
-        assert int(head.abs().sum()) == 0, "arrival counters not left at zero"
+        ws.buf.fill_(0x7F)      # NaN-patterned leftovers must not matter to the next call
