@@ -424,19 +424,51 @@ __device__ __forceinline__ void dma16(const uint16_t* gsrc, uint16_t* lds_dst) {
                                      (lds_void_ptr)(lds_dst), 16, 0, 0);
 }
 
-template <int BM, int BN, int WM, int WN, bool SPLIT>
+// Weight sources of the direct-load kernel.
+enum WeightSource : int {
+    W_PACKED = 0,      // packed [W1|W2] tiles, rows K-contiguous; dual Gate/Up
+    W_ROW_DUAL = 1,    // row-major W1 and W2 [K,N]; dual Gate/Up
+    W_ROW_SINGLE = 2   // row-major W [K,N]; plain GEMM, bf16 output
+};
+
+// Row-major weight stage in LDS: 64 K-rows of NB columns (N-contiguous); the
+// 16-byte chunks of row k are XOR-swizzled by (k & 3) << 2, which keeps the
+// transposing fragment reads below free of bank conflicts (each 16-lane group
+// reads 4 consecutive rows x 32 bytes, two groups read 16 columns apart).
+template <int NB>
+__device__ __forceinline__ int rm_off(int k, int col) {
+    return k * NB + ((((col >> 3) ^ ((k & 3) << 2))) << 3) + (col & 7);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// (i & 3) of the 8-byte pieces addressed by lanes 4e + (i >> 2), e = 0..3.
+__device__ __forceinline__ s16x4 ds_read_tr16(const uint16_t* lds) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_ptr)((__attribute__((address_space(3))) uint16_t*)(lds)));
+}
+
+template <int BM, int BN, int WM, int WN, bool SPLIT, int WSRC>
 __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p) {
+    constexpr bool PACKED_W = WSRC == W_PACKED;
+    constexpr int NG = WSRC == W_ROW_SINGLE ? 1 : 2;   // accumulator groups (Gate, Up)
     constexpr int NW = WM * WN;
-    constexpr int NB = 2 * BN;                // Gate rows then Up rows
+    constexpr int NB = NG * BN;               // weight columns (or packed rows) per stage
     constexpr int TM = BM / WM / 32;
     constexpr int TN = BN / WN / 32;
     constexpr int A_INS = BM / 8 / NW;        // 1 KiB direct loads per wave per stage (A)
     constexpr int B_INS = NB / 8 / NW;        // ... (weights)
     constexpr int STAGE = (BM + NB) * BK;     // elements per LDS stage
+    constexpr int CPRB = NB / 8;              // row-major weights: 16-byte chunks per K-row
+    constexpr int RPIB = 64 / CPRB;           // ... K-rows per wave-wide direct load
     constexpr int GROUP_M = 8;
     static_assert(TM >= 1 && TN >= 1, "tile too small for the wave grid");
     static_assert(A_INS >= 1 && B_INS >= 1 && (BM / 8) % NW == 0 && (NB / 8) % NW == 0, "load split");
-    static_assert(PACK_BN % BN == 0, "tile must divide the packed tile");
+    static_assert(!PACKED_W || PACK_BN % BN == 0, "tile must divide the packed tile");
+    static_assert(PACKED_W || (CPRB >= 16 && CPRB <= 64), "row-major weight rows of 128..512 columns");
+    static_assert(!SPLIT || NG == 2, "split-K is a fused schedule");
 
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
 
@@ -448,7 +480,7 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
     const int wcol0 = wn * (BN / WN);
 
     // logical id -> (output tile, K split); the splits of a tile are
-    // consecutive, so they and their reduction stay on one XCD
+    // consecutive, so they stay on one XCD
     const int S = SPLIT ? p.splits : 1;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int tile = SPLIT ? logical / S : logical;
@@ -466,30 +498,45 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
     const int m0 = tm * BM;
     const int n0 = tn * BN;
     const int M = p.M, K = p.K, N = p.N, KB = p.KB;
-    const int jp = n0 / PACK_BN, ro = n0 % PACK_BN;
     const bool ragged_k = (K % BK) != 0;
     // this workgroup's K blocks [kb_first, kb_last]; the host never makes an
     // empty split
     const int kb_first = SPLIT ? split * p.kb_per_split : 0;
     const int kb_last = SPLIT ? min(KB, kb_first + p.kb_per_split) - 1 : KB - 1;
 
-    // per-lane source offsets (elements), constant over K steps
+    // per-lane source addresses, constant over K steps
     const int lrow = lane >> 3, lpc = lane & 7;
     const uint16_t* a_src[A_INS];
-    int b_off[B_INS];
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
         const int r = (wave * A_INS + i) * 8 + lrow;
         const int grow = min(m0 + r, M - 1);
         a_src[i] = p.A + (size_t)grow * K + 8 * (lpc ^ swz(r));
     }
+    // packed: element offset within a 64-deep block; row-major: pointer to the
+    // lane's 16 bytes in K-row r of the tile (advanced by k0 rows per stage)
+    int b_off[PACKED_W ? B_INS : 1];
+    const uint16_t* b_src[PACKED_W ? 1 : B_INS];
+    const uint16_t* wtile = p.W1;
+    if constexpr (PACKED_W) {
+        const int jp = n0 / PACK_BN, ro = n0 % PACK_BN;
 #pragma unroll
-    for (int i = 0; i < B_INS; ++i) {
-        const int r = (wave * B_INS + i) * 8 + lrow;
-        const int prow = r < BN ? ro + r : PACK_BN + ro + (r - BN);
-        b_off[i] = prow * PACK_BK + 8 * (lpc ^ swz(r));
+        for (int i = 0; i < B_INS; ++i) {
+            const int r = (wave * B_INS + i) * 8 + lrow;
+            const int prow = r < BN ? ro + r : PACK_BN + ro + (r - BN);
+            b_off[i] = prow * PACK_BK + 8 * (lpc ^ swz(r));
+        }
+        wtile = p.W1 + (size_t)jp * KB * (PACK_ROWS * PACK_BK);
+    } else {
+#pragma unroll
+        for (int i = 0; i < B_INS; ++i) {
+            const int r = (wave * B_INS + i) * RPIB + lane / CPRB;   // K-row within the stage
+            const int c = 8 * ((lane % CPRB) ^ ((r & 3) << 2));      // logical column in the stage
+            const bool up = NG == 2 && c >= BN;
+            const int col = min(n0 + (up ? c - BN : c), N - 8);
+            b_src[i] = (up ? p.W2 : p.W1) + (size_t)r * N + col;
+        }
     }
-    const uint16_t* wtile = p.W1 + (size_t)jp * KB * (PACK_ROWS * PACK_BK);
 
     // activation columns beyond K (ragged last block) are zero-filled through
     // registers; every other stage is a direct load
@@ -513,14 +560,37 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
     };
     auto issue_b = [&](int kb, int buf) {
         uint16_t* sB = smem + buf * STAGE + BM * BK;
-        const uint16_t* blk = wtile + (size_t)kb * (PACK_ROWS * PACK_BK);
+        if constexpr (PACKED_W) {
+            const uint16_t* blk = wtile + (size_t)kb * (PACK_ROWS * PACK_BK);
 #pragma unroll
-        for (int i = 0; i < B_INS; ++i) dma16(blk + b_off[i], sB + (wave * B_INS + i) * 512);
+            for (int i = 0; i < B_INS; ++i) dma16(blk + b_off[i], sB + (wave * B_INS + i) * 512);
+        } else {
+            const size_t k0N = (size_t)kb * BK * N;
+#pragma unroll
+            for (int i = 0; i < B_INS; ++i) dma16(b_src[i] + k0N, sB + (wave * B_INS + i) * 512);
+        }
+    };
+    // row-major weights, ragged last block: K-rows beyond K are zero-filled
+    // through registers (packed weights are already zero there)
+    auto issue_b_regs = [&](int kb, int buf) {
+        if constexpr (!PACKED_W) {
+            uint16_t* sB = smem + buf * STAGE + BM * BK;
+            const size_t k0N = (size_t)kb * BK * N;
+#pragma unroll
+            for (int i = 0; i < B_INS; ++i) {
+                const int r = (wave * B_INS + i) * RPIB + lane / CPRB;
+                u32x4 v = u32x4{0u, 0u, 0u, 0u};
+                if (kb * BK + r < K) v = ld16(b_src[i] + k0N);
+                *reinterpret_cast<u32x4*>(sB + ((wave * B_INS + i) * 64 + lane) * 8) = v;
+            }
+        } else {
+            issue_b(kb, buf);
+        }
     };
 
-    f32x16 acc[2][TM][TN];
+    f32x16 acc[NG][TM][TN];
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < NG; ++g)
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -528,7 +598,7 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[g][i][j][r] = 0.0f;
 
-    bf16x8 fa[2][TM], fb[2][2][TN];
+    bf16x8 fa[2][TM], fb[2][NG][TN];
     auto read_frags = [&](int buf, int kk, int set) {
         const uint16_t* sA = smem + buf * STAGE;
         const uint16_t* sB = sA + BM * BK;
@@ -536,16 +606,33 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
 #pragma unroll
         for (int i = 0; i < TM; ++i)
             fa[set][i] = *reinterpret_cast<const bf16x8*>(sA + lds_off(wrow0 + i * 32 + (lane & 31), c));
+        if constexpr (PACKED_W) {
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
+            for (int g = 0; g < NG; ++g)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                fb[set][g][j] = *reinterpret_cast<const bf16x8*>(
-                    sB + lds_off(g * BN + wcol0 + j * 32 + (lane & 31), c));
+                for (int j = 0; j < TN; ++j)
+                    fb[set][g][j] = *reinterpret_cast<const bf16x8*>(
+                        sB + lds_off(g * BN + wcol0 + j * 32 + (lane & 31), c));
+        } else {
+            // two transposing reads give lane l the 8 K-consecutive values
+            // W[16kk + 8(l>>5) + 0..7][column l & 31 of the fragment]
+            const int kr = kk * 16 + 8 * (lane >> 5) + ((lane & 15) >> 2);
+            const int cl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int col = g * BN + wcol0 + j * 32 + cl;
+                    const s16x4 lo = ds_read_tr16(sB + rm_off<NB>(kr, col));
+                    const s16x4 hi = ds_read_tr16(sB + rm_off<NB>(kr + 4, col));
+                    const s16x4 both[2] = {lo, hi};
+                    fb[set][g][j] = __builtin_bit_cast(bf16x8, both);
+                }
+        }
     };
     auto mfmas = [&](int set) {
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
+        for (int g = 0; g < NG; ++g)
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -558,30 +645,29 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
     // the fragments of sub-step kk+1 are read while the MFMAs of kk run
     // (each read slotted between MFMAs), and the one barrier per stage sits
     // before the last sub-step's MFMAs, so the first reads of the next stage
-    // overlap those 16 MFMAs instead of stalling the matrix pipe.
-    constexpr int NFRAG = TM + 2 * TN;          // ds_read_b128 per sub-step
-    constexpr int NMFMA = 2 * TM * TN;          // MFMAs per sub-step
-    static_assert(NMFMA >= NFRAG, "sub-step needs at least one MFMA per fragment read");
-    // [MFMA, LDS read] x NFRAG, then the remaining MFMAs: the sub-step opens
-    // with an MFMA (its operands were read a whole sub-step earlier) and its
-    // last read is issued well before the next sub-step needs it.
+    // overlap those MFMAs instead of stalling the matrix pipe.
+    constexpr int NFRAG = TM + (PACKED_W ? 1 : 2) * NG * TN;   // LDS reads per sub-step
+    constexpr int NMFMA = NG * TM * TN;                          // MFMAs per sub-step
+    constexpr int NSLOT = NMFMA > NFRAG ? NMFMA : NFRAG;
+    // [MFMA, LDS read (, direct load)] pairs, then whatever is left: the
+    // sub-step opens with an MFMA (its operands were read a whole sub-step
+    // earlier) and its reads are issued early enough for the next sub-step.
     auto interleave = [&](auto ndma) {
         constexpr int ND = decltype(ndma)::value;
 #pragma unroll
-        for (int t = 0; t < NFRAG; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-            if (t < ND) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // direct load
+        for (int t = 0; t < NSLOT; ++t) {
+            if (t < NMFMA) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            if (t < NFRAG) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+            if (t < ND) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // direct load
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NFRAG, 0);
     };
     using Z = std::integral_constant<int, 0>;
-    using NA = std::integral_constant<int, A_INS>;
-    using NB_ = std::integral_constant<int, B_INS>;
+    using NA = std::integral_constant<int, (A_INS < NSLOT ? A_INS : NSLOT)>;
+    using NB_ = std::integral_constant<int, (B_INS < NSLOT ? B_INS : NSLOT)>;
 
     // One 64-deep stage.  PREFETCH: stage kb+1 is loaded into the other LDS
-    // buffer during this one (the activation part through registers when
-    // RAGGED_NEXT, i.e. stage kb+1 is a ragged last block).
+    // buffer during this one (through registers when RAGGED_NEXT, i.e. stage
+    // kb+1 is a ragged last block).
     auto stage = [&](auto prefetch, auto ragged_next, int kb) {
         constexpr bool PF = decltype(prefetch)::value;
         constexpr bool RN = decltype(ragged_next)::value;
@@ -596,10 +682,13 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
         if constexpr (PF && !RN) interleave(NA{});
         else interleave(Z{});
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (PF) issue_b(kb + 1, buf ^ 1);
+        if constexpr (PF) {
+            if constexpr (RN && !PACKED_W) issue_b_regs(kb + 1, buf ^ 1);
+            else issue_b(kb + 1, buf ^ 1);
+        }
         read_frags(buf, 2, 0);
         mfmas(1);
-        if constexpr (PF) interleave(NB_{});
+        if constexpr (PF && (PACKED_W || !RN)) interleave(NB_{});
         else interleave(Z{});
         __builtin_amdgcn_sched_barrier(0);
         read_frags(buf, 3, 1);
@@ -621,9 +710,13 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
     };
 
     const bool last_ragged = ragged_k && kb_last == KB - 1;
-    if (last_ragged && kb_first == kb_last) issue_a_regs(kb_first, 0);
-    else issue_a(kb_first, 0);
-    issue_b(kb_first, 0);
+    if (last_ragged && kb_first == kb_last) {
+        issue_a_regs(kb_first, 0);
+        issue_b_regs(kb_first, 0);
+    } else {
+        issue_a(kb_first, 0);
+        issue_b(kb_first, 0);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     read_frags(0, 0, 0);
@@ -641,19 +734,22 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
         return;
     }
 
-    // Epilogue: SiLU(Gate) * Up -> bf16, staged through LDS so the global
-    // stores are 16 bytes per lane over whole row segments of the wave's
-    // sub-tile.  Every wave is done with the operand stages (the last barrier
-    // came before the final sub-step, whose operands were in registers, and a
-    // split's reduction reads only global memory), so the stage buffers hold
-    // the Y tile: each wave owns a disjoint (BM/WM) x CW region with rows
-    // padded by 16 bytes to spread the banks.
-    constexpr int CW = BN / WN;                 // columns per wave: 32 or 64
-    constexpr int PY = CW + 8;                  // padded row pitch (elements)
+    // Epilogue: SiLU(Gate) * Up (or the plain GEMM value) -> bf16, staged
+    // through LDS so the global stores are 16 bytes per lane over whole row
+    // segments of the wave's sub-tile.  Every wave is done with the operand
+    // stages (the last barrier came before the final sub-step, whose operands
+    // were in registers), so the stage buffers hold the Y tile: each wave owns
+    // a disjoint (BM/WM) x CW region; rows of up to 64 columns are padded by
+    // 16 bytes, 128-column rows have their chunks XOR-swizzled by row.
+    constexpr int CW = BN / WN;                 // columns per wave
+    constexpr int PY = CW == 128 ? CW : CW + 8; // row pitch (elements)
     constexpr int CPR = CW / 8;                 // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;               // rows per wave-wide store
-    static_assert(CW == 32 || CW == 64, "epilogue handles 32 or 64 columns per wave");
+    static_assert(CW == 32 || CW == 64 || CW == 128, "epilogue handles 32, 64 or 128 columns per wave");
     static_assert(NW * (BM / WM) * PY <= 2 * STAGE, "epilogue staging fits the stage buffers");
+    auto y_off = [&](int r, int chunk) {
+        return r * PY + 8 * (CW == 128 ? (chunk ^ (r & 15)) : chunk);
+    };
     __syncthreads();
     uint16_t* sY = smem + wave * (BM / WM) * PY;
 #pragma unroll
@@ -665,12 +761,16 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
             for (int q = 0; q < 4; ++q) {
                 float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[e] = silu_f(acc[0][i][j][4 * q + e]) * acc[1][i][j][4 * q + e];
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (NG == 2)
+                        v[e] = silu_f(acc[0][i][j][4 * q + e]) * acc[NG - 1][i][j][4 * q + e];
+                    else
+                        v[e] = acc[0][i][j][4 * q + e];
+                }
                 u32x2 out;
                 out[0] = pack2(v[0], v[1]);
                 out[1] = pack2(v[2], v[3]);
-                *reinterpret_cast<u32x2*>(sY + r * PY + j * 32 + 8 * q + 4 * (lane >> 5)) = out;
+                *reinterpret_cast<u32x2*>(sY + y_off(r, 4 * j + q) + 4 * (lane >> 5)) = out;
             }
         }
     }
@@ -681,7 +781,7 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
         const int c = lane % CPR;
         const int m = m0 + wrow0 + r;
         const int n = n0 + wcol0 + 8 * c;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(sY + r * PY + 8 * c);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sY + y_off(r, c));
         if (m < M && n < N) *reinterpret_cast<u32x4*>(p.Y + (size_t)m * N + n) = v;
     }
 }

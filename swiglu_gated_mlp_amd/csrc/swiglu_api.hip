@@ -184,9 +184,9 @@ hipError_t launch_decode(const swk::DecodeArgs& a, int groups, hipStream_t s) {
     return hipLaunchKernel(fn, dim3(groups), dim3(256), kargs, 0, s);
 }
 
-template <int BM, int BN, int WM, int WN, bool SPLIT>
+template <int BM, int BN, int WM, int WN, bool SPLIT, int WSRC = swk::W_PACKED>
 hipError_t launch_prefill(const swk::FusedArgs& a, int grid, hipStream_t s) {
-    const void* fn = reinterpret_cast<const void*>(&swk::fused_prefill_kernel<BM, BN, WM, WN, SPLIT>);
+    const void* fn = reinterpret_cast<const void*>(&swk::fused_prefill_kernel<BM, BN, WM, WN, SPLIT, WSRC>);
     swk::FusedArgs args = a;
     void* kargs[] = {&args};
     return hipLaunchKernel(fn, dim3(grid), dim3(64 * WM * WN), kargs, 0, s);
@@ -315,15 +315,20 @@ swiglu_status swiglu_fused(const swiglu_bf16* A, const swiglu_bf16* W1, const sw
     a.splits = 1; a.kb_per_split = a.KB;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
+    // M <= 64: register-transposing tile kernel; above: direct loads of the
+    // row-major weight tiles, fragments through the transposing LDS read
     if (M <= 32) {
         a.tiles_m = (int)ceil_div(M, 32); a.tiles_n = (int)ceil_div(N, 128);
         e = launch_tile<32, 128, 1, 4, true, false, false>(a, a.tiles_m * a.tiles_n, s);
+    } else if (M <= 64) {
+        a.tiles_m = 1; a.tiles_n = (int)ceil_div(N, 128);
+        e = launch_tile<64, 128, 2, 2, true, false, false>(a, a.tiles_m * a.tiles_n, s);
     } else if (M <= 2048) {
         a.tiles_m = (int)ceil_div(M, 128); a.tiles_n = (int)ceil_div(N, 128);
-        e = launch_tile<128, 128, 2, 2, true, false, false>(a, a.tiles_m * a.tiles_n, s);
+        e = launch_prefill<128, 128, 2, 2, false, swk::W_ROW_DUAL>(a, a.tiles_m * a.tiles_n, s);
     } else {
         a.tiles_m = (int)ceil_div(M, 256); a.tiles_n = (int)ceil_div(N, 128);
-        e = launch_tile<256, 128, 2, 2, true, false, false>(a, a.tiles_m * a.tiles_n, s);
+        e = launch_prefill<256, 128, 2, 2, false, swk::W_ROW_DUAL>(a, a.tiles_m * a.tiles_n, s);
     }
     if (log_enabled()) std::fprintf(stderr, "[swiglu] fused M=%lld K=%lld N=%lld\n", (long long)M, (long long)K, (long long)N);
     return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
@@ -408,12 +413,15 @@ swiglu_status swiglu_gemm_bf16(const swiglu_bf16* A, const swiglu_bf16* W, swigl
     if (M <= 32) {
         a.tiles_m = (int)ceil_div(M, 32); a.tiles_n = (int)ceil_div(N, 256);
         e = launch_tile<32, 256, 1, 4, false, false, false>(a, a.tiles_m * a.tiles_n, s);
+    } else if (M <= 64) {
+        a.tiles_m = 1; a.tiles_n = (int)ceil_div(N, 256);
+        e = launch_tile<64, 256, 2, 2, false, false, false>(a, a.tiles_m * a.tiles_n, s);
     } else if (M <= 2048) {
         a.tiles_m = (int)ceil_div(M, 128); a.tiles_n = (int)ceil_div(N, 256);
-        e = launch_tile<128, 256, 2, 2, false, false, false>(a, a.tiles_m * a.tiles_n, s);
+        e = launch_prefill<128, 256, 2, 2, false, swk::W_ROW_SINGLE>(a, a.tiles_m * a.tiles_n, s);
     } else {
         a.tiles_m = (int)ceil_div(M, 256); a.tiles_n = (int)ceil_div(N, 256);
-        e = launch_tile<256, 256, 2, 2, false, false, false>(a, a.tiles_m * a.tiles_n, s);
+        e = launch_prefill<256, 256, 2, 2, false, swk::W_ROW_SINGLE>(a, a.tiles_m * a.tiles_n, s);
     }
     return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
 }

@@ -264,3 +264,19 @@ def test_split_workspace_reused_across_shapes(dev):
         rows = sample_rows(M, 4)
         check_close(gpu_bits(Y)[rows], oracle_rows(A, W1, W2, rows), "split reuse %s" % ((M, K, N),))
         ws.buf.fill_(0x7F)      # NaN-patterned leftovers must not matter to the next call
+
+
+@pytest.mark.parametrize("M,K,N", [(65, 72, 264), (300, 200, 520), (1024, 896, 4864), (2100, 136, 256),
+                                   (4096, 896, 4864)])
+def test_gemm_bf16_against_oracle(dev, M, K, N):
+    """The unfused pipeline's GEMM: bf16 of an fp32 sum, so the GPU and the
+    oracle differ by at most one bf16 rounding flip of sums that differ only in
+    order (plus an absolute floor for sums that cancel to near zero)."""
+    A, W, _ = inputs.gaussian_case(M, K, N, seed=M + K)
+    C = sw.swiglu_gemm_bf16(A.to(dev), W.to(dev))
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 8) if M > 512 else list(range(M))
+    got = f32(gpu_bits(C)[rows]).astype(np.float64)
+    ref = f32(oracle.gemm_bf16(A[rows].contiguous(), W)).astype(np.float64)
+    bad = np.argwhere(np.abs(got - ref) > 2.0 ** -7 * np.abs(ref) + 1e-3)
+    assert bad.size == 0, "%d elements beyond 1 ulp, e.g. %s" % (len(bad), bad[0].tolist())
