@@ -110,6 +110,7 @@ struct FusedArgs {
     float* part;          // split-K partials (fp32, [split][M][2N])
     int M, K, N;
     int tiles_m, tiles_n;
+    int n_tile0;          // first output-column tile this launch covers (in tiles of BN)
     int splits;           // number of K splits (1 = none)
     int kb_per_split;     // K blocks (of 64) per split
     int KB;               // ceil(K / 64)
@@ -496,7 +497,7 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
         tn = in_group / gsize;
     }
     const int m0 = tm * BM;
-    const int n0 = tn * BN;
+    const int n0 = (p.n_tile0 + tn) * BN;
     const int M = p.M, K = p.K, N = p.N, KB = p.KB;
     const bool ragged_k = (K % BK) != 0;
     // this workgroup's K blocks [kb_first, kb_last]; the host never makes an

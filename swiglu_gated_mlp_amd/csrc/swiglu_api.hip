@@ -118,6 +118,7 @@ constexpr int kMaxSplitTiles = 16384;
 struct Plan {
     TileCfg t;
     int tiles_m, tiles_n, tiles;
+    int tail_ntiles;   // data-parallel 256-row tiles: last column tiles run as 128x128 tiles
     int splits, kb_per_split, KB;
     int variant;   // resolved: DATA_PARALLEL, SPLIT_K or DECODE
     int decode_mt; // DECODE: 16-token tiles per workgroup
@@ -146,6 +147,17 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int variant, int cus) {
     p.tiles_m = (int)ceil_div(M, p.t.BM);
     p.tiles_n = (int)ceil_div(N, p.t.BN);
     p.tiles = p.tiles_m * p.tiles_n;
+    // Wave quantisation of the 256 x 128 schedule: when the last round of
+    // tiles would leave most CUs idle, the column tiles that make up that round
+    // run afterwards as 128 x 128 tiles (twice as many, half the work each).
+    p.tail_ntiles = 0;
+    if (v == SWIGLU_VARIANT_DATA_PARALLEL && p.t.BM == 256 && p.tiles > cus) {
+        const int rem = p.tiles % cus;
+        if (rem > 0 && rem * 10 <= cus * 6) {
+            const int nt = (int)ceil_div(rem, p.tiles_m);
+            if (nt < p.tiles_n) p.tail_ntiles = nt;
+        }
+    }
     if (v == SWIGLU_VARIANT_SPLIT_K && p.tiles <= kMaxSplitTiles) {
         // about kSplitWavesPerCu workgroups per CU, at least two K blocks per split
         int s = (int)ceil_div((int64_t)kSplitWavesPerCu * cus, p.tiles);
@@ -219,9 +231,18 @@ hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) 
                              : launch_prefill<128, 64, 2, 2, false>(a, grid, s);
             return split ? launch_prefill<128, 128, 2, 2, true>(a, grid, s)
                          : launch_prefill<128, 128, 2, 2, false>(a, grid, s);
-        default:
-            return split ? launch_prefill<256, 128, 2, 2, true>(a, grid, s)
-                         : launch_prefill<256, 128, 2, 2, false>(a, grid, s);
+        default: {
+            if (split) return launch_prefill<256, 128, 2, 2, true>(a, grid, s);
+            if (p.tail_ntiles == 0) return launch_prefill<256, 128, 2, 2, false>(a, grid, s);
+            swk::FusedArgs big = a, tail = a;
+            big.tiles_n = p.tiles_n - p.tail_ntiles;
+            hipError_t e = launch_prefill<256, 128, 2, 2, false>(big, big.tiles_m * big.tiles_n, s);
+            if (e != hipSuccess) return e;
+            tail.tiles_m = (int)ceil_div(a.M, 128);
+            tail.tiles_n = p.tail_ntiles;
+            tail.n_tile0 = big.tiles_n;
+            return launch_prefill<128, 128, 2, 2, false>(tail, tail.tiles_m * tail.tiles_n, s);
+        }
     }
 }
 
@@ -377,8 +398,9 @@ swiglu_status swiglu_fused_packed(const swiglu_bf16* A, const swiglu_bf16* Wp, s
     a.splits = p.splits; a.kb_per_split = p.kb_per_split; a.KB = p.KB;
     if (need > 0) a.part = reinterpret_cast<float*>(workspace);
     if (log_enabled())
-        std::fprintf(stderr, "[swiglu] fused_packed M=%lld K=%lld N=%lld variant=%d tile=%dx%d tiles=%d splits=%d\n",
-                     (long long)M, (long long)K, (long long)N, p.variant, p.t.BM, p.t.BN, p.tiles, p.splits);
+        std::fprintf(stderr, "[swiglu] fused_packed M=%lld K=%lld N=%lld variant=%d tile=%dx%d tiles=%d splits=%d tail_ntiles=%d\n",
+                     (long long)M, (long long)K, (long long)N, p.variant, p.t.BM, p.t.BN, p.tiles, p.splits,
+                     p.tail_ntiles);
     hipError_t e = launch_packed(a, p, (hipStream_t)stream);
     if (e == hipSuccess && p.splits > 1) {
         const int cus = std::max(1, cu_count_now());

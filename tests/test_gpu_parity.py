@@ -53,6 +53,7 @@ SMALL_SHAPES = [
     (1, 64, 128), (3, 72, 136), (17, 200, 256), (32, 128, 128), (33, 64, 264), (63, 128, 384),
     (65, 896, 512), (128, 512, 256), (130, 256, 264), (255, 192, 128), (257, 512, 640),
     (300, 136, 520), (2049, 128, 256), (2100, 64, 136),
+    (2304, 128, 3840),   # 270 tiles of 256x128: the last column tiles run as 128x128 tiles
 ]
 
 
