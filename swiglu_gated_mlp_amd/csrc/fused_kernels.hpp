@@ -810,36 +810,39 @@ struct DecodeArgs {
     int KB;               // ceil(K / 64)
 };
 
-template <int MT, int UNROLL>
+template <int MT, int CG, int UNROLL>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
     constexpr int WAVES = 4;
-    __shared__ f32x4 red[WAVES][MT][2][64];
+    __shared__ f32x4 red[WAVES][MT][CG][2][64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int r16 = lane & 15;          // weight row within the group / token within a tile
+    const int r16 = lane & 15;          // weight row within a group / token within a tile
     const int kq = lane >> 4;           // which 8-wide K slice of a 32-deep step
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * (16 * CG);
     const int jt = n0 / PACK_BN, ro = n0 % PACK_BN;
     const int M = p.M, K = p.K, N = p.N, KB = p.KB;
 
+    // Gate rows of group c are packed rows ro + 16c + r16 (Up: +128); 16*CG
+    // columns never straddle a packed tile (128 is a multiple of 16*CG)
     const uint16_t* wg_base = p.Wp + (size_t)jt * KB * (PACK_ROWS * PACK_BK)
                               + (size_t)(ro + r16) * PACK_BK + 8 * kq;
-    const uint16_t* wu_base = wg_base + (size_t)PACK_BN * PACK_BK;
     const uint16_t* a_row[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) a_row[t] = p.A + (size_t)min(t * 16 + r16, M - 1) * K + 8 * kq;
 
-    f32x4 accg[MT], accu[MT];
+    f32x4 accg[MT][CG], accu[MT][CG];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        accg[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accu[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int c = 0; c < CG; ++c) {
+            accg[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accu[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 
     for (int kb0 = wave; kb0 < KB; kb0 += WAVES * UNROLL) {
-        u32x4 wg[UNROLL][2], wu[UNROLL][2], av[UNROLL][2][MT];
+        u32x4 wg[UNROLL][2][CG], wu[UNROLL][2][CG], av[UNROLL][2][MT];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int kb = kb0 + u * WAVES;
@@ -847,8 +850,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
                 const size_t boff = (size_t)kb * (PACK_ROWS * PACK_BK);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    wg[u][h] = ld16(wg_base + boff + 32 * h);
-                    wu[u][h] = ld16(wu_base + boff + 32 * h);
+#pragma unroll
+                    for (int c = 0; c < CG; ++c) {
+                        wg[u][h][c] = ld16(wg_base + boff + c * 16 * PACK_BK + 32 * h);
+                        wu[u][h][c] = ld16(wg_base + boff + (PACK_BN + c * 16) * PACK_BK + 32 * h);
+                    }
                     const int k = kb * PACK_BK + 32 * h + 8 * kq;
 #pragma unroll
                     for (int t = 0; t < MT; ++t)
@@ -862,36 +868,41 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
             const int kb = kb0 + u * WAVES;
             if (kb < KB) {
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const bf16x8 g8 = __builtin_bit_cast(bf16x8, wg[u][h]);
-                    const bf16x8 u8 = __builtin_bit_cast(bf16x8, wu[u][h]);
+                for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int t = 0; t < MT; ++t) {
                         const bf16x8 a8 = __builtin_bit_cast(bf16x8, av[u][h][t]);
-                        accg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g8, a8, accg[t], 0, 0, 0);
-                        accu[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(u8, a8, accu[t], 0, 0, 0);
+#pragma unroll
+                        for (int c = 0; c < CG; ++c) {
+                            accg[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, wg[u][h][c]), a8, accg[t][c], 0, 0, 0);
+                            accu[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, wu[u][h][c]), a8, accu[t][c], 0, 0, 0);
+                        }
                     }
-                }
             }
         }
     }
 
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        red[wave][t][0][lane] = accg[t];
-        red[wave][t][1][lane] = accu[t];
-    }
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int c = 0; c < CG; ++c) {
+            red[wave][t][c][0][lane] = accg[t][c];
+            red[wave][t][c][1][lane] = accu[t][c];
+        }
     __syncthreads();
-    // epilogue: wave w finishes token tiles t = w, w+4, ...
-    for (int t = wave; t < MT; t += WAVES) {
-        f32x4 g = red[0][t][0][lane], u = red[0][t][1][lane];
+    // epilogue: wave w finishes (token tile, column group) pairs w, w+4, ...
+    for (int tc = wave; tc < MT * CG; tc += WAVES) {
+        const int t = tc / CG, c = tc % CG;
+        f32x4 g = red[0][t][c][0][lane], u = red[0][t][c][1][lane];
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) {
-            g += red[w][t][0][lane];
-            u += red[w][t][1][lane];
+            g += red[w][t][c][0][lane];
+            u += red[w][t][c][1][lane];
         }
         const int m = t * 16 + r16;
-        const int n = n0 + 4 * kq;
+        const int n = n0 + 16 * c + 4 * kq;
         if (m < M && n < N) {
             u32x2 out;
             out[0] = pack2(silu_f(g[0]) * u[0], silu_f(g[1]) * u[1]);

@@ -122,6 +122,7 @@ struct Plan {
     int splits, kb_per_split, KB;
     int variant;   // resolved: DATA_PARALLEL, SPLIT_K or DECODE
     int decode_mt; // DECODE: 16-token tiles per workgroup
+    int cus;       // compute units the plan was made for
 };
 
 constexpr int kDecodeMaxM = 64;
@@ -130,6 +131,7 @@ bool variant_known(int v) { return v >= SWIGLU_VARIANT_AUTO && v <= SWIGLU_VARIA
 Plan make_plan(int64_t M, int64_t K, int64_t N, int variant, int cus) {
     Plan p{};
     if (cus <= 0) cus = 256;
+    p.cus = cus;
     p.KB = (int)ceil_div(K, swk::BK);
     int v = variant;
     if (v == SWIGLU_VARIANT_AUTO) {
@@ -185,15 +187,12 @@ hipError_t launch_tile(const swk::FusedArgs& a, int grid, hipStream_t s) {
     return hipLaunchKernel(fn, dim3(grid), dim3(64 * WM * WN), kargs, 0, s);
 }
 
-template <int MT>
-hipError_t launch_decode(const swk::DecodeArgs& a, int groups, hipStream_t s) {
-    // K blocks per wave in flight: 4 for one token tile, 2 for more (their
-    // activation fragments take registers too)
-    constexpr int UNROLL = MT == 1 ? 4 : 2;
-    const void* fn = reinterpret_cast<const void*>(&swk::decode_kernel<MT, UNROLL>);
+template <int MT, int CG, int UNROLL>
+hipError_t launch_decode(const swk::DecodeArgs& a, hipStream_t s) {
+    const void* fn = reinterpret_cast<const void*>(&swk::decode_kernel<MT, CG, UNROLL>);
     swk::DecodeArgs args = a;
     void* kargs[] = {&args};
-    return hipLaunchKernel(fn, dim3(groups), dim3(256), kargs, 0, s);
+    return hipLaunchKernel(fn, dim3((unsigned)ceil_div(a.N, 16 * CG)), dim3(256), kargs, 0, s);
 }
 
 template <int BM, int BN, int WM, int WN, bool SPLIT, int WSRC = swk::W_PACKED>
@@ -209,11 +208,13 @@ hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) 
         swk::DecodeArgs d{};
         d.A = a.A; d.Wp = a.W1; d.Y = a.Y;
         d.M = a.M; d.K = a.K; d.N = a.N; d.KB = a.KB;
-        const int groups = (int)ceil_div(a.N, 16);
+        // two 16-column groups per wave (each activation fragment feeds twice
+        // the weight bytes) when that still leaves >= 2 workgroups per CU
+        const bool wide = p.decode_mt > 1 && ceil_div(a.N, 32) >= 2 * p.cus;
         switch (p.decode_mt) {
-            case 1: return launch_decode<1>(d, groups, s);
-            case 2: return launch_decode<2>(d, groups, s);
-            default: return launch_decode<4>(d, groups, s);
+            case 1: return wide ? launch_decode<1, 2, 2>(d, s) : launch_decode<1, 1, 4>(d, s);
+            case 2: return wide ? launch_decode<2, 2, 2>(d, s) : launch_decode<2, 1, 2>(d, s);
+            default: return wide ? launch_decode<4, 2, 1>(d, s) : launch_decode<4, 1, 2>(d, s);
         }
     }
     const int grid = p.tiles * p.splits;
