@@ -115,14 +115,19 @@ swiglu_status swiglu_fused(const swiglu_bf16 *A, const swiglu_bf16 *W1,
  * Packed weights.  The pages build one fused weight matrix holding W1 and W2
  * side by side before the GEMM runs ([Summary: Methodology] Kernel-2,
  * "Strategy": W_fused in R^{K x 2N}).  Here the two are interleaved per tile
- * of 128 output columns instead of per column, and stored K-contiguous:
+ * of 128 output columns instead of per column, and stored K-contiguous in
+ * the lane order of the matrix-core fragments:
  *
  *   Wp = for jt in 0 .. ceil(N/128)-1:            (output-column tile)
- *          for kb in 0 .. ceil(K/64)-1:           (64-deep K block)
- *            block[256][64]:                      (32 KiB)
- *              row r <  128: W1[kb*64 + c, jt*128 + r]        for c in 0..63
- *              row r >= 128: W2[kb*64 + c, jt*128 + r - 128]  for c in 0..63
- *   Entries with k >= K or column >= N are zero.
+ *          for kb in 0 .. ceil(K/64)-1:           (64-deep K block, 32 KiB)
+ *            for g in 0 .. 15:                    (16-row group: 0-7 W1, 8-15 W2)
+ *              for h in 0 .. 1:                   (32-deep half of the block)
+ *                for l in 0 .. 63:                (16 bytes each)
+ *                  for e in 0 .. 7:
+ *                    W[k][n] with  k = kb*64 + h*32 + (l/16)*8 + e,
+ *                                  n = jt*128 + (g%8)*16 + l%16,
+ *                                  W = W1 for g < 8, W2 for g >= 8
+ *   Entries with k >= K or n >= N are zero.
  *
  * swiglu_packed_bytes: size of Wp in bytes for a K x N weight pair (0 if the
  *   shape is invalid).

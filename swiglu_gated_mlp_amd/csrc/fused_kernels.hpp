@@ -59,6 +59,25 @@ __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 // element offset of 16-byte chunk c (0..7) of row r in an LDS tile [rows][64]
 __device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 3); }
 
+// Packed weights, within one 64-deep block of a 128-column tile: packed row
+// p (0..127 Gate columns, 128..255 Up columns) and depth k (0..63).  Each
+// 16-row group x 32-deep half is one 1 KiB fragment in MFMA lane order:
+// lane (k % 32) / 8 * 16 + p % 16 holds the 8 consecutive k of its 16 bytes,
+// so a wave reads a whole fragment with one fully coalesced load.
+__host__ __device__ __forceinline__ int packed_off(int p, int k) {
+    return ((((p >> 4) * 2 + (k >> 5)) * 64 + ((k & 31) >> 3) * 16 + (p & 15)) << 3) + (k & 7);
+}
+
+// LDS stage of packed weights in the direct-load kernel: groups of 8 rows,
+// chunk-major inside a group (16-byte unit (row & 7) of chunk slot s), slots
+// XOR-ed with the group's parity.  A direct load of one group then has lanes
+// 8s..8s+7 reading 128 contiguous bytes of one packed fragment line, and the
+// 16 rows of a fragment read fall in two groups 1 KiB +- 128 B apart (disjoint
+// banks).  Element offset of chunk c of row r:
+__device__ __forceinline__ int wlds_off(int r, int c) {
+    return (((r >> 3) << 6) + ((c ^ ((r >> 3) & 1)) << 3) + (r & 7)) << 3;
+}
+
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
@@ -260,7 +279,7 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_tile_kernel(FusedArgs p) {
                 const int q = tid + i * NT;
                 const int row = q >> 3, c = q & 7;
                 const int prow = row < BN ? ro + row : PACK_BN + ro + (row - BN);
-                rb[i] = ld16(blk + prow * PACK_BK + c * 8);
+                rb[i] = ld16(blk + packed_off(prow, c * 8));
             }
         } else {
             constexpr int NGRP = NB / 8;
@@ -523,9 +542,11 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
         const int jp = n0 / PACK_BN, ro = n0 % PACK_BN;
 #pragma unroll
         for (int i = 0; i < B_INS; ++i) {
-            const int r = (wave * B_INS + i) * 8 + lrow;
+            const int g8 = wave * B_INS + i;                  // 8-row group = one direct load
+            const int r = g8 * 8 + (lane & 7);
+            const int c = (lane >> 3) ^ (g8 & 1);
             const int prow = r < BN ? ro + r : PACK_BN + ro + (r - BN);
-            b_off[i] = prow * PACK_BK + 8 * (lpc ^ swz(r));
+            b_off[i] = packed_off(prow, 8 * c);
         }
         wtile = p.W1 + (size_t)jp * KB * (PACK_ROWS * PACK_BK);
     } else {
@@ -613,7 +634,7 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
                     fb[set][g][j] = *reinterpret_cast<const bf16x8*>(
-                        sB + lds_off(g * BN + wcol0 + j * 32 + (lane & 31), c));
+                        sB + wlds_off(g * BN + wcol0 + j * 32 + (lane & 31), c));
         } else {
             // two transposing reads give lane l the 8 K-consecutive values
             // W[16kk + 8(l>>5) + 0..7][column l & 31 of the fragment]
@@ -824,10 +845,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
     const int jt = n0 / PACK_BN, ro = n0 % PACK_BN;
     const int M = p.M, K = p.K, N = p.N, KB = p.KB;
 
-    // Gate rows of group c are packed rows ro + 16c + r16 (Up: +128); 16*CG
-    // columns never straddle a packed tile (128 is a multiple of 16*CG)
-    const uint16_t* wg_base = p.Wp + (size_t)jt * KB * (PACK_ROWS * PACK_BK)
-                              + (size_t)(ro + r16) * PACK_BK + 8 * kq;
+    // Gate rows of group c are packed rows ro + 16c + (0..15), Up rows the
+    // same + 128; each (16-row group, 32-deep half) is one 1 KiB fragment in
+    // lane order, so lane l's 16 bytes sit at l * 8 in it.  16*CG columns never
+    // straddle a packed tile (128 is a multiple of 16*CG).
+    const uint16_t* wtile = p.Wp + (size_t)jt * KB * (PACK_ROWS * PACK_BK);
+    const int grp0 = ro >> 4;
     const uint16_t* a_row[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) a_row[t] = p.A + (size_t)min(t * 16 + r16, M - 1) * K + 8 * kq;
@@ -852,8 +875,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
                 for (int h = 0; h < 2; ++h) {
 #pragma unroll
                     for (int c = 0; c < CG; ++c) {
-                        wg[u][h][c] = ld16(wg_base + boff + c * 16 * PACK_BK + 32 * h);
-                        wu[u][h][c] = ld16(wg_base + boff + (PACK_BN + c * 16) * PACK_BK + 32 * h);
+                        wg[u][h][c] = ld16(wtile + boff + (((grp0 + c) * 2 + h) * 64 + lane) * 8);
+                        wu[u][h][c] = ld16(wtile + boff + (((grp0 + c + 8) * 2 + h) * 64 + lane) * 8);
                     }
                     const int k = kb * PACK_BK + 32 * h + 8 * kq;
 #pragma unroll
@@ -913,29 +936,47 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Weight pack / unpack (one-time transforms; see the packed layout in swiglu.h).
-// One thread per 16-byte packed chunk (8 consecutive k of one packed row).
+// Weight pack / unpack (one-time transforms; see the packed layout in swiglu.h
+// and packed_off above).  One thread per 16-byte packed chunk: 8 consecutive
+// k of one packed row, at chunk index q = block * 2048 + ((group * 2 + half)
+// * 64 + lane), where the chunk's row is group * 16 + lane % 16 and its first
+// k is half * 32 + (lane / 16) * 8.
 // ---------------------------------------------------------------------------
+struct PackChunk {
+    int n;          // output column (may be >= N: padding)
+    bool up;        // Up weight (W2) rather than Gate (W1)
+    int k0;         // first of the chunk's 8 consecutive k (may be >= K: padding)
+};
+
+__device__ __forceinline__ PackChunk pack_chunk(long long q, int KB) {
+    const long long blk = q >> 11;                  // jt * KB + kb
+    const int within = (int)(q & 2047);
+    const int grp = within >> 7;
+    const int half = (within >> 6) & 1;
+    const int lane = within & 63;
+    const int prow = grp * 16 + (lane & 15);
+    const int kb = (int)(blk % KB);
+    const int jt = (int)(blk / KB);
+    PackChunk c;
+    c.up = prow >= PACK_BN;
+    c.n = jt * PACK_BN + (c.up ? prow - PACK_BN : prow);
+    c.k0 = kb * PACK_BK + half * 32 + (lane >> 4) * 8;
+    return c;
+}
+
 __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ W1,
                                                    const uint16_t* __restrict__ W2,
                                                    uint16_t* __restrict__ Wp, int K, int N,
                                                    int KB, long long nchunks) {
     const long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= nchunks) return;
-    const int c = (int)(q & 7);
-    const long long rowid = q >> 3;                 // packed row over all blocks
-    const int prow = (int)(rowid % PACK_ROWS);
-    const long long blk = rowid / PACK_ROWS;        // jt * KB + kb
-    const int kb = (int)(blk % KB);
-    const int jt = (int)(blk / KB);
-    const bool up = prow >= PACK_BN;
-    const int n = jt * PACK_BN + (up ? prow - PACK_BN : prow);
-    const uint16_t* W = up ? W2 : W1;
+    const PackChunk c = pack_chunk(q, KB);
+    const uint16_t* W = c.up ? W2 : W1;
     unsigned short v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int k = kb * PACK_BK + c * 8 + i;
-        v[i] = (n < N && k < K) ? W[(size_t)k * N + n] : (unsigned short)0;
+        const int k = c.k0 + i;
+        v[i] = (c.n < N && k < K) ? W[(size_t)k * N + c.n] : (unsigned short)0;
     }
     u32x4 out;
 #pragma unroll
@@ -949,21 +990,14 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint16_t* __restrict_
                                                      int KB, long long nchunks) {
     const long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= nchunks) return;
-    const int c = (int)(q & 7);
-    const long long rowid = q >> 3;
-    const int prow = (int)(rowid % PACK_ROWS);
-    const long long blk = rowid / PACK_ROWS;
-    const int kb = (int)(blk % KB);
-    const int jt = (int)(blk / KB);
-    const bool up = prow >= PACK_BN;
-    const int n = jt * PACK_BN + (up ? prow - PACK_BN : prow);
-    if (n >= N) return;
-    uint16_t* W = up ? W2 : W1;
+    const PackChunk c = pack_chunk(q, KB);
+    if (c.n >= N) return;
+    uint16_t* W = c.up ? W2 : W1;
     const u32x4 in = *reinterpret_cast<const u32x4*>(Wp + q * 8);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int k = kb * PACK_BK + c * 8 + i;
-        if (k < K) W[(size_t)k * N + n] = (uint16_t)((in[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+        const int k = c.k0 + i;
+        if (k < K) W[(size_t)k * N + c.n] = (uint16_t)((in[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
     }
 }
 

@@ -77,23 +77,34 @@ def test_pack_roundtrip_and_layout(dev):
         torch.cuda.synchronize()
         assert torch.equal(V1.view(torch.int16), W1d.view(torch.int16))
         assert torch.equal(V2.view(torch.int16), W2d.view(torch.int16))
-        # layout as documented: tile jt, block kb, row r, k offset c
+        # layout as documented in swiglu.h: tile jt, block kb, 16-row group g,
+        # half h, lane l, element e
         P = inputs.as_bits(Wp.cpu())
         KB = (K + 63) // 64
         w1, w2 = inputs.as_bits(W1), inputs.as_bits(W2)
+
+        def pos(jt, kb, g, h, l, e):
+            return ((((jt * KB + kb) * 16 + g) * 2 + h) * 64 + l) * 8 + e
+
         rng = np.random.default_rng(K)
-        for _ in range(200):
+        for _ in range(300):
             n = int(rng.integers(0, N))
             k = int(rng.integers(0, K))
-            jt, r, kb, c = n // 128, n % 128, k // 64, k % 64
-            base = ((jt * KB + kb) * 256) * 64
-            assert P[base + r * 64 + c] == w1[k, n]
-            assert P[base + (128 + r) * 64 + c] == w2[k, n]
-        # padding is zero
+            jt, r, kb, kk = n // 128, n % 128, k // 64, k % 64
+            g, h, l, e = r // 16, kk // 32, ((kk % 32) // 8) * 16 + r % 16, kk % 8
+            assert P[pos(jt, kb, g, h, l, e)] == w1[k, n]
+            assert P[pos(jt, kb, g + 8, h, l, e)] == w2[k, n]
+        # padding is zero: columns past N in the last tile, k past K in the last block
         if N % 128:
             jt = N // 128
-            r = N % 128
-            assert np.all(P[((jt * KB) * 256 + r) * 64:((jt * KB) * 256 + 128) * 64] == 0)
+            for r in range(N % 128, 128, 7):
+                g, l = r // 16, r % 16
+                assert P[pos(jt, 0, g, 0, l, 0)] == 0 and P[pos(jt, 0, g + 8, 1, 48 + l, 7)] == 0
+        if K % 64:
+            kk = K % 64
+            for n in range(0, N, 37):
+                r = n % 128
+                assert P[pos(n // 128, KB - 1, r // 16, kk // 32, ((kk % 32) // 8) * 16 + r % 16, kk % 8)] == 0
 
 
 # The five Qwen-2.5-shaped workloads, eight (workload, M) points.
