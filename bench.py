@@ -313,6 +313,7 @@ def main():
                    "N": w.N, "variant": args.variant, "rotation_sets": res["rotation"]},
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 5),
+                     "scope": "one swiglu_fused_packed call, all of its kernel launches",
                      "traffic": measured_traffic("%s M=%d K=%d N=%d" % (w.name, M, w.K, w.N))},
         "cpu_baseline": cpu,
     }
