@@ -809,6 +809,345 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_prefill_kernel(FusedArgs p
 }
 
 // ---------------------------------------------------------------------------
+// Prefill on packed weights with the weights streamed to registers.
+//   The direct global->LDS path moves far more bytes per CU with two 64-deep
+//   stages in flight than with one, but with both operands in LDS only one
+//   stage fits beside the stage being read (2 x 64 KiB of 160 KiB).  So only
+//   the activation tile, the operand all four waves share, goes through LDS:
+//   a ring of three BM x 64 stages (32 KiB each at BM = 256), loaded two
+//   stages ahead.  The weights skip LDS.  The four waves sit side by side and
+//   own 32 output columns each (Gate and Up), so every packed weight fragment
+//   is needed by exactly one wave, which loads it straight into registers,
+//   also two stages ahead (three register sets of 8 x 16 bytes per lane).  In
+//   the packed fragment order each such load is two contiguous 512-byte runs.
+//   Per wave and 16-deep sub-step: 2 x TM MFMA 32x32x16, TM fragment reads
+//   (double-buffered: the next sub-step's, issued in the first half) and a
+//   quarter of the stage's A_INS direct loads + 8 weight loads.  One barrier
+//   per stage, before the last sub-step's MFMAs: it publishes the next
+//   stage's activation tile and frees the ring slot just read.  Wait counts
+//   are explicit (vmcnt counts vector-memory instructions in issue order):
+//   at that barrier only loads of the stage two ahead may be in flight.
+//   Activation columns beyond K (ragged last block, RAGGED) are fetched from
+//   a 16-byte zero chunk, so the ragged stage stays on the direct path; the
+//   packed weights are already zero there.
+//   Each output sums the same MFMAs in the same order (k ascending, weight
+//   fragment as first operand) as fused_prefill_kernel, so the two agree
+//   bitwise.
+// ---------------------------------------------------------------------------
+__device__ __attribute__((aligned(16))) uint16_t g_zero_chunk[8];
+
+// s_waitcnt immediate: vector-memory count vm, LDS/scalar count lgkm (no
+// export wait)
+constexpr int waitcnt_imm(int vm, int lgkm) {
+    return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+template <int BM, bool SPLIT, bool RAGGED>
+__global__ __launch_bounds__(256) void stream_prefill_kernel(FusedArgs p) {
+    constexpr int NW = 4;                       // waves, 32 output columns each
+    constexpr int TM = BM / 32;                 // 32-row MFMA tiles per wave
+    constexpr int A_INS = BM / 8 / NW;          // 1 KiB direct loads per wave per stage
+    constexpr int ASTAGE = BM * BK;             // elements per activation stage
+    constexpr int NBUF = 3;                     // ring slots == weight register sets
+    constexpr int LOADS = A_INS + 8;            // vector-memory instructions per wave per stage
+    constexpr int SMEM = NBUF * ASTAGE > BM * PACK_BN ? NBUF * ASTAGE : BM * PACK_BN;
+    constexpr int GROUP_M = 8;
+    static_assert(TM >= 1 && A_INS >= 1 && (BM / 8) % NW == 0, "tile");
+    static_assert(LOADS <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    const int S = SPLIT ? p.splits : 1;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int tile = SPLIT ? logical / S : logical;
+    const int split = SPLIT ? logical - tile * S : 0;
+    int tm, tn;
+    {
+        const int per_group = GROUP_M * p.tiles_n;
+        const int group = tile / per_group;
+        const int first_m = group * GROUP_M;
+        const int gsize = min(p.tiles_m - first_m, GROUP_M);
+        const int in_group = tile - group * per_group;
+        tm = first_m + in_group % gsize;
+        tn = in_group / gsize;
+    }
+    const int m0 = tm * BM;
+    const int n0 = (p.n_tile0 + tn) * PACK_BN;
+    const int M = p.M, K = p.K, N = p.N, KB = p.KB;
+    const int kb_first = SPLIT ? split * p.kb_per_split : 0;
+    const int kb_end = SPLIT ? min(KB, kb_first + p.kb_per_split) : KB;
+    const int ns = kb_end - kb_first;           // >= 1: the host never makes an empty split
+
+    // activation: lane l of direct load i fetches row (wave*A_INS+i)*8 + l/8,
+    // logical chunk (l%8) ^ swz(row), so LDS holds the tile in lds_off order;
+    // byte offsets from A (the host keeps M*K*2 below 4 GiB) so the uniform
+    // part of the address stays scalar
+    uint32_t a_off[A_INS];
+    int a_kc[A_INS];
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) {
+        const int r = (wave * A_INS + i) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r);
+        a_off[i] = (uint32_t)(((size_t)min(m0 + r, M - 1) * K + 8 * c) * 2);
+        a_kc[i] = 8 * c;
+    }
+    // weights: lane l needs column wave*32 + (l & 31) and the 8 k at chunk
+    // c = 2kk + (l >> 5) of each 64-deep block, i.e. packed group
+    // t*8 + wave*2 + ((l >> 4) & 1), half kk >> 1, fragment lane
+    // (2(kk & 1) + (l >> 5))*16 + (l & 15): a lane byte offset plus a
+    // constant per (t, kk)
+    const uint32_t w_off = (uint32_t)(((wave * 2 + ((lane >> 4) & 1)) * 1024 + (lane >> 5) * 128 + (lane & 15) * 8) * 2);
+    const char* w_tile = reinterpret_cast<const char*>(p.W1) + (size_t)(n0 / PACK_BN) * KB * (PACK_ROWS * PACK_BK * 2);
+    // fragment reads: lane l reads row i*32 + (l & 31), logical chunk
+    // 2kk + (l >> 5).  swz(i*32 + r) = swz(r) ^ 4(i & 1) for r < 32, so the
+    // physical chunk is ((l >> 5) ^ swz(l & 31)) ^ 2(kk ^ 2(i & 1)): four lane
+    // base offsets (x = kk ^ 2(i & 1)) plus i*4096 bytes plus the ring slot
+    const int lrow = lane & 31;
+    const int hs = (lane >> 5) ^ swz(lrow);
+    uint32_t rd_base[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) rd_base[x] = (uint32_t)((lrow * BK + ((hs ^ (2 * x)) << 3)) * 2);
+
+    f32x16 acc[2][TM][1];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[g][i][0][r] = 0.0f;
+    bf16x8 fa[2][TM];
+    bf16x8 wf[NBUF][2][4];
+    // every register set defined on every path into the stage loop
+#pragma unroll
+    for (int q = 0; q < NBUF; ++q)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) wf[q][t][kk] = bf16x8{};
+
+    // byte offset of ring slot b, kept opaque so the fragment addresses are
+    // formed per stage from the four lane bases instead of being precomputed
+    // for every (slot, sub-step, tile)
+    auto slot_off = [&](int b) {
+        uint32_t so = (uint32_t)(b * ASTAGE * 2);
+        asm volatile("" : "+s"(so));
+        return so;
+    };
+    auto read_a = [&](uint32_t so, int kk, int i, int set) {
+        fa[set][i] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(smem) + so + i * 4096 +
+                                                      rd_base[kk ^ (2 * (i & 1))]);
+    };
+    auto issue_a = [&](int s, int buf) {
+        const int k0 = (kb_first + s) * BK;
+        const char* base = reinterpret_cast<const char*>(p.A) + (size_t)k0 * 2;
+#pragma unroll
+        for (int j = 0; j < A_INS; ++j) {
+            const uint16_t* src = reinterpret_cast<const uint16_t*>(base + a_off[j]);
+            if constexpr (RAGGED) {
+                if (k0 + a_kc[j] >= K) src = g_zero_chunk;
+            }
+            dma16(src, smem + buf * ASTAGE + (wave * A_INS + j) * 512);
+        }
+    };
+    auto issue_w = [&](int s, auto setc) {
+        constexpr int SET = decltype(setc)::value;
+        const char* blk = w_tile + (size_t)(kb_first + s) * (PACK_ROWS * PACK_BK * 2);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                wf[SET][t][kk] = *reinterpret_cast<const bf16x8*>(blk + t * 16384 + w_off + (kk >> 1) * 1024 + (kk & 1) * 512);
+    };
+    // load j of stage s: j < A_INS the activation direct load j into slot
+    // buf, else weight fragment (t, kk) = ((j - A_INS) / 4, (j - A_INS) % 4)
+    // into register set SET
+    auto issue_one = [&](int j, int s, int buf, auto setc) {
+        constexpr int SET = decltype(setc)::value;
+        if (j < A_INS) {
+            const int k0 = (kb_first + s) * BK;
+            const uint16_t* src = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(p.A) +
+                                                                    (size_t)k0 * 2 + a_off[j]);
+            if constexpr (RAGGED) {
+                if (k0 + a_kc[j] >= K) src = g_zero_chunk;
+            }
+            dma16(src, smem + buf * ASTAGE + (wave * A_INS + j) * 512);
+        } else {
+            const int t = (j - A_INS) >> 2, kk = (j - A_INS) & 3;
+            const char* blk = w_tile + (size_t)(kb_first + s) * (PACK_ROWS * PACK_BK * 2) + t * 16384;
+            wf[SET][t][kk] = *reinterpret_cast<const bf16x8*>(blk + w_off + (kk >> 1) * 1024 + (kk & 1) * 512);
+        }
+    };
+    constexpr int LPS = LOADS / 4;                // loads per sub-step
+    static_assert(LOADS % 4 == 0, "loads split over four sub-steps");
+    constexpr int LPI = (LPS + TM - 1) / TM;      // loads per 32-row step
+    constexpr int RPI = TM >= 2 ? 2 : 1;          // next-sub-step reads per step
+    // One 16-deep sub-step on fragment set CUR, in a fixed order (each step
+    // fenced): for each 32-row tile, its Gate and Up MFMAs, then the next
+    // sub-step's fragments (RD: from slot offset rso, sub-step rkk; two per
+    // step, so they are all issued in the first half), then (LD) LPI loads of
+    // stage ls.  The reads go to the other fragment set, so any wait for
+    // them lands at the start of the next sub-step, long after they were
+    // issued.
+    auto substep = [&](auto wsetc, int kk, int cur, auto rdc, uint32_t rso, int rkk, auto ldc, int ls, int lbuf,
+                       auto lsetc, int lq) {
+        constexpr int WS = decltype(wsetc)::value;
+        constexpr bool RD = decltype(rdc)::value;
+        constexpr bool LD = decltype(ldc)::value;
+        // this sub-step's fragments were all read during the first half of
+        // the previous one: wait for them here, before any new read, so no
+        // later wait in this sub-step has to cover the new reads
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            acc[0][i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[WS][0][kk], fa[cur][i], acc[0][i][0], 0, 0, 0);
+            acc[1][i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[WS][1][kk], fa[cur][i], acc[1][i][0], 0, 0, 0);
+            if constexpr (RD) {
+#pragma unroll
+                for (int q = i * RPI; q < (i + 1) * RPI; ++q)
+                    if (q < TM) read_a(rso, rkk, q, cur ^ 1);
+            }
+            if constexpr (LD) {
+#pragma unroll
+                for (int j = i * LPI; j < (i + 1) * LPI; ++j)
+                    if (j < LPS) issue_one(lq * LPS + j, ls, lbuf, lsetc);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+
+    // One 64-deep stage s in ring slot / register set P = s % 3.  LD: issue
+    // stage s+2's loads (slot and set (P+2) % 3, freed by the previous
+    // stage's barrier), LPS per sub-step; NX: a next stage exists, its first
+    // fragments are read during this stage's last sub-step.
+    auto stage = [&](auto pc, auto ldc, auto nxc, int s) {
+        constexpr int P = decltype(pc)::value;
+        constexpr bool NX = decltype(nxc)::value;
+        constexpr bool LD = decltype(ldc)::value;
+        constexpr int PN = (P + 1) % NBUF, PL = (P + 2) % NBUF;
+        using WP = std::integral_constant<int, P>;
+        using WL = std::integral_constant<int, PL>;
+        const uint32_t so = slot_off(P);
+        __builtin_amdgcn_sched_barrier(0);
+        substep(WP{}, 0, 0, T{}, so, 1, ldc, s + 2, PL, WL{}, 0);
+        substep(WP{}, 1, 1, T{}, so, 2, ldc, s + 2, PL, WL{}, 1);
+        substep(WP{}, 2, 0, T{}, so, 3, ldc, s + 2, PL, WL{}, 2);
+        if constexpr (NX) {
+            const uint32_t son = slot_off(PN);
+            // stage s+1 (activations and this wave's weights) has landed once
+            // at most the 3*LPS loads of stage s+2 issued so far are in
+            // flight; after the barrier every wave is done reading slot P
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(LD ? 3 * LPS : 0, 0));
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            substep(WP{}, 3, 1, T{}, son, 0, ldc, s + 2, PL, WL{}, 3);
+        } else {
+            substep(WP{}, 3, 1, F{}, 0u, 0, F{}, 0, 0, WL{}, 3);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+
+    // Ring phase: stage s uses slot / register set (s + phase) % 3, with the
+    // phase chosen so that the two draining stages (ns-2, ns-1) always use
+    // slots 0 and 1; the stages before them that issue loads then run as a
+    // short prefix (slots 3-r .. 2) and whole periods 0, 1, 2.
+    if (ns == 1) {
+        issue_a(0, 0);
+        issue_w(0, I0{});
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int i = 0; i < TM; ++i) read_a(0u, 0, i, 0);
+        stage(I0{}, F{}, F{}, 0);
+    } else {
+        const int nfull = ns - 2;         // stages that issue loads two ahead
+        const int r = nfull % 3;
+        const int phase = (3 - r) % 3;
+        switch (phase) {
+            case 0:
+                issue_a(0, 0); issue_w(0, I0{});
+                issue_a(1, 1); issue_w(1, I1{});
+                break;
+            case 1:
+                issue_a(0, 1); issue_w(0, I1{});
+                issue_a(1, 2); issue_w(1, I2{});
+                break;
+            default:
+                issue_a(0, 2); issue_w(0, I2{});
+                issue_a(1, 0); issue_w(1, I0{});
+                break;
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(LOADS, 0));
+        __builtin_amdgcn_s_barrier();
+        const uint32_t so0 = (uint32_t)(phase * ASTAGE * 2);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) read_a(so0, 0, i, 0);
+        int s = 0;
+        if (r == 2) {
+            stage(I1{}, T{}, T{}, 0);
+            stage(I2{}, T{}, T{}, 1);
+            s = 2;
+        } else if (r == 1) {
+            stage(I2{}, T{}, T{}, 0);
+            s = 1;
+        }
+        for (; s < nfull; s += 3) {
+            stage(I0{}, T{}, T{}, s);
+            stage(I1{}, T{}, T{}, s + 1);
+            stage(I2{}, T{}, T{}, s + 2);
+        }
+        stage(I0{}, F{}, T{}, ns - 2);
+        stage(I1{}, F{}, F{}, ns - 1);
+    }
+
+    if constexpr (SPLIT) {
+        store_partials<TM, 1>(acc, p.part, split, M, N, m0, n0 + wave * 32, lane);
+        return;
+    }
+
+    // Epilogue: SiLU(Gate) * Up -> bf16 into an LDS copy of the BM x 128 Y
+    // tile (16-byte chunk index XOR row & 15, and the two 8-byte halves
+    // swapped on rows with bit 4 set, so each 32-lane write pass covers all
+    // banks), then whole 256-byte row segments to HBM.  No load is in flight
+    // and every wave is past its last fragment read after the barrier.
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int r = i * 32 + (lane & 31);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = silu_f(acc[0][i][0][4 * q + e]) * acc[1][i][0][4 * q + e];
+            u32x2 out;
+            out[0] = pack2(v[0], v[1]);
+            out[1] = pack2(v[2], v[3]);
+            const int chunk = wave * 4 + q;
+            *reinterpret_cast<u32x2*>(smem + r * PACK_BN + 8 * (chunk ^ (r & 15)) +
+                                      4 * ((lane >> 5) ^ ((r >> 4) & 1))) = out;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < BM / 16; ++t) {
+        const int r = wave * (BM / 4) + t * 4 + (lane >> 4);
+        const int c = lane & 15;
+        u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * PACK_BN + 8 * (c ^ (r & 15)));
+        if ((r >> 4) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+        const int m = m0 + r, n = n0 + 8 * c;
+        if (m < M && n < N) *reinterpret_cast<u32x4*>(p.Y + (size_t)m * N + n) = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Decode (small M): weight streaming.
 //   The product is bound by reading the packed weights once from HBM, so the
 //   kernel is shaped around keeping many 16-byte loads in flight, not around

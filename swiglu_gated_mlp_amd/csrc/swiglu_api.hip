@@ -103,7 +103,7 @@ struct TileCfg {
 TileCfg packed_tile_for(int64_t M, int variant) {
     if (M <= 32) return {32, 128};
     if (M <= 64) return {64, 128};
-    if (variant == SWIGLU_VARIANT_SPLIT_K) return {128, 64};
+    if (variant == SWIGLU_VARIANT_SPLIT_K) return {128, 128};
     if (M <= 2048) return {128, 128};
     return {256, 128};
 }
@@ -134,13 +134,22 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int variant, int cus) {
     p.cus = cus;
     p.KB = (int)ceil_div(K, swk::BK);
     int v = variant;
+    int auto_split_cap = 0;   // AUTO's split-K: most splits worth their partial-sum traffic
     if (v == SWIGLU_VARIANT_AUTO) {
         if (M <= kDecodeMaxM) {
             v = SWIGLU_VARIANT_DECODE;
         } else {
+            // Split-K writes and re-reads S fp32 partial sums of Gate and Up,
+            // 16*S*M*N bytes against the 4*K*N bytes of weights: worth it only
+            // while the data-parallel tiles leave most CUs idle, and with at
+            // most K / (16 M) splits (extra traffic <= a quarter of the
+            // weights).  A data-parallel grid that fills half the CUs streams
+            // the weights faster than split-K does.
             const TileCfg dp = packed_tile_for(M, SWIGLU_VARIANT_DATA_PARALLEL);
             const int64_t dp_tiles = ceil_div(M, dp.BM) * ceil_div(N, dp.BN);
-            v = (dp_tiles >= cus || p.KB < 4) ? SWIGLU_VARIANT_DATA_PARALLEL : SWIGLU_VARIANT_SPLIT_K;
+            auto_split_cap = (int)std::min<int64_t>(K / (16 * M), 1 << 20);
+            v = (2 * dp_tiles >= cus || p.KB < 4 || auto_split_cap < 2) ? SWIGLU_VARIANT_DATA_PARALLEL
+                                                                         : SWIGLU_VARIANT_SPLIT_K;
         }
     }
     p.variant = v;
@@ -163,6 +172,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int variant, int cus) {
     if (v == SWIGLU_VARIANT_SPLIT_K && p.tiles <= kMaxSplitTiles) {
         // about kSplitWavesPerCu workgroups per CU, at least two K blocks per split
         int s = (int)ceil_div((int64_t)kSplitWavesPerCu * cus, p.tiles);
+        if (auto_split_cap > 0) s = std::min(s, auto_split_cap);
         s = std::max(1, std::min(s, p.KB / 2 > 0 ? p.KB / 2 : 1));
         p.kb_per_split = (int)ceil_div(p.KB, s);
         p.splits = (int)ceil_div(p.KB, p.kb_per_split);
@@ -203,6 +213,16 @@ hipError_t launch_prefill(const swk::FusedArgs& a, int grid, hipStream_t s) {
     return hipLaunchKernel(fn, dim3(grid), dim3(64 * WM * WN), kargs, 0, s);
 }
 
+template <int BM, bool SPLIT>
+hipError_t launch_stream(const swk::FusedArgs& a, int grid, hipStream_t s) {
+    const void* fn = (a.K % swk::BK) != 0
+                         ? reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, true>)
+                         : reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, false>);
+    swk::FusedArgs args = a;
+    void* kargs[] = {&args};
+    return hipLaunchKernel(fn, dim3(grid), dim3(256), kargs, 0, s);
+}
+
 hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) {
     if (p.variant == SWIGLU_VARIANT_DECODE) {
         swk::DecodeArgs d{};
@@ -227,22 +247,18 @@ hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) 
             return split ? launch_tile<64, 128, 2, 2, true, true, true>(a, grid, s)
                          : launch_tile<64, 128, 2, 2, true, true, false>(a, grid, s);
         case 128:
-            if (p.t.BN == 64)
-                return split ? launch_prefill<128, 64, 2, 2, true>(a, grid, s)
-                             : launch_prefill<128, 64, 2, 2, false>(a, grid, s);
-            return split ? launch_prefill<128, 128, 2, 2, true>(a, grid, s)
-                         : launch_prefill<128, 128, 2, 2, false>(a, grid, s);
+            return split ? launch_stream<128, true>(a, grid, s) : launch_stream<128, false>(a, grid, s);
         default: {
-            if (split) return launch_prefill<256, 128, 2, 2, true>(a, grid, s);
-            if (p.tail_ntiles == 0) return launch_prefill<256, 128, 2, 2, false>(a, grid, s);
+            if (split) return launch_stream<256, true>(a, grid, s);
+            if (p.tail_ntiles == 0) return launch_stream<256, false>(a, grid, s);
             swk::FusedArgs big = a, tail = a;
             big.tiles_n = p.tiles_n - p.tail_ntiles;
-            hipError_t e = launch_prefill<256, 128, 2, 2, false>(big, big.tiles_m * big.tiles_n, s);
+            hipError_t e = launch_stream<256, false>(big, big.tiles_m * big.tiles_n, s);
             if (e != hipSuccess) return e;
             tail.tiles_m = (int)ceil_div(a.M, 128);
             tail.tiles_n = p.tail_ntiles;
             tail.n_tile0 = big.tiles_n;
-            return launch_prefill<128, 128, 2, 2, false>(tail, tail.tiles_m * tail.tiles_n, s);
+            return launch_stream<128, false>(tail, tail.tiles_m * tail.tiles_n, s);
         }
     }
 }
