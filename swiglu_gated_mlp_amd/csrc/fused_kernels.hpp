@@ -940,44 +940,35 @@ __global__ __launch_bounds__(256) void stream_prefill_kernel(FusedArgs p) {
         fa[set][i] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(smem) + so + i * 4096 +
                                                       rd_base[kk ^ (2 * (i & 1))]);
     };
-    auto issue_a = [&](int s, int buf) {
-        const int k0 = (kb_first + s) * BK;
-        const char* base = reinterpret_cast<const char*>(p.A) + (size_t)k0 * 2;
-#pragma unroll
-        for (int j = 0; j < A_INS; ++j) {
-            const uint16_t* src = reinterpret_cast<const uint16_t*>(base + a_off[j]);
-            if constexpr (RAGGED) {
-                if (k0 + a_kc[j] >= K) src = g_zero_chunk;
-            }
-            dma16(src, smem + buf * ASTAGE + (wave * A_INS + j) * 512);
-        }
-    };
-    auto issue_w = [&](int s, auto setc) {
-        constexpr int SET = decltype(setc)::value;
-        const char* blk = w_tile + (size_t)(kb_first + s) * (PACK_ROWS * PACK_BK * 2);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                wf[SET][t][kk] = *reinterpret_cast<const bf16x8*>(blk + t * 16384 + w_off + (kk >> 1) * 1024 + (kk & 1) * 512);
-    };
-    // load j of stage s: j < A_INS the activation direct load j into slot
+    // Stages past the last (ls >= ns) are issued like any other, but every
+    // lane then reads the 16-byte zero chunk (a single cache line): the
+    // stage code stays the same for every stage, with no tail variants.
+    // Their weight registers are consumed (without instructions) after the
+    // loop, so those loads are not dropped as dead code and every stage
+    // issues exactly LOADS vector-memory instructions, which the wait counts
+    // rely on.
+    // load j of stage ls: j < A_INS the activation direct load j into slot
     // buf, else weight fragment (t, kk) = ((j - A_INS) / 4, (j - A_INS) % 4)
     // into register set SET
-    auto issue_one = [&](int j, int s, int buf, auto setc) {
+    auto issue_one = [&](int j, int ls, int buf, auto setc) {
         constexpr int SET = decltype(setc)::value;
+        const bool valid = ls < ns;
+        const uint32_t keep = valid ? 0xffffffffu : 0u;
         if (j < A_INS) {
-            const int k0 = (kb_first + s) * BK;
-            const uint16_t* src = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(p.A) +
-                                                                    (size_t)k0 * 2 + a_off[j]);
+            const int k0 = (kb_first + ls) * BK;
+            const char* base = valid ? reinterpret_cast<const char*>(p.A) + (size_t)k0 * 2
+                                     : reinterpret_cast<const char*>(g_zero_chunk);
+            const uint16_t* src = reinterpret_cast<const uint16_t*>(base + (a_off[j] & keep));
             if constexpr (RAGGED) {
                 if (k0 + a_kc[j] >= K) src = g_zero_chunk;
             }
             dma16(src, smem + buf * ASTAGE + (wave * A_INS + j) * 512);
         } else {
             const int t = (j - A_INS) >> 2, kk = (j - A_INS) & 3;
-            const char* blk = w_tile + (size_t)(kb_first + s) * (PACK_ROWS * PACK_BK * 2) + t * 16384;
-            wf[SET][t][kk] = *reinterpret_cast<const bf16x8*>(blk + w_off + (kk >> 1) * 1024 + (kk & 1) * 512);
+            const char* base = valid ? w_tile + (size_t)(kb_first + ls) * (PACK_ROWS * PACK_BK * 2) + t * 16384 +
+                                           (kk >> 1) * 1024 + (kk & 1) * 512
+                                     : reinterpret_cast<const char*>(g_zero_chunk);
+            wf[SET][t][kk] = *reinterpret_cast<const bf16x8*>(base + (w_off & keep));
         }
     };
     constexpr int LPS = LOADS / 4;                // loads per sub-step
@@ -1020,34 +1011,29 @@ __global__ __launch_bounds__(256) void stream_prefill_kernel(FusedArgs p) {
     using T = std::true_type;
     using F = std::false_type;
 
-    // One 64-deep stage s in ring slot / register set P = s % 3.  LD: issue
+    // One 64-deep stage s in ring slot / register set P = s % 3: issues
     // stage s+2's loads (slot and set (P+2) % 3, freed by the previous
-    // stage's barrier), LPS per sub-step; NX: a next stage exists, its first
-    // fragments are read during this stage's last sub-step.
-    auto stage = [&](auto pc, auto ldc, auto nxc, int s) {
+    // stage's barrier), LPS per sub-step, and reads stage s+1's first
+    // fragments during its last sub-step.
+    auto stage = [&](auto pc, int s) {
         constexpr int P = decltype(pc)::value;
-        constexpr bool NX = decltype(nxc)::value;
-        constexpr bool LD = decltype(ldc)::value;
         constexpr int PN = (P + 1) % NBUF, PL = (P + 2) % NBUF;
         using WP = std::integral_constant<int, P>;
         using WL = std::integral_constant<int, PL>;
         const uint32_t so = slot_off(P);
         __builtin_amdgcn_sched_barrier(0);
-        substep(WP{}, 0, 0, T{}, so, 1, ldc, s + 2, PL, WL{}, 0);
-        substep(WP{}, 1, 1, T{}, so, 2, ldc, s + 2, PL, WL{}, 1);
-        substep(WP{}, 2, 0, T{}, so, 3, ldc, s + 2, PL, WL{}, 2);
-        if constexpr (NX) {
-            const uint32_t son = slot_off(PN);
-            // stage s+1 (activations and this wave's weights) has landed once
-            // at most the 3*LPS loads of stage s+2 issued so far are in
-            // flight; after the barrier every wave is done reading slot P
-            __builtin_amdgcn_s_waitcnt(waitcnt_imm(LD ? 3 * LPS : 0, 0));
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            substep(WP{}, 3, 1, T{}, son, 0, ldc, s + 2, PL, WL{}, 3);
-        } else {
-            substep(WP{}, 3, 1, F{}, 0u, 0, F{}, 0, 0, WL{}, 3);
-        }
+        substep(WP{}, 0, 0, T{}, so, 1, T{}, s + 2, PL, WL{}, 0);
+        substep(WP{}, 1, 1, T{}, so, 2, T{}, s + 2, PL, WL{}, 1);
+        substep(WP{}, 2, 0, T{}, so, 3, T{}, s + 2, PL, WL{}, 2);
+        const uint32_t son = slot_off(PN);
+        // stage s+1 (activations and this wave's weights) has landed once at
+        // most the 3*LPS loads of stage s+2 issued so far are in flight (every
+        // stage issues all LOADS loads, also past the end: see below); after
+        // the barrier every wave is done reading slot P
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * LPS, 0));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        substep(WP{}, 3, 1, T{}, son, 0, T{}, s + 2, PL, WL{}, 3);
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -1055,58 +1041,38 @@ __global__ __launch_bounds__(256) void stream_prefill_kernel(FusedArgs p) {
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
 
-    // Ring phase: stage s uses slot / register set (s + phase) % 3, with the
-    // phase chosen so that the two draining stages (ns-2, ns-1) always use
-    // slots 0 and 1; the stages before them that issue loads then run as a
-    // short prefix (slots 3-r .. 2) and whole periods 0, 1, 2.
-    if (ns == 1) {
-        issue_a(0, 0);
-        issue_w(0, I0{});
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-        __builtin_amdgcn_s_barrier();
+    // stages 0 and 1 into slots 0 and 1 (weights of both first, so that
+    // waiting for stage 0 leaves only stage 1's direct loads in flight and
+    // no register load pending into the loop), then periods of three stages
+    // and a remainder of one or two (slots 0, 1)
 #pragma unroll
-        for (int i = 0; i < TM; ++i) read_a(0u, 0, i, 0);
-        stage(I0{}, F{}, F{}, 0);
-    } else {
-        const int nfull = ns - 2;         // stages that issue loads two ahead
-        const int r = nfull % 3;
-        const int phase = (3 - r) % 3;
-        switch (phase) {
-            case 0:
-                issue_a(0, 0); issue_w(0, I0{});
-                issue_a(1, 1); issue_w(1, I1{});
-                break;
-            case 1:
-                issue_a(0, 1); issue_w(0, I1{});
-                issue_a(1, 2); issue_w(1, I2{});
-                break;
-            default:
-                issue_a(0, 2); issue_w(0, I2{});
-                issue_a(1, 0); issue_w(1, I0{});
-                break;
-        }
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(LOADS, 0));
-        __builtin_amdgcn_s_barrier();
-        const uint32_t so0 = (uint32_t)(phase * ASTAGE * 2);
+    for (int j = A_INS; j < LOADS; ++j) issue_one(j, 0, 0, I0{});
 #pragma unroll
-        for (int i = 0; i < TM; ++i) read_a(so0, 0, i, 0);
-        int s = 0;
-        if (r == 2) {
-            stage(I1{}, T{}, T{}, 0);
-            stage(I2{}, T{}, T{}, 1);
-            s = 2;
-        } else if (r == 1) {
-            stage(I2{}, T{}, T{}, 0);
-            s = 1;
-        }
-        for (; s < nfull; s += 3) {
-            stage(I0{}, T{}, T{}, s);
-            stage(I1{}, T{}, T{}, s + 1);
-            stage(I2{}, T{}, T{}, s + 2);
-        }
-        stage(I0{}, F{}, T{}, ns - 2);
-        stage(I1{}, F{}, F{}, ns - 1);
+    for (int j = A_INS; j < LOADS; ++j) issue_one(j, 1, 1, I1{});
+#pragma unroll
+    for (int j = 0; j < A_INS; ++j) issue_one(j, 0, 0, I0{});
+#pragma unroll
+    for (int j = 0; j < A_INS; ++j) issue_one(j, 1, 1, I1{});
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(A_INS, 0));
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) read_a(0u, 0, i, 0);
+    int s = 0;
+    for (; s + 3 <= ns; s += 3) {
+        stage(I0{}, s);
+        stage(I1{}, s + 1);
+        stage(I2{}, s + 2);
     }
+    if (ns - s >= 1) stage(I0{}, s);
+    if (ns - s >= 2) stage(I1{}, s + 1);
+    // the zero-chunk loads of the two stages past the end are still in flight
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+#pragma unroll
+    for (int q = 0; q < NBUF; ++q)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) asm volatile("" ::"v"(wf[q][t][kk]));
 
     if constexpr (SPLIT) {
         store_partials<TM, 1>(acc, p.part, split, M, N, m0, n0 + wave * 32, lane);

@@ -54,6 +54,9 @@ SMALL_SHAPES = [
     (65, 896, 512), (128, 512, 256), (130, 256, 264), (255, 192, 128), (257, 512, 640),
     (300, 136, 520), (2049, 128, 256), (2100, 64, 136),
     (2304, 128, 3840),   # 270 tiles of 256x128: the last column tiles run as 128x128 tiles
+    # streaming prefill kernel: ragged K (zero-chunk activation loads) with each
+    # ring phase, 128- and 256-row tiles, M tails
+    (200, 328, 384), (2600, 520, 256), (3000, 456, 640),
 ]
 
 
