@@ -228,13 +228,23 @@ hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) 
         swk::DecodeArgs d{};
         d.A = a.A; d.Wp = a.W1; d.Y = a.Y;
         d.M = a.M; d.K = a.K; d.N = a.N; d.KB = a.KB;
-        // two 16-column groups per wave (each activation fragment feeds twice
-        // the weight bytes) when that still leaves >= 2 workgroups per CU
-        const bool wide = p.decode_mt > 1 && ceil_div(a.N, 32) >= 2 * p.cus;
+        // Column groups per workgroup (CG) and K blocks in flight per wave
+        // (UNROLL), measured on this chip: wider groups read each activation
+        // fragment for more weight bytes and stream longer contiguous runs of
+        // the packed blocks; they pay off for long K (>= 96 blocks) as long
+        // as the grid still gives about one workgroup per CU.
+        const bool long_k = p.KB >= 96;
+        const int64_t wg64 = ceil_div(a.N, 64), wg128 = ceil_div(a.N, 128);
         switch (p.decode_mt) {
-            case 1: return wide ? launch_decode<1, 2, 2>(d, s) : launch_decode<1, 1, 4>(d, s);
-            case 2: return wide ? launch_decode<2, 2, 2>(d, s) : launch_decode<2, 1, 2>(d, s);
-            default: return wide ? launch_decode<4, 2, 1>(d, s) : launch_decode<4, 1, 2>(d, s);
+            case 1:
+                return (long_k && 4 * wg128 >= 3 * p.cus) ? launch_decode<1, 8, 2>(d, s)
+                                                         : launch_decode<1, 1, 8>(d, s);
+            case 2:
+                if (long_k && 4 * wg64 >= 3 * p.cus) return launch_decode<2, 4, 1>(d, s);
+                return 2 * wg128 >= p.cus ? launch_decode<2, 8, 1>(d, s) : launch_decode<2, 2, 2>(d, s);
+            default:
+                return (long_k && 4 * wg64 >= 3 * p.cus) ? launch_decode<4, 4, 1>(d, s)
+                                                        : launch_decode<4, 2, 1>(d, s);
         }
     }
     const int grid = p.tiles * p.splits;
