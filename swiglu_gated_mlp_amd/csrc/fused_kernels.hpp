@@ -842,19 +842,13 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
     return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
 }
 
-//   NB = 2 is the two-workgroups-per-CU form (half the registers, a third
-//   of the LDS): loads one stage ahead, all issued in the first sub-step and
-//   waited for in full at the barrier; the other resident workgroup's MFMAs
-//   cover those waits and this workgroup's epilogue.
-template <int BM, bool SPLIT, bool RAGGED, int NB = 3>
-__global__ __launch_bounds__(256, NB == 2 ? 2 : 1) void stream_prefill_kernel(FusedArgs p) {
+template <int BM, bool SPLIT, bool RAGGED>
+__global__ __launch_bounds__(256) void stream_prefill_kernel(FusedArgs p) {
     constexpr int NW = 4;                       // waves, 32 output columns each
     constexpr int TM = BM / 32;                 // 32-row MFMA tiles per wave
     constexpr int A_INS = BM / 8 / NW;          // 1 KiB direct loads per wave per stage
     constexpr int ASTAGE = BM * BK;             // elements per activation stage
-    constexpr int NBUF = NB;                    // ring slots == weight register sets
-    constexpr int DIST = NB - 1;                // stages loaded ahead
-    static_assert(NB == 2 || NB == 3, "ring of two or three slots");
+    constexpr int NBUF = 3;                     // ring slots == weight register sets
     constexpr int LOADS = A_INS + 8;            // vector-memory instructions per wave per stage
     constexpr int SMEM = NBUF * ASTAGE > BM * PACK_BN ? NBUF * ASTAGE : BM * PACK_BN;
     constexpr int GROUP_M = 8;
@@ -977,10 +971,8 @@ __global__ __launch_bounds__(256, NB == 2 ? 2 : 1) void stream_prefill_kernel(Fu
             wf[SET][t][kk] = *reinterpret_cast<const bf16x8*>(base + (w_off & keep));
         }
     };
-    // NB = 3: the stage's loads spread over its four sub-steps; NB = 2: all
-    // in the first sub-step (they must land by this stage's barrier)
-    constexpr int LPS = NB == 3 ? LOADS / 4 : LOADS;   // loads per loading sub-step
-    static_assert(NB == 2 || LOADS % 4 == 0, "loads split over four sub-steps");
+    constexpr int LPS = LOADS / 4;                // loads per sub-step
+    static_assert(LOADS % 4 == 0, "loads split over four sub-steps");
     constexpr int LPI = (LPS + TM - 1) / TM;      // loads per 32-row step
     constexpr int RPI = TM >= 2 ? 2 : 1;          // next-sub-step reads per step
     // One 16-deep sub-step on fragment set CUR, in a fixed order (each step
@@ -1019,32 +1011,29 @@ __global__ __launch_bounds__(256, NB == 2 ? 2 : 1) void stream_prefill_kernel(Fu
     using T = std::true_type;
     using F = std::false_type;
 
-    // One 64-deep stage s in ring slot / register set P = s % NB: issues
-    // stage s+DIST's loads (slot and set (P+DIST) % NB, freed by the previous
-    // stage's barrier) and reads stage s+1's first fragments during its last
-    // sub-step.
+    // One 64-deep stage s in ring slot / register set P = s % 3: issues
+    // stage s+2's loads (slot and set (P+2) % 3, freed by the previous
+    // stage's barrier), LPS per sub-step, and reads stage s+1's first
+    // fragments during its last sub-step.
     auto stage = [&](auto pc, int s) {
         constexpr int P = decltype(pc)::value;
-        constexpr int PN = (P + 1) % NBUF, PL = (P + DIST) % NBUF;
+        constexpr int PN = (P + 1) % NBUF, PL = (P + 2) % NBUF;
         using WP = std::integral_constant<int, P>;
         using WL = std::integral_constant<int, PL>;
-        using L1 = std::integral_constant<bool, NB == 3>;   // sub-steps 1..3 load too
         const uint32_t so = slot_off(P);
         __builtin_amdgcn_sched_barrier(0);
-        substep(WP{}, 0, 0, T{}, so, 1, T{}, s + DIST, PL, WL{}, 0);
-        substep(WP{}, 1, 1, T{}, so, 2, L1{}, s + DIST, PL, WL{}, 1);
-        substep(WP{}, 2, 0, T{}, so, 3, L1{}, s + DIST, PL, WL{}, 2);
+        substep(WP{}, 0, 0, T{}, so, 1, T{}, s + 2, PL, WL{}, 0);
+        substep(WP{}, 1, 1, T{}, so, 2, T{}, s + 2, PL, WL{}, 1);
+        substep(WP{}, 2, 0, T{}, so, 3, T{}, s + 2, PL, WL{}, 2);
         const uint32_t son = slot_off(PN);
         // stage s+1 (activations and this wave's weights) has landed once at
-        // most the loads of stage s+DIST issued so far in this stage are in
-        // flight (3*LPS for NB = 3; for NB = 2 they are stage s+1's own).
-        // Every stage issues exactly LOADS vector-memory instructions, also
-        // past the end (see below).  After the barrier every wave is done
-        // reading slot P.
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(NB == 3 ? 3 * LPS : 0, 0));
+        // most the 3*LPS loads of stage s+2 issued so far are in flight (every
+        // stage issues all LOADS loads, also past the end: see below); after
+        // the barrier every wave is done reading slot P
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * LPS, 0));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        substep(WP{}, 3, 1, T{}, son, 0, L1{}, s + DIST, PL, WL{}, 3);
+        substep(WP{}, 3, 1, T{}, son, 0, T{}, s + 2, PL, WL{}, 3);
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -1052,48 +1041,31 @@ __global__ __launch_bounds__(256, NB == 2 ? 2 : 1) void stream_prefill_kernel(Fu
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
 
-    if constexpr (NB == 3) {
-        // stages 0 and 1 into slots 0 and 1 (weights of both first, so that
-        // waiting for stage 0 leaves only stage 1's direct loads in flight and
-        // no register load pending into the loop), then periods of three
-        // stages and a remainder of one or two (slots 0, 1)
+    // stages 0 and 1 into slots 0 and 1 (weights of both first, so that
+    // waiting for stage 0 leaves only stage 1's direct loads in flight and
+    // no register load pending into the loop), then periods of three stages
+    // and a remainder of one or two (slots 0, 1)
 #pragma unroll
-        for (int j = A_INS; j < LOADS; ++j) issue_one(j, 0, 0, I0{});
+    for (int j = A_INS; j < LOADS; ++j) issue_one(j, 0, 0, I0{});
 #pragma unroll
-        for (int j = A_INS; j < LOADS; ++j) issue_one(j, 1, 1, I1{});
+    for (int j = A_INS; j < LOADS; ++j) issue_one(j, 1, 1, I1{});
 #pragma unroll
-        for (int j = 0; j < A_INS; ++j) issue_one(j, 0, 0, I0{});
+    for (int j = 0; j < A_INS; ++j) issue_one(j, 0, 0, I0{});
 #pragma unroll
-        for (int j = 0; j < A_INS; ++j) issue_one(j, 1, 1, I1{});
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(A_INS, 0));
-        __builtin_amdgcn_s_barrier();
+    for (int j = 0; j < A_INS; ++j) issue_one(j, 1, 1, I1{});
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(A_INS, 0));
+    __builtin_amdgcn_s_barrier();
 #pragma unroll
-        for (int i = 0; i < TM; ++i) read_a(0u, 0, i, 0);
-        int s = 0;
-        for (; s + 3 <= ns; s += 3) {
-            stage(I0{}, s);
-            stage(I1{}, s + 1);
-            stage(std::integral_constant<int, 2 % NBUF>{}, s + 2);
-        }
-        if (ns - s >= 1) stage(I0{}, s);
-        if (ns - s >= 2) stage(I1{}, s + 1);
-    } else {
-        // stage 0 into slot 0, then periods of two stages and a remainder of
-        // one (slot 0)
-#pragma unroll
-        for (int j = 0; j < LOADS; ++j) issue_one(j, 0, 0, I0{});
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-        __builtin_amdgcn_s_barrier();
-#pragma unroll
-        for (int i = 0; i < TM; ++i) read_a(0u, 0, i, 0);
-        int s = 0;
-        for (; s + 2 <= ns; s += 2) {
-            stage(I0{}, s);
-            stage(I1{}, s + 1);
-        }
-        if (ns - s >= 1) stage(I0{}, s);
+    for (int i = 0; i < TM; ++i) read_a(0u, 0, i, 0);
+    int s = 0;
+    for (; s + 3 <= ns; s += 3) {
+        stage(I0{}, s);
+        stage(I1{}, s + 1);
+        stage(I2{}, s + 2);
     }
-    // the zero-chunk loads of the stages past the end are still in flight
+    if (ns - s >= 1) stage(I0{}, s);
+    if (ns - s >= 2) stage(I1{}, s + 1);
+    // the zero-chunk loads of the two stages past the end are still in flight
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 #pragma unroll
     for (int q = 0; q < NBUF; ++q)
