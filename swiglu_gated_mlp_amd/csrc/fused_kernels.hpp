@@ -842,26 +842,33 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
     return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
 }
 
+// LDS elements one BM-row streaming tile needs: the three ring slots, reused
+// for the Y tile in the epilogue
+template <int BM>
+constexpr int stream_smem_elems() {
+    return 3 * BM * BK > BM * PACK_BN ? 3 * BM * BK : BM * PACK_BN;
+}
+
+// One output tile (one K split) of the streaming kernel: workgroup bid of
+// nblocks, LDS at smem (stream_smem_elems<BM>() elements, 16-byte aligned).
 template <int BM, bool SPLIT, bool RAGGED>
-__global__ __launch_bounds__(256) void stream_prefill_kernel(FusedArgs p) {
+__device__ __forceinline__ void stream_prefill_tile(const FusedArgs& p, uint16_t* smem, int bid, int nblocks) {
     constexpr int NW = 4;                       // waves, 32 output columns each
     constexpr int TM = BM / 32;                 // 32-row MFMA tiles per wave
     constexpr int A_INS = BM / 8 / NW;          // 1 KiB direct loads per wave per stage
     constexpr int ASTAGE = BM * BK;             // elements per activation stage
     constexpr int NBUF = 3;                     // ring slots == weight register sets
     constexpr int LOADS = A_INS + 8;            // vector-memory instructions per wave per stage
-    constexpr int SMEM = NBUF * ASTAGE > BM * PACK_BN ? NBUF * ASTAGE : BM * PACK_BN;
     constexpr int GROUP_M = 8;
     static_assert(TM >= 1 && A_INS >= 1 && (BM / 8) % NW == 0, "tile");
     static_assert(LOADS <= 63, "vmcnt range");
-    __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     const int S = SPLIT ? p.splits : 1;
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int logical = xcd_remap(bid, nblocks);
     const int tile = SPLIT ? logical / S : logical;
     const int split = SPLIT ? logical - tile * S : 0;
     int tm, tn;
@@ -1111,6 +1118,25 @@ __global__ __launch_bounds__(256) void stream_prefill_kernel(FusedArgs p) {
         const int m = m0 + r, n = n0 + 8 * c;
         if (m < M && n < N) *reinterpret_cast<u32x4*>(p.Y + (size_t)m * N + n) = v;
     }
+}
+
+template <int BM, bool SPLIT, bool RAGGED>
+__global__ __launch_bounds__(256) void stream_prefill_kernel(FusedArgs p) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[stream_smem_elems<BM>()];
+    stream_prefill_tile<BM, SPLIT, RAGGED>(p, smem, blockIdx.x, gridDim.x);
+}
+
+// The 256-row grid and its 128-row tail column tiles in one launch: blocks
+// 0 .. n_big-1 run the 256-row tiles of `big`, the rest the 128-row tiles of
+// `tail`, so the tail tiles start on CUs as the last 256-row tiles finish
+// instead of after a second launch.
+template <bool RAGGED>
+__global__ __launch_bounds__(256) void stream_prefill_mixed_kernel(FusedArgs big, FusedArgs tail, int n_big) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[stream_smem_elems<256>()];
+    static_assert(stream_smem_elems<256>() >= stream_smem_elems<128>(), "one LDS block serves both tiles");
+    const int b = blockIdx.x;
+    if (b < n_big) stream_prefill_tile<256, false, RAGGED>(big, smem, b, n_big);
+    else stream_prefill_tile<128, false, RAGGED>(tail, smem, b - n_big, gridDim.x - n_big);
 }
 
 // ---------------------------------------------------------------------------

@@ -261,14 +261,20 @@ hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) 
         default: {
             if (split) return launch_stream<256, true>(a, grid, s);
             if (p.tail_ntiles == 0) return launch_stream<256, false>(a, grid, s);
+            // one launch: the 256-row tiles of the first column tiles, then
+            // the last tail_ntiles column tiles as 128-row tiles
             swk::FusedArgs big = a, tail = a;
             big.tiles_n = p.tiles_n - p.tail_ntiles;
-            hipError_t e = launch_stream<256, false>(big, big.tiles_m * big.tiles_n, s);
-            if (e != hipSuccess) return e;
             tail.tiles_m = (int)ceil_div(a.M, 128);
             tail.tiles_n = p.tail_ntiles;
             tail.n_tile0 = big.tiles_n;
-            return launch_stream<128, false>(tail, tail.tiles_m * tail.tiles_n, s);
+            int n_big = big.tiles_m * big.tiles_n;
+            const int grid_all = n_big + tail.tiles_m * tail.tiles_n;
+            const void* fn = (a.K % swk::BK) != 0
+                                 ? reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<true>)
+                                 : reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<false>);
+            void* kargs[] = {&big, &tail, &n_big};
+            return hipLaunchKernel(fn, dim3(grid_all), dim3(256), kargs, 0, s);
         }
     }
 }
