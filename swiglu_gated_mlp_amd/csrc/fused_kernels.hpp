@@ -439,6 +439,17 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_tile_kernel(FusedArgs p) {
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
+// 16-byte global store that the compiler does not track: the streaming
+// kernel leaves its Y stores in flight across the next tile's K loop, and a
+// tracked store would make the compiler's own waits for later register
+// loads conservative (it treats loads and stores as completing in any order
+// relative to each other).  The kernel's explicit waits only ever rely on
+// loads completing in order among themselves, which extra stores in the
+// count cannot break.  The s_nop covers the store-data read of the VGPRs.
+__device__ __forceinline__ void store16_untracked(uint16_t* gdst, u32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" ::"v"(gdst), "v"(v) : "memory");
+}
+
 __device__ __forceinline__ void dma16(const uint16_t* gsrc, uint16_t* lds_dst) {
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gsrc),
                                      (lds_void_ptr)(lds_dst), 16, 0, 0);
@@ -842,89 +853,124 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
     return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
 }
 
-// LDS elements one BM-row streaming tile needs: the three ring slots, reused
-// for the Y tile in the epilogue
+// LDS elements of the streaming kernel: three ring slots of BM x 64
+// activations, then the BM x 128 Y tile of the epilogue (kept apart from the
+// ring so that the next tile's first stages can stream in meanwhile)
 template <int BM>
 constexpr int stream_smem_elems() {
-    return 3 * BM * BK > BM * PACK_BN ? 3 * BM * BK : BM * PACK_BN;
+    return 3 * BM * BK + BM * PACK_BN;
 }
 
-// One output tile (one K split) of the streaming kernel: workgroup bid of
-// nblocks, LDS at smem (stream_smem_elems<BM>() elements, 16-byte aligned).
+// Output tiles (or K splits) w = first, first + stride, ... < total of the
+// streaming kernel, one after another in one workgroup; LDS at smem
+// (stream_smem_elems<BM>() elements, 16-byte aligned).  Between two tiles the
+// next tile's first two stages are issued before the epilogue of the
+// current one, and its Y stores are left in flight while the next tile's K
+// loop starts.
 template <int BM, bool SPLIT, bool RAGGED>
-__device__ __forceinline__ void stream_prefill_tile(const FusedArgs& p, uint16_t* smem, int bid, int nblocks) {
+__device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_t* smem, int first, int stride,
+                                                     int total) {
     constexpr int NW = 4;                       // waves, 32 output columns each
     constexpr int TM = BM / 32;                 // 32-row MFMA tiles per wave
     constexpr int A_INS = BM / 8 / NW;          // 1 KiB direct loads per wave per stage
     constexpr int ASTAGE = BM * BK;             // elements per activation stage
     constexpr int NBUF = 3;                     // ring slots == weight register sets
     constexpr int LOADS = A_INS + 8;            // vector-memory instructions per wave per stage
+    constexpr int NST = BM / 16;                // Y stores per wave per tile
     constexpr int GROUP_M = 8;
     static_assert(TM >= 1 && A_INS >= 1 && (BM / 8) % NW == 0, "tile");
-    static_assert(LOADS <= 63, "vmcnt range");
+    static_assert(LOADS + NST <= 63, "vmcnt range");
+    uint16_t* const sY = smem + NBUF * ASTAGE;  // the Y tile
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
+    const int M = p.M, K = p.K, N = p.N, KB = p.KB;
     const int S = SPLIT ? p.splits : 1;
-    const int logical = xcd_remap(bid, nblocks);
-    const int tile = SPLIT ? logical / S : logical;
-    const int split = SPLIT ? logical - tile * S : 0;
-    int tm, tn;
-    {
+
+    // work item w -> output tile (m0, n0) and K blocks [kb_first, kb_first + ns)
+    struct Item {
+        int m0, n0, kb_first, ns, split;
+    };
+    auto item_of = [&](int w) {
+        const int logical = xcd_remap(w, total);
+        const int tile = SPLIT ? logical / S : logical;
+        const int split = SPLIT ? logical - tile * S : 0;
         const int per_group = GROUP_M * p.tiles_n;
         const int group = tile / per_group;
         const int first_m = group * GROUP_M;
         const int gsize = min(p.tiles_m - first_m, GROUP_M);
         const int in_group = tile - group * per_group;
-        tm = first_m + in_group % gsize;
-        tn = in_group / gsize;
-    }
-    const int m0 = tm * BM;
-    const int n0 = (p.n_tile0 + tn) * PACK_BN;
-    const int M = p.M, K = p.K, N = p.N, KB = p.KB;
-    const int kb_first = SPLIT ? split * p.kb_per_split : 0;
-    const int kb_end = SPLIT ? min(KB, kb_first + p.kb_per_split) : KB;
-    const int ns = kb_end - kb_first;           // >= 1: the host never makes an empty split
+        Item it;
+        it.m0 = (first_m + in_group % gsize) * BM;
+        it.n0 = (p.n_tile0 + in_group / gsize) * PACK_BN;
+        it.kb_first = SPLIT ? split * p.kb_per_split : 0;
+        it.ns = (SPLIT ? min(KB, it.kb_first + p.kb_per_split) : KB) - it.kb_first;   // >= 1
+        it.split = split;
+        return it;
+    };
 
     // activation: lane l of direct load i fetches row (wave*A_INS+i)*8 + l/8,
     // logical chunk (l%8) ^ swz(row), so LDS holds the tile in lds_off order;
     // byte offsets from A (the host keeps M*K*2 below 4 GiB) so the uniform
     // part of the address stays scalar
     uint32_t a_off[A_INS];
-    int a_kc[A_INS];
-#pragma unroll
-    for (int i = 0; i < A_INS; ++i) {
-        const int r = (wave * A_INS + i) * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ swz(r);
-        a_off[i] = (uint32_t)(((size_t)min(m0 + r, M - 1) * K + 8 * c) * 2);
-        a_kc[i] = 8 * c;
-    }
+    // lane l's logical chunk in direct load i is (l%8) ^ swz(row) with
+    // row = (wave*A_INS + i)*8 + l/8, i.e. chunk_x ^ ((wave*A_INS + i) & 7)
+    // with chunk_x = ((l & 7) ^ (l >> 3)) & 7 (only the ragged K stage needs it)
+    int chunk_x = 0;
     // weights: lane l needs column wave*32 + (l & 31) and the 8 k at chunk
     // c = 2kk + (l >> 5) of each 64-deep block, i.e. packed group
     // t*8 + wave*2 + ((l >> 4) & 1), half kk >> 1, fragment lane
     // (2(kk & 1) + (l >> 5))*16 + (l & 15): a lane byte offset plus a
     // constant per (t, kk)
-    const uint32_t w_off = (uint32_t)(((wave * 2 + ((lane >> 4) & 1)) * 1024 + (lane >> 5) * 128 + (lane & 15) * 8) * 2);
-    const char* w_tile = reinterpret_cast<const char*>(p.W1) + (size_t)(n0 / PACK_BN) * KB * (PACK_ROWS * PACK_BK * 2);
+    uint32_t w_off = 0;
+    const char* w_tile = nullptr;
+    // the item whose stages the loads below fetch (ld_ns = 0: none, every
+    // load reads the zero chunk)
+    int ld_kb_first = 0, ld_ns = 0;
+    auto load_item = [&](const Item& it, bool valid) {
+        // lane index behind an opaque copy: recomputed per item rather than
+        // hoisted out of the tile loop (see the epilogue)
+        int ll = lane;
+        asm volatile("" : "+v"(ll));
+#pragma unroll
+        for (int i = 0; i < A_INS; ++i) {
+            const int r = (wave * A_INS + i) * 8 + (ll >> 3);
+            const int c = (ll & 7) ^ swz(r);
+            a_off[i] = (uint32_t)(((size_t)min(it.m0 + r, M - 1) * K + 8 * c) * 2);
+        }
+        chunk_x = ((ll & 7) ^ (ll >> 3)) & 7;
+        w_off = (uint32_t)(((wave * 2 + ((ll >> 4) & 1)) * 1024 + (ll >> 5) * 128 + (ll & 15) * 8) * 2);
+        w_tile = reinterpret_cast<const char*>(p.W1) + (size_t)(it.n0 / PACK_BN) * KB * (PACK_ROWS * PACK_BK * 2);
+        ld_kb_first = it.kb_first;
+        ld_ns = valid ? it.ns : 0;
+    };
     // fragment reads: lane l reads row i*32 + (l & 31), logical chunk
     // 2kk + (l >> 5).  swz(i*32 + r) = swz(r) ^ 4(i & 1) for r < 32, so the
     // physical chunk is ((l >> 5) ^ swz(l & 31)) ^ 2(kk ^ 2(i & 1)): four lane
     // base offsets (x = kk ^ 2(i & 1)) plus i*4096 bytes plus the ring slot
-    const int lrow = lane & 31;
-    const int hs = (lane >> 5) ^ swz(lrow);
     uint32_t rd_base[4];
+    // formed per item from an opaque lane copy (not held across epilogues)
+    auto set_rd_base = [&]() {
+        int lr = lane;
+        asm volatile("" : "+v"(lr));
+        const int lrow = lr & 31;
+        const int hs = (lr >> 5) ^ swz(lrow);
 #pragma unroll
-    for (int x = 0; x < 4; ++x) rd_base[x] = (uint32_t)((lrow * BK + ((hs ^ (2 * x)) << 3)) * 2);
+        for (int x = 0; x < 4; ++x) rd_base[x] = (uint32_t)((lrow * BK + ((hs ^ (2 * x)) << 3)) * 2);
+    };
 
     f32x16 acc[2][TM][1];
+    auto zero_acc = [&]() {
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+        for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[g][i][0][r] = 0.0f;
+                for (int r = 0; r < 16; ++r) acc[g][i][0][r] = 0.0f;
+    };
+    zero_acc();
     bf16x8 fa[2][TM];
     bf16x8 wf[NBUF][2][4];
     // every register set defined on every path into the stage loop
@@ -947,32 +993,31 @@ __device__ __forceinline__ void stream_prefill_tile(const FusedArgs& p, uint16_t
         fa[set][i] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(smem) + so + i * 4096 +
                                                       rd_base[kk ^ (2 * (i & 1))]);
     };
-    // Stages past the last (ls >= ns) are issued like any other, but every
+    // Stages past the last (ls >= ld_ns) are issued like any other, but every
     // lane then reads the 16-byte zero chunk (a single cache line): the
     // stage code stays the same for every stage, with no tail variants.
-    // Their weight registers are consumed (without instructions) after the
-    // loop, so those loads are not dropped as dead code and every stage
-    // issues exactly LOADS vector-memory instructions, which the wait counts
-    // rely on.
+    // Their weight registers are consumed (without instructions) at the end,
+    // so those loads are not dropped as dead code and every stage issues
+    // exactly LOADS vector-memory instructions, which the wait counts rely on.
     // load j of stage ls: j < A_INS the activation direct load j into slot
     // buf, else weight fragment (t, kk) = ((j - A_INS) / 4, (j - A_INS) % 4)
     // into register set SET
     auto issue_one = [&](int j, int ls, int buf, auto setc) {
         constexpr int SET = decltype(setc)::value;
-        const bool valid = ls < ns;
+        const bool valid = ls < ld_ns;
         const uint32_t keep = valid ? 0xffffffffu : 0u;
         if (j < A_INS) {
-            const int k0 = (kb_first + ls) * BK;
+            const int k0 = (ld_kb_first + ls) * BK;
             const char* base = valid ? reinterpret_cast<const char*>(p.A) + (size_t)k0 * 2
                                      : reinterpret_cast<const char*>(g_zero_chunk);
             const uint16_t* src = reinterpret_cast<const uint16_t*>(base + (a_off[j] & keep));
             if constexpr (RAGGED) {
-                if (k0 + a_kc[j] >= K) src = g_zero_chunk;
+                if (k0 + 8 * (chunk_x ^ ((wave * A_INS + j) & 7)) >= K) src = g_zero_chunk;
             }
             dma16(src, smem + buf * ASTAGE + (wave * A_INS + j) * 512);
         } else {
             const int t = (j - A_INS) >> 2, kk = (j - A_INS) & 3;
-            const char* base = valid ? w_tile + (size_t)(kb_first + ls) * (PACK_ROWS * PACK_BK * 2) + t * 16384 +
+            const char* base = valid ? w_tile + (size_t)(ld_kb_first + ls) * (PACK_ROWS * PACK_BK * 2) + t * 16384 +
                                            (kk >> 1) * 1024 + (kk & 1) * 512
                                      : reinterpret_cast<const char*>(g_zero_chunk);
             wf[SET][t][kk] = *reinterpret_cast<const bf16x8*>(base + (w_off & keep));
@@ -1048,95 +1093,169 @@ __device__ __forceinline__ void stream_prefill_tile(const FusedArgs& p, uint16_t
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
 
-    // stages 0 and 1 into slots 0 and 1 (weights of both first, so that
-    // waiting for stage 0 leaves only stage 1's direct loads in flight and
-    // no register load pending into the loop), then periods of three stages
-    // and a remainder of one or two (slots 0, 1)
+
+    // stages 0 and 1 of an item into slots 0 and 1 and register sets 0 and 1
+    auto issue_first_w = [&]() {
 #pragma unroll
-    for (int j = A_INS; j < LOADS; ++j) issue_one(j, 0, 0, I0{});
+        for (int j = A_INS; j < LOADS; ++j) issue_one(j, 0, 0, I0{});
 #pragma unroll
-    for (int j = A_INS; j < LOADS; ++j) issue_one(j, 1, 1, I1{});
+        for (int j = A_INS; j < LOADS; ++j) issue_one(j, 1, 1, I1{});
+    };
+    auto issue_first_a = [&]() {
 #pragma unroll
-    for (int j = 0; j < A_INS; ++j) issue_one(j, 0, 0, I0{});
+        for (int j = 0; j < A_INS; ++j) issue_one(j, 0, 0, I0{});
 #pragma unroll
-    for (int j = 0; j < A_INS; ++j) issue_one(j, 1, 1, I1{});
+        for (int j = 0; j < A_INS; ++j) issue_one(j, 1, 1, I1{});
+    };
+
+    // first item: weights of both stages first, so that waiting for stage 0
+    // leaves only stage 1's direct loads in flight, no register load pending
+    // into the loop
+    Item cur = item_of(first);
+    load_item(cur, true);
+    issue_first_w();
+    issue_first_a();
+    set_rd_base();
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(A_INS, 0));
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int i = 0; i < TM; ++i) read_a(0u, 0, i, 0);
-    int s = 0;
-    for (; s + 3 <= ns; s += 3) {
-        stage(I0{}, s);
-        stage(I1{}, s + 1);
-        stage(I2{}, s + 2);
+
+    for (int w = first;;) {
+        const int ns = cur.ns;
+        // periods of three stages and a remainder of one or two (slots 0, 1)
+        int s = 0;
+        for (; s + 3 <= ns; s += 3) {
+            stage(I0{}, s);
+            stage(I1{}, s + 1);
+            stage(I2{}, s + 2);
+        }
+        if (ns - s >= 1) stage(I0{}, s);
+        if (ns - s >= 2) stage(I1{}, s + 1);
+        // the zero-chunk loads of the two stages past the end are still in
+        // flight (their weight registers are consumed here, without
+        // instructions, so the loads are not dropped); after the barrier no
+        // wave reads the ring any more
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+#pragma unroll
+        for (int q = 0; q < NBUF; ++q)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) asm volatile("" ::"v"(wf[q][t][kk]));
+        __builtin_amdgcn_s_barrier();
+
+        if constexpr (SPLIT) {
+            store_partials<TM, 1>(acc, p.part, cur.split, M, N, cur.m0, cur.n0 + wave * 32, lane);
+            break;   // one item per workgroup
+        }
+
+        // the next item's first two stages stream in during this epilogue
+        // (past the last item they read the zero chunk): activations and
+        // stage 0's weights now, stage 1's weights once the accumulators are
+        // consumed
+        const int wn = w + stride;
+        const bool more = wn < total;
+        const Item nxt = item_of(more ? wn : w);
+        load_item(nxt, more);
+        issue_first_a();
+#pragma unroll
+        for (int j = A_INS; j < LOADS; ++j) issue_one(j, 0, 0, I0{});
+
+        // Epilogue: SiLU(Gate) * Up -> bf16 into the LDS Y tile (16-byte chunk
+        // index XOR row & 15, and the two 8-byte halves swapped on rows with
+        // bit 4 set, so each 32-lane write pass covers all banks), then whole
+        // 256-byte row segments to HBM, left in flight.
+        // (one 32-row step at a time, so the accumulators are not all moved
+        // to VGPRs at once).  `el` is the lane index behind an opaque copy:
+        // the epilogue's many lane-dependent addresses are then formed here,
+        // per tile, instead of being hoisted out of the tile loop and held
+        // in registers across every K loop.
+        int el = lane;
+        asm volatile("" : "+v"(el));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int r = i * 32 + (el & 31);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = silu_f(acc[0][i][0][4 * q + e]) * acc[1][i][0][4 * q + e];
+                u32x2 out;
+                out[0] = pack2(v[0], v[1]);
+                out[1] = pack2(v[2], v[3]);
+                const int chunk = wave * 4 + q;
+                *reinterpret_cast<u32x2*>(sY + r * PACK_BN + 8 * (chunk ^ (r & 15)) +
+                                          4 * ((el >> 5) ^ ((r >> 4) & 1))) = out;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // the offsets are formed again rather than held through the epilogue
+        load_item(nxt, more);
+#pragma unroll
+        for (int j = A_INS; j < LOADS; ++j) issue_one(j, 1, 1, I1{});
+        // the next item's stage 0 (and stage 1's activations) has landed once
+        // at most stage 1's weight loads are in flight; the Y tile is in LDS
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(8, 0));
+        __builtin_amdgcn_s_barrier();
+        {
+            // wave w stores rows w*BM/4 + 4t + l/16, 16 bytes at column 8(l%16)
+            const int r0 = wave * (BM / 4) + (el >> 4);
+            const int c = el & 15;
+            const int n = cur.n0 + 8 * c;
+            const int rows_left = M - cur.m0 - r0;   // rows r0 + 4t < M - m0
+            uint16_t* yp = p.Y + (size_t)(cur.m0 + r0) * N + n;
+#pragma unroll
+            for (int t = 0; t < NST; ++t) {
+                const int r = r0 + t * 4;
+                u32x4 v = *reinterpret_cast<const u32x4*>(sY + r * PACK_BN + 8 * (c ^ (r & 15)));
+                if ((r >> 4) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+                if (4 * t < rows_left && n < N) store16_untracked(yp + (size_t)t * 4 * N, v);
+            }
+        }
+        if (!more) break;
+
+        // next item: the Y stores stay in flight into its K loop
+        zero_acc();
+        cur = nxt;
+        w = wn;
+        set_rd_base();
+#pragma unroll
+        for (int i = 0; i < TM; ++i) read_a(0u, 0, i, 0);
     }
-    if (ns - s >= 1) stage(I0{}, s);
-    if (ns - s >= 2) stage(I1{}, s + 1);
-    // the zero-chunk loads of the two stages past the end are still in flight
+    // the zero-chunk loads of the stages past the last item are in flight
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 #pragma unroll
-    for (int q = 0; q < NBUF; ++q)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) asm volatile("" ::"v"(wf[q][t][kk]));
-
-    if constexpr (SPLIT) {
-        store_partials<TM, 1>(acc, p.part, split, M, N, m0, n0 + wave * 32, lane);
-        return;
-    }
-
-    // Epilogue: SiLU(Gate) * Up -> bf16 into an LDS copy of the BM x 128 Y
-    // tile (16-byte chunk index XOR row & 15, and the two 8-byte halves
-    // swapped on rows with bit 4 set, so each 32-lane write pass covers all
-    // banks), then whole 256-byte row segments to HBM.  No load is in flight
-    // and every wave is past its last fragment read after the barrier.
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int r = i * 32 + (lane & 31);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            float v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = silu_f(acc[0][i][0][4 * q + e]) * acc[1][i][0][4 * q + e];
-            u32x2 out;
-            out[0] = pack2(v[0], v[1]);
-            out[1] = pack2(v[2], v[3]);
-            const int chunk = wave * 4 + q;
-            *reinterpret_cast<u32x2*>(smem + r * PACK_BN + 8 * (chunk ^ (r & 15)) +
-                                      4 * ((lane >> 5) ^ ((r >> 4) & 1))) = out;
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < BM / 16; ++t) {
-        const int r = wave * (BM / 4) + t * 4 + (lane >> 4);
-        const int c = lane & 15;
-        u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * PACK_BN + 8 * (c ^ (r & 15)));
-        if ((r >> 4) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-        const int m = m0 + r, n = n0 + 8 * c;
-        if (m < M && n < N) *reinterpret_cast<u32x4*>(p.Y + (size_t)m * N + n) = v;
-    }
 }
 
 template <int BM, bool SPLIT, bool RAGGED>
-__global__ __launch_bounds__(256) void stream_prefill_kernel(FusedArgs p) {
+__global__ __launch_bounds__(256) void stream_prefill_kernel(FusedArgs p, int total) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[stream_smem_elems<BM>()];
-    stream_prefill_tile<BM, SPLIT, RAGGED>(p, smem, blockIdx.x, gridDim.x);
+    stream_prefill_tiles<BM, SPLIT, RAGGED>(p, smem, blockIdx.x, gridDim.x, total);
 }
 
-// The 256-row grid and its 128-row tail column tiles in one launch: blocks
-// 0 .. n_big-1 run the 256-row tiles of `big`, the rest the 128-row tiles of
-// `tail`, so the tail tiles start on CUs as the last 256-row tiles finish
-// instead of after a second launch.
+// The 256-row tiles and the 128-row tail column tiles in one launch: blocks
+// 0 .. n_pers-1 work through the n_big 256-row tiles of `big` (block b takes
+// tiles b, b + n_pers, ...), the remaining blocks take one 128-row tile of
+// `tail` each and start on CUs as the 256-row work drains.
 template <bool RAGGED>
-__global__ __launch_bounds__(256) void stream_prefill_mixed_kernel(FusedArgs big, FusedArgs tail, int n_big) {
+__global__ __launch_bounds__(256) void stream_prefill_mixed_kernel(FusedArgs big, FusedArgs tail, int n_pers,
+                                                                   int n_big) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[stream_smem_elems<256>()];
     static_assert(stream_smem_elems<256>() >= stream_smem_elems<128>(), "one LDS block serves both tiles");
     const int b = blockIdx.x;
-    if (b < n_big) stream_prefill_tile<256, false, RAGGED>(big, smem, b, n_big);
-    else stream_prefill_tile<128, false, RAGGED>(tail, smem, b - n_big, gridDim.x - n_big);
+    if (b < n_pers) {
+        stream_prefill_tiles<256, false, RAGGED>(big, smem, b, n_pers, n_big);
+    } else {
+        const int n_tail = gridDim.x - n_pers;
+        stream_prefill_tiles<128, false, RAGGED>(tail, smem, b - n_pers, n_tail, n_tail);
+    }
 }
 
 // ---------------------------------------------------------------------------

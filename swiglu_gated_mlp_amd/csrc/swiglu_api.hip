@@ -213,13 +213,15 @@ hipError_t launch_prefill(const swk::FusedArgs& a, int grid, hipStream_t s) {
     return hipLaunchKernel(fn, dim3(grid), dim3(64 * WM * WN), kargs, 0, s);
 }
 
+// `total` work items (tiles, or tile x K split) on `grid` <= total workgroups;
+// each workgroup takes items b, b + grid, ...
 template <int BM, bool SPLIT>
-hipError_t launch_stream(const swk::FusedArgs& a, int grid, hipStream_t s) {
+hipError_t launch_stream(const swk::FusedArgs& a, int total, int grid, hipStream_t s) {
     const void* fn = (a.K % swk::BK) != 0
                          ? reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, true>)
                          : reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, false>);
     swk::FusedArgs args = a;
-    void* kargs[] = {&args};
+    void* kargs[] = {&args, &total};
     return hipLaunchKernel(fn, dim3(grid), dim3(256), kargs, 0, s);
 }
 
@@ -257,10 +259,11 @@ hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) 
             return split ? launch_tile<64, 128, 2, 2, true, true, true>(a, grid, s)
                          : launch_tile<64, 128, 2, 2, true, true, false>(a, grid, s);
         case 128:
-            return split ? launch_stream<128, true>(a, grid, s) : launch_stream<128, false>(a, grid, s);
+            return split ? launch_stream<128, true>(a, grid, grid, s) : launch_stream<128, false>(a, grid, grid, s);
         default: {
-            if (split) return launch_stream<256, true>(a, grid, s);
-            if (p.tail_ntiles == 0) return launch_stream<256, false>(a, grid, s);
+            if (split) return launch_stream<256, true>(a, grid, grid, s);
+            // one workgroup per CU works through the 256-row tiles
+            if (p.tail_ntiles == 0) return launch_stream<256, false>(a, grid, std::min(grid, p.cus), s);
             // one launch: the 256-row tiles of the first column tiles, then
             // the last tail_ntiles column tiles as 128-row tiles
             swk::FusedArgs big = a, tail = a;
@@ -269,11 +272,12 @@ hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) 
             tail.tiles_n = p.tail_ntiles;
             tail.n_tile0 = big.tiles_n;
             int n_big = big.tiles_m * big.tiles_n;
-            const int grid_all = n_big + tail.tiles_m * tail.tiles_n;
+            int n_pers = std::min(n_big, p.cus);
+            const int grid_all = n_pers + tail.tiles_m * tail.tiles_n;
             const void* fn = (a.K % swk::BK) != 0
                                  ? reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<true>)
                                  : reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<false>);
-            void* kargs[] = {&big, &tail, &n_big};
+            void* kargs[] = {&big, &tail, &n_pers, &n_big};
             return hipLaunchKernel(fn, dim3(grid_all), dim3(256), kargs, 0, s);
         }
     }
