@@ -95,8 +95,13 @@ __device__ __forceinline__ unsigned bf16_bits(float x) {
     return (unsigned)__builtin_bit_cast(unsigned short, h);
 }
 
+// Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32;
+// `lo` lands in the low half.
 __device__ __forceinline__ unsigned pack2(float lo, float hi) {
-    return bf16_bits(lo) | (bf16_bits(hi) << 16);
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+    const h2 h = __builtin_convertvector((f2){lo, hi}, h2);
+    return __builtin_bit_cast(unsigned, h);
 }
 
 // Map the hardware workgroup id to a logical id such that XCD x (which gets
@@ -133,6 +138,9 @@ struct FusedArgs {
     int splits;           // number of K splits (1 = none)
     int kb_per_split;     // K blocks (of 64) per split
     int KB;               // ceil(K / 64)
+    int panels;           // > 0: panel schedule over this many 32-column weight panels
+                          // (streaming kernel, one row tile): work item w takes
+                          // panels [w*panels/total, (w+1)*panels/total), one per wave
 };
 
 // ---------------------------------------------------------------------------
@@ -439,15 +447,20 @@ __global__ __launch_bounds__(64 * WM * WN) void fused_tile_kernel(FusedArgs p) {
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-// 16-byte global store that the compiler does not track: the streaming
-// kernel leaves its Y stores in flight across the next tile's K loop, and a
-// tracked store would make the compiler's own waits for later register
-// loads conservative (it treats loads and stores as completing in any order
-// relative to each other).  The kernel's explicit waits only ever rely on
-// loads completing in order among themselves, which extra stores in the
-// count cannot break.  The s_nop covers the store-data read of the VGPRs.
+// 16-byte global store of an output tile, written through: device scope
+// (sc1) with the non-temporal hint (nt), so the line goes out to memory now
+// instead of sitting dirty in this XCD's L2 until the end-of-kernel
+// writeback, and the output does not displace operand lines (measured: the
+// 0.5B prefill launch ends about 6 us sooner).
+// The compiler does not track the store: the streaming kernel leaves its Y
+// stores in flight across the next tile's K loop, and a tracked store would
+// make the compiler's own waits for later register loads conservative (it
+// treats loads and stores as completing in any order relative to each
+// other).  The kernel's explicit waits only ever rely on loads completing in
+// order among themselves, which extra stores in the count cannot break.  The
+// s_nop covers the store-data read of the VGPRs.
 __device__ __forceinline__ void store16_untracked(uint16_t* gdst, u32x4 v) {
-    asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" ::"v"(gdst), "v"(v) : "memory");
+    asm volatile("global_store_dwordx4 %0, %1, off nt sc1\n\ts_nop 1" ::"v"(gdst), "v"(v) : "memory");
 }
 
 __device__ __forceinline__ void dma16(const uint16_t* gsrc, uint16_t* lds_dst) {
@@ -867,7 +880,7 @@ constexpr int stream_smem_elems() {
 // next tile's first two stages are issued before the epilogue of the
 // current one, and its Y stores are left in flight while the next tile's K
 // loop starts.
-template <int BM, bool SPLIT, bool RAGGED>
+template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false>
 __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_t* smem, int first, int stride,
                                                      int total) {
     constexpr int NW = 4;                       // waves, 32 output columns each
@@ -888,11 +901,31 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
     const int M = p.M, K = p.K, N = p.N, KB = p.KB;
     const int S = SPLIT ? p.splits : 1;
 
-    // work item w -> output tile (m0, n0) and K blocks [kb_first, kb_first + ns)
+    // work item w -> output tile (m0, n0), K blocks [kb_first, kb_first + ns)
+    // and the number np of waves with weights (32-column panels from n0 on)
     struct Item {
-        int m0, n0, kb_first, ns, split;
+        int m0, n0, kb_first, ns, split, np;
     };
     auto item_of = [&](int w) {
+        if constexpr (PANELS) {
+            // Panel schedule: when the row tile has fewer 128-column tiles
+            // than there are CUs, the 32-column panels (one wave's share of a
+            // tile) are spread evenly over `total` workgroups, so every CU
+            // streams weights: adjacent panels, possibly from two packed
+            // tiles, all sharing the one activation tile in LDS.
+            {
+                const int q0 = (int)((long long)w * p.panels / total);
+                const int q1 = (int)((long long)(w + 1) * p.panels / total);
+                Item it;
+                it.m0 = 0;
+                it.n0 = q0 * 32;
+                it.kb_first = 0;
+                it.ns = KB;
+                it.split = 0;
+                it.np = q1 - q0;
+                return it;
+            }
+        }
         const int logical = xcd_remap(w, total);
         const int tile = SPLIT ? logical / S : logical;
         const int split = SPLIT ? logical - tile * S : 0;
@@ -907,6 +940,7 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
         it.kb_first = SPLIT ? split * p.kb_per_split : 0;
         it.ns = (SPLIT ? min(KB, it.kb_first + p.kb_per_split) : KB) - it.kb_first;   // >= 1
         it.split = split;
+        it.np = 4;
         return it;
     };
 
@@ -919,16 +953,18 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
     // row = (wave*A_INS + i)*8 + l/8, i.e. chunk_x ^ ((wave*A_INS + i) & 7)
     // with chunk_x = ((l & 7) ^ (l >> 3)) & 7 (only the ragged K stage needs it)
     int chunk_x = 0;
-    // weights: lane l needs column wave*32 + (l & 31) and the 8 k at chunk
-    // c = 2kk + (l >> 5) of each 64-deep block, i.e. packed group
-    // t*8 + wave*2 + ((l >> 4) & 1), half kk >> 1, fragment lane
+    // weights: the wave's 32 columns are panel wq = n0/32 + wave, i.e.
+    // columns 32(wq & 3) + (l & 31) of packed tile wq >> 2; lane l needs the
+    // 8 k at chunk c = 2kk + (l >> 5) of each 64-deep block, i.e. packed
+    // group t*8 + (wq & 3)*2 + ((l >> 4) & 1), half kk >> 1, fragment lane
     // (2(kk & 1) + (l >> 5))*16 + (l & 15): a lane byte offset plus a
     // constant per (t, kk)
     uint32_t w_off = 0;
     const char* w_tile = nullptr;
     // the item whose stages the loads below fetch (ld_ns = 0: none, every
-    // load reads the zero chunk)
-    int ld_kb_first = 0, ld_ns = 0;
+    // load reads the zero chunk; ld_ns_w: the same for this wave's weights,
+    // 0 for a wave without a panel)
+    int ld_kb_first = 0, ld_ns = 0, ld_ns_w = 0;
     auto load_item = [&](const Item& it, bool valid) {
         // lane index behind an opaque copy: recomputed per item rather than
         // hoisted out of the tile loop (see the epilogue)
@@ -941,10 +977,12 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
             a_off[i] = (uint32_t)(((size_t)min(it.m0 + r, M - 1) * K + 8 * c) * 2);
         }
         chunk_x = ((ll & 7) ^ (ll >> 3)) & 7;
-        w_off = (uint32_t)(((wave * 2 + ((ll >> 4) & 1)) * 1024 + (ll >> 5) * 128 + (ll & 15) * 8) * 2);
-        w_tile = reinterpret_cast<const char*>(p.W1) + (size_t)(it.n0 / PACK_BN) * KB * (PACK_ROWS * PACK_BK * 2);
+        const int wq = it.n0 / 32 + wave;
+        w_off = (uint32_t)((((wq & 3) * 2 + ((ll >> 4) & 1)) * 1024 + (ll >> 5) * 128 + (ll & 15) * 8) * 2);
+        w_tile = reinterpret_cast<const char*>(p.W1) + (size_t)(wq >> 2) * KB * (PACK_ROWS * PACK_BK * 2);
         ld_kb_first = it.kb_first;
         ld_ns = valid ? it.ns : 0;
+        ld_ns_w = (!PANELS || wave < it.np) ? ld_ns : 0;
     };
     // fragment reads: lane l reads row i*32 + (l & 31), logical chunk
     // 2kk + (l >> 5).  swz(i*32 + r) = swz(r) ^ 4(i & 1) for r < 32, so the
@@ -1004,7 +1042,7 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
     // into register set SET
     auto issue_one = [&](int j, int ls, int buf, auto setc) {
         constexpr int SET = decltype(setc)::value;
-        const bool valid = ls < ld_ns;
+        const bool valid = ls < (j < A_INS ? ld_ns : ld_ns_w);
         const uint32_t keep = valid ? 0xffffffffu : 0u;
         if (j < A_INS) {
             const int k0 = (ld_kb_first + ls) * BK;
@@ -1204,6 +1242,7 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
             const int r0 = wave * (BM / 4) + (el >> 4);
             const int c = el & 15;
             const int n = cur.n0 + 8 * c;
+            const int n_lim = PANELS ? min(N, cur.n0 + 32 * cur.np) : N;
             const int rows_left = M - cur.m0 - r0;   // rows r0 + 4t < M - m0
             uint16_t* yp = p.Y + (size_t)(cur.m0 + r0) * N + n;
 #pragma unroll
@@ -1211,7 +1250,7 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
                 const int r = r0 + t * 4;
                 u32x4 v = *reinterpret_cast<const u32x4*>(sY + r * PACK_BN + 8 * (c ^ (r & 15)));
                 if ((r >> 4) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-                if (4 * t < rows_left && n < N) store16_untracked(yp + (size_t)t * 4 * N, v);
+                if (4 * t < rows_left && n < n_lim) store16_untracked(yp + (size_t)t * 4 * N, v);
             }
         }
         if (!more) break;
@@ -1234,10 +1273,11 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
             for (int kk = 0; kk < 4; ++kk) asm volatile("" ::"v"(wf[q][t][kk]));
 }
 
-template <int BM, bool SPLIT, bool RAGGED>
+template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false>
 __global__ __launch_bounds__(256) void stream_prefill_kernel(FusedArgs p, int total) {
+    static_assert(!PANELS || (BM == 128 && !SPLIT), "panel schedule: one 128-row tile, data-parallel");
     __shared__ __attribute__((aligned(16))) uint16_t smem[stream_smem_elems<BM>()];
-    stream_prefill_tiles<BM, SPLIT, RAGGED>(p, smem, blockIdx.x, gridDim.x, total);
+    stream_prefill_tiles<BM, SPLIT, RAGGED, PANELS>(p, smem, blockIdx.x, gridDim.x, total);
 }
 
 // The 256-row tiles and the 128-row tail column tiles in one launch: blocks

@@ -119,6 +119,7 @@ struct Plan {
     TileCfg t;
     int tiles_m, tiles_n, tiles;
     int tail_ntiles;   // data-parallel 256-row tiles: last column tiles run as 128x128 tiles
+    int panels;        // data-parallel, one 128-row tile: 32-column panels spread over the CUs
     int splits, kb_per_split, KB;
     int variant;   // resolved: DATA_PARALLEL, SPLIT_K or DECODE
     int decode_mt; // DECODE: 16-token tiles per workgroup
@@ -169,6 +170,12 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int variant, int cus) {
             if (nt < p.tiles_n) p.tail_ntiles = nt;
         }
     }
+    // One row of 128-row tiles that leaves CUs idle: the 32-column weight
+    // panels (four per tile) are spread evenly over the CUs instead, so every
+    // CU streams weights.
+    p.panels = 0;
+    if (v == SWIGLU_VARIANT_DATA_PARALLEL && p.t.BM == 128 && p.tiles_m == 1 && p.tiles_n < cus)
+        p.panels = 4 * p.tiles_n;
     if (v == SWIGLU_VARIANT_SPLIT_K && p.tiles <= kMaxSplitTiles) {
         // about kSplitWavesPerCu workgroups per CU, at least two K blocks per split
         int s = (int)ceil_div((int64_t)kSplitWavesPerCu * cus, p.tiles);
@@ -215,11 +222,11 @@ hipError_t launch_prefill(const swk::FusedArgs& a, int grid, hipStream_t s) {
 
 // `total` work items (tiles, or tile x K split) on `grid` <= total workgroups;
 // each workgroup takes items b, b + grid, ...
-template <int BM, bool SPLIT>
+template <int BM, bool SPLIT, bool PANELS = false>
 hipError_t launch_stream(const swk::FusedArgs& a, int total, int grid, hipStream_t s) {
     const void* fn = (a.K % swk::BK) != 0
-                         ? reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, true>)
-                         : reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, false>);
+                         ? reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, true, PANELS>)
+                         : reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, false, PANELS>);
     swk::FusedArgs args = a;
     void* kargs[] = {&args, &total};
     return hipLaunchKernel(fn, dim3(grid), dim3(256), kargs, 0, s);
@@ -259,7 +266,14 @@ hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) 
             return split ? launch_tile<64, 128, 2, 2, true, true, true>(a, grid, s)
                          : launch_tile<64, 128, 2, 2, true, true, false>(a, grid, s);
         case 128:
-            return split ? launch_stream<128, true>(a, grid, grid, s) : launch_stream<128, false>(a, grid, grid, s);
+            if (split) return launch_stream<128, true>(a, grid, grid, s);
+            if (p.panels > 0) {
+                swk::FusedArgs pa = a;
+                pa.panels = p.panels;
+                const int g = std::min(p.panels, p.cus);
+                return launch_stream<128, false, true>(pa, g, g, s);
+            }
+            return launch_stream<128, false>(a, grid, grid, s);
         default: {
             if (split) return launch_stream<256, true>(a, grid, grid, s);
             // one workgroup per CU works through the 256-row tiles
@@ -435,9 +449,9 @@ swiglu_status swiglu_fused_packed(const swiglu_bf16* A, const swiglu_bf16* Wp, s
     a.splits = p.splits; a.kb_per_split = p.kb_per_split; a.KB = p.KB;
     if (need > 0) a.part = reinterpret_cast<float*>(workspace);
     if (log_enabled())
-        std::fprintf(stderr, "[swiglu] fused_packed M=%lld K=%lld N=%lld variant=%d tile=%dx%d tiles=%d splits=%d tail_ntiles=%d\n",
+        std::fprintf(stderr, "[swiglu] fused_packed M=%lld K=%lld N=%lld variant=%d tile=%dx%d tiles=%d splits=%d tail_ntiles=%d panels=%d\n",
                      (long long)M, (long long)K, (long long)N, p.variant, p.t.BM, p.t.BN, p.tiles, p.splits,
-                     p.tail_ntiles);
+                     p.tail_ntiles, p.panels);
     hipError_t e = launch_packed(a, p, (hipStream_t)stream);
     if (e == hipSuccess && p.splits > 1) {
         const int cus = std::max(1, cu_count_now());

@@ -284,6 +284,30 @@ def test_decode_configurations(dev, M, K, N):
     check_close(gpu_bits(Y), oracle.swiglu(A, W1, W2), "decode %s" % ((M, K, N),))
 
 
+@pytest.mark.parametrize("M,K,N", [
+    (100, 256, 8192),     # 256 panels: one per workgroup
+    (72, 64, 12040),      # one or two panels per workgroup; the last panel partly past N
+    (128, 200, 24576),    # three panels per workgroup, across packed-tile borders; ragged K
+    (96, 136, 30000),     # three or four panels; a partial last packed tile
+])
+def test_panel_schedule(dev, M, K, N):
+    """One row of 128-row tiles with fewer column tiles than CUs: the
+    32-column weight panels are spread over the workgroups (data-parallel and
+    AUTO), all elements against the oracle and bitwise against the row-major
+    entry point (same MFMA chain per element)."""
+    A, W1, W2 = inputs.gaussian_case(M, K, N, seed=M + 3 * K + N)
+    Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
+    Wp = sw.swiglu_pack_weights(W1d, W2d)
+    say("[panels] M=%d K=%d N=%d" % (M, K, N))
+    ys = {name: gpu_bits(sw.swiglu_fused_packed(Ad, Wp, N, variant=v)) for name, v in (("dp", DP), ("auto", AUTO))}
+    yf = gpu_bits(sw.swiglu_fused(Ad, W1d, W2d))
+    torch.cuda.synchronize()
+    ref = oracle.swiglu(A, W1, W2)
+    for name, y in ys.items():
+        check_close(y, ref, "panels/%s %s" % (name, (M, K, N)))
+        assert np.array_equal(y, yf), "panels/%s != fused bitwise" % name
+
+
 def test_split_workspace_reused_across_shapes(dev):
     """One workspace serves split-K calls of different shapes in a row, and
     its earlier contents (partials of another shape, or garbage) never leak
