@@ -7,8 +7,12 @@ timed region, as a model-load step.
 
 Prints ONE JSON line (metric, value, ..., roofline, cpu_baseline).
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--m M]
+    python bench.py [--steps K] [--warmup W] [--prewarm SECONDS] [--workload NAME] [--m M]
                     [--variant auto|data_parallel|split_k] [--no-cpu] [--all]
+
+The timed region is exactly K steps after W warm-up steps; before those, the
+same calls run untimed for --prewarm seconds so the GPU has left its idle
+clock (a 75 us step would otherwise be timed partly at the idle clock).
 """
 from __future__ import annotations
 
@@ -59,11 +63,21 @@ def rotation_count(M, K, N):
     return max(1, math.ceil(2 * MALL_BYTES / fused_bytes(M, K, N)))
 
 
-def time_gpu(fn_list, steps, warmup, stream):
+def time_gpu(fn_list, steps, warmup, stream, prewarm_s=0.0):
     """Run fn_list[i % R]() for warmup + steps; time the steps with HIP events
-    recorded on the launch stream.  Returns total seconds for `steps`."""
+    recorded on the launch stream.  Returns total seconds for `steps`.
+    Before the warm-up steps the calls run untimed for prewarm_s seconds of
+    wall time: a GPU coming out of idle needs tens of milliseconds to reach
+    its sustained clock, longer than a few dozen short steps take."""
     import torch
     R = len(fn_list)
+    t_end = time.perf_counter() + prewarm_s
+    i = 0
+    while time.perf_counter() < t_end:
+        for _ in range(16):
+            fn_list[i % R]()
+            i += 1
+        torch.cuda.synchronize()
     for i in range(warmup):
         fn_list[i % R]()
     torch.cuda.synchronize()
@@ -103,7 +117,8 @@ def measured_traffic(workload_label):
 
 def cpu_baseline(w, M, target_s=12.0):
     """Time the CPU oracle (as it stands) on the first rows of the same workload:
-    a few rows first to estimate the rate, then enough rows for ~target_s."""
+    a few rows first to estimate the rate, then enough rows for ~target_s (the
+    whole workload, repeated, when it takes less)."""
     import oracle
     from swiglu_gated_mlp_amd import inputs
     threads = min(len(os.sched_getaffinity(0)), 16)
@@ -118,18 +133,24 @@ def cpu_baseline(w, M, target_s=12.0):
     m = max(threads, (m // threads) * threads) if m >= threads else m
     m = min(m, M)
     t0 = time.perf_counter()
-    oracle.swiglu(Ab[:m], W1b, W2b)
-    dt = time.perf_counter() - t0
+    reps = 0
+    while True:
+        oracle.swiglu(Ab[:m], W1b, W2b)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 0.8 * target_s or m < M:
+            break
     return {
-        "value": round(flops(m, w.K, w.N) / dt / 1e12, 6),
+        "value": round(reps * flops(m, w.K, w.N) / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(oracle.max_threads()),
         "kind": "oracle",
-        "sample": "first %d of %d rows of A, all %d columns (K=%d); %.1f s" % (m, M, w.N, w.K, dt),
+        "sample": "first %d of %d rows of A, all %d columns (K=%d), %d run(s); %.1f s"
+                  % (m, M, w.N, w.K, reps, dt),
     }
 
 
-def bench_point(w, M, steps, warmup, variant, stream):
+def bench_point(w, M, steps, warmup, variant, stream, prewarm_s=0.0):
     import torch
     import swiglu_gated_mlp_amd as sw
     from swiglu_gated_mlp_amd import inputs
@@ -150,7 +171,7 @@ def bench_point(w, M, steps, warmup, variant, stream):
     v = sw.VARIANTS[variant]
     fns = [(lambda s=s: sw.swiglu_fused_packed(s[0], s[1], N, Y=s[2], workspace=s[3], variant=v))
            for s in sets]
-    sec = time_gpu(fns, steps, warmup, stream)
+    sec = time_gpu(fns, steps, warmup, stream, prewarm_s)
     per = sec / steps
     return {
         "M": M, "K": K, "N": N, "rotation": R, "seconds": sec, "per_launch_s": per,
@@ -160,7 +181,7 @@ def bench_point(w, M, steps, warmup, variant, stream):
     }
 
 
-def bench_unfused(w, M, steps, warmup, stream):
+def bench_unfused(w, M, steps, warmup, stream, prewarm_s=0.0):
     import torch
     import swiglu_gated_mlp_amd as sw
     from swiglu_gated_mlp_amd import inputs
@@ -172,7 +193,7 @@ def bench_unfused(w, M, steps, warmup, stream):
     U = torch.empty_like(G)
     Y = torch.empty_like(G)
     fn = lambda: sw.swiglu_unfused(Ad, W1d, W2d, G, U, Y)  # noqa: E731
-    sec = time_gpu([fn], steps, warmup, stream)
+    sec = time_gpu([fn], steps, warmup, stream, prewarm_s)
     return sec / steps
 
 
@@ -230,6 +251,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--prewarm", type=float, default=0.5, metavar="SECONDS",
+                    help="untimed calls before the warm-up steps, in seconds of wall time (0 under a profiler)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--m", type=int, default=None, help="token count (default: the workload's largest)")
     ap.add_argument("--variant", default="auto", choices=["auto", "data_parallel", "split_k"])
@@ -266,7 +289,7 @@ def main():
     w = inputs.BY_NAME[args.workload]
     M = args.m or w.m_max
 
-    res = bench_point(w, M, args.steps, args.warmup, args.variant, stream)
+    res = bench_point(w, M, args.steps, args.warmup, args.variant, stream, args.prewarm)
     per = res["per_launch_s"]
     bound = bound_of(M, w.K, w.N)
     if bound == "mfma":
@@ -278,8 +301,8 @@ def main():
     if args.all:
         for ww in inputs.WORKLOADS:
             for mm in ww.ms:
-                r = bench_point(ww, mm, max(10, args.steps // 2), 5, args.variant, stream)
-                tu = bench_unfused(ww, mm, max(5, args.steps // 4), 3, stream)
+                r = bench_point(ww, mm, max(10, args.steps // 2), 5, args.variant, stream, args.prewarm)
+                tu = bench_unfused(ww, mm, max(5, args.steps // 4), 3, stream, args.prewarm)
                 b = bound_of(mm, ww.K, ww.N)
                 frac = r["tflops"] / MFMA_BF16_PEAK_TFLOPS if b == "mfma" else r["gbs"] / HBM_PEAK_GBS
                 line = {"workload": ww.name, "M": mm, "K": ww.K, "N": ww.N, "bound": b,
