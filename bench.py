@@ -197,6 +197,45 @@ def bench_unfused(w, M, steps, warmup, stream, prewarm_s=0.0):
     return sec / steps
 
 
+def bench_mlp(w, M, steps, warmup, stream, prewarm_s=0.0):
+    """The gated MLP block (SwiGLU product, then the down projection Y @ W3)
+    fused and unfused, and the down projection alone, each over rotated
+    input sets; returns per-call seconds and the SwiGLU shares of MLP time."""
+    import torch
+    import swiglu_gated_mlp_amd as sw
+    from swiglu_gated_mlp_amd import inputs
+    dev = torch.device("cuda:0")
+    K, N = w.K, w.N
+    A, W1, W2 = inputs.workload_tensors(w, M)
+    W3 = inputs.down_weight(w)
+    R = max(1, math.ceil(2 * MALL_BYTES / (fused_bytes(M, K, N) + 2 * (N * K + M * K))))
+    mk = lambda r, c: torch.empty((r, c), dtype=torch.bfloat16, device=dev)  # noqa: E731
+    sets = []
+    for _ in range(R):
+        W1d, W2d = W1.to(dev), W2.to(dev)
+        sets.append(dict(A=A.to(dev), W1=W1d, W2=W2d, Wp=sw.swiglu_pack_weights(W1d, W2d), W3=W3.to(dev),
+                         G=mk(M, N), U=mk(M, N), Y=mk(M, N), Z=mk(M, K), ws=sw.Workspace(dev)))
+    torch.cuda.synchronize()
+    fused = [(lambda d=d: sw.swiglu_mlp_packed(d["A"], d["Wp"], d["W3"], N, Y=d["Y"], Z=d["Z"],
+                                               workspace=d["ws"])) for d in sets]
+    unfused = [(lambda d=d: sw.swiglu_mlp_unfused(d["A"], d["W1"], d["W2"], d["W3"], d["G"], d["U"],
+                                                  d["Y"], d["Z"])) for d in sets]
+    down = [(lambda d=d: sw.swiglu_mlp_down(d["Y"], d["W3"], d["Z"])) for d in sets]
+    tf = time_gpu(fused, steps, warmup, stream, prewarm_s) / steps
+    tu = time_gpu(unfused, steps, warmup, stream, prewarm_s) / steps
+    td = time_gpu(down, steps, warmup, stream, prewarm_s) / steps
+    # removed_by_fusion: the share of the unfused MLP's time that fusion takes
+    # away (materialised Gate/Up, the separate activation pass, and the
+    # difference between the two SwiGLU kernels); gateup_share_*: the share of
+    # the gate/up projections plus activation in each MLP (the rest is the
+    # down projection)
+    return {"workload": w.name, "M": M, "K": K, "N": N, "rotation": R,
+            "mlp_fused_us": round(tf * 1e6, 2), "mlp_unfused_us": round(tu * 1e6, 2),
+            "down_proj_us": round(td * 1e6, 2), "mlp_speedup": round(tu / tf, 3),
+            "removed_by_fusion": round((tu - tf) / tu, 4),
+            "gateup_share_unfused": round((tu - td) / tu, 4), "gateup_share_fused": round((tf - td) / tf, 4)}
+
+
 def ceilings(stream):
     """What the device sustains: MFMA-only loop, streaming read, and the vendor
     library's bf16 GEMM on the same [M,K]x[K,2N] shapes (context only)."""
@@ -257,6 +296,9 @@ def main():
     ap.add_argument("--m", type=int, default=None, help="token count (default: the workload's largest)")
     ap.add_argument("--variant", default="auto", choices=["auto", "data_parallel", "split_k"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--mlp", action="store_true",
+                    help="also time the whole gated MLP block (with the down projection), fused and "
+                         "unfused, at the workload point (with --all: at every point) (stderr)")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload point and the unfused pipeline (stderr)")
     ap.add_argument("--ceilings", action="store_true",
@@ -313,6 +355,11 @@ def main():
                         "resolved_variant": r["resolved_variant"]}
                 log("POINT " + json.dumps(line))
                 extra.setdefault("points", []).append(line)
+                if args.mlp:
+                    log("MLP " + json.dumps(bench_mlp(ww, mm, max(10, args.steps // 2), 5, stream,
+                                                      args.prewarm)))
+    elif args.mlp:
+        log("MLP " + json.dumps(bench_mlp(w, M, args.steps, args.warmup, stream, args.prewarm)))
 
     cpu = None
     if not args.no_cpu:

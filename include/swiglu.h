@@ -190,6 +190,47 @@ swiglu_status swiglu_unfused(const swiglu_bf16 *A, const swiglu_bf16 *W1,
                              swiglu_bf16 *U_scratch, swiglu_bf16 *Y, int64_t M,
                              int64_t K, int64_t N, void *stream);
 
+/* ------------------------------------------------------------------------
+ * The whole gated MLP block: the SwiGLU product followed by the down
+ * projection back to the model width, Z[M,K] = bf16_RNE(Y[M,N] x W3[N,K])
+ * with fp32 accumulation, W3 row-major.  The pages give SwiGLU's cost as a
+ * share of MLP execution time ([Summary: Problem Statement], 9-37 %; the
+ * speedup falling with model size in [Summary: Results]); these two entry
+ * points are that MLP, fused and unfused, so the share can be measured.
+ *
+ * The down projection is a plain GEMM outside the fused product and runs on
+ * rocBLAS (bf16 in and out, fp32 compute; one handle per device, created on
+ * first use and kept for the process), in both entry points.
+ *
+ * swiglu_mlp_packed:  Y = swiglu_fused_packed(A, Wp, ...), then Z = gemm(Y,
+ *   W3).  Y is a caller-owned [M,N] bf16 device buffer and holds the SwiGLU
+ *   product on return; workspace, workspace_bytes and variant are those of
+ *   swiglu_fused_packed.  Z must not overlap A, Wp, W3, Y or the workspace;
+ *   Y must not overlap W3 (nor the inputs, as in swiglu_fused_packed).
+ * swiglu_mlp_unfused: Y = swiglu_unfused(A, W1, W2, G, U, ...), then
+ *   Z = gemm(Y, W3); Z must not overlap any other buffer, and no scratch may
+ *   overlap W3.
+ * swiglu_mlp_down:    the down projection alone, Z = gemm(Y, W3) (the step
+ *   both entry points above end with); Z must not overlap Y or W3.
+ * Both: K and N multiples of 8, pointers 16-byte aligned; M == 0 returns
+ * SWIGLU_OK without a launch; the validation codes return before any launch;
+ * a rocBLAS failure returns SWIGLU_ERR_HIP; work is enqueued on `stream`
+ * with no synchronisation.
+ * ---------------------------------------------------------------------- */
+swiglu_status swiglu_mlp_packed(const swiglu_bf16 *A, const swiglu_bf16 *Wp,
+                                const swiglu_bf16 *W3, swiglu_bf16 *Y,
+                                swiglu_bf16 *Z, int64_t M, int64_t K, int64_t N,
+                                void *workspace, size_t workspace_bytes,
+                                int variant, void *stream);
+swiglu_status swiglu_mlp_down(const swiglu_bf16 *Y, const swiglu_bf16 *W3,
+                             swiglu_bf16 *Z, int64_t M, int64_t K, int64_t N,
+                             void *stream);
+swiglu_status swiglu_mlp_unfused(const swiglu_bf16 *A, const swiglu_bf16 *W1,
+                                 const swiglu_bf16 *W2, const swiglu_bf16 *W3,
+                                 swiglu_bf16 *G_scratch, swiglu_bf16 *U_scratch,
+                                 swiglu_bf16 *Y, swiglu_bf16 *Z, int64_t M,
+                                 int64_t K, int64_t N, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,10 @@ Inference" as summarised on gist.science ("Summary"):
 * ``silu``        -- SiLU(x) = x / (1 + e^-x), the Swish applied to Gate;
   Summary, "Methodology", Kernel-1.
 * ``bf16_rne``    -- rounding of the fp32 result to the bf16 output type.
+* ``mlp``         -- the gated MLP block the pages' "share of MLP time" refers
+  to: the bf16 SwiGLU product Y, then the down projection Z = bf16(Y x W3) with
+  fp32 accumulation (Summary, "Problem Statement"; the pages do not spell the
+  down projection out, this is the standard gated-MLP reading).
 
 Pins: every function here is checked by ``tests/test_oracle.py`` against fp64
 brute force with a closed-form error bound, exact integer regimes, closed
@@ -188,6 +192,12 @@ class Oracle:
         self.lib.oracle_gemm_bf16(_p16(A), _p16(W), M, K, N, _p16(C))
         return C
 
+    def mlp(self, A, W1, W2, W3):
+        """The gated MLP block: Y = swiglu(A, W1, W2) (bf16), then the down
+        projection Z = gemm_bf16(Y, W3), W3 [N, K'].  Returns (Y, Z)."""
+        Y = self.swiglu(A, W1, W2)
+        return Y, self.gemm_bf16(Y, W3)
+
     def unfused(self, A, W1, W2):
         """The unfused pipeline: returns (Gate_bf16, Up_bf16, Y)."""
         A, W1, W2 = _u16(A), _u16(W1), _u16(W2)
@@ -248,3 +258,7 @@ def gemm_bf16(A, W) -> np.ndarray:
 
 def unfused(A, W1, W2):
     return default().unfused(A, W1, W2)
+
+
+def mlp(A, W1, W2, W3):
+    return default().mlp(A, W1, W2, W3)

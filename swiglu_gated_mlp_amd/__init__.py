@@ -48,6 +48,10 @@ SIGNATURES = {
     "swiglu_gemm_bf16": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "swiglu_silu_mul": ([_P, _P, _P, _I64, _P], ctypes.c_int),
     "swiglu_unfused": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "swiglu_mlp_packed": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, ctypes.c_int, _P],
+                          ctypes.c_int),
+    "swiglu_mlp_unfused": ([_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "swiglu_mlp_down": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     # include/swiglu_probe.h (diagnostic ceilings)
     "swiglu_probe_mfma": ([_P, ctypes.c_int, ctypes.c_int, _P], ctypes.c_int),
     "swiglu_probe_read": ([_P, ctypes.c_size_t, _P, ctypes.c_int, _P], ctypes.c_int),
@@ -281,6 +285,64 @@ def swiglu_unfused(A: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor, G: torch
                               _stream(stream))
     _check("swiglu_unfused", st)
     return G, U, Y
+
+
+def swiglu_mlp_packed(A: torch.Tensor, Wp: torch.Tensor, W3: torch.Tensor, N: int,
+                      Y: torch.Tensor | None = None, Z: torch.Tensor | None = None,
+                      workspace: torch.Tensor | Workspace | None = None, variant: int = VARIANT_AUTO,
+                      stream=None):
+    """The gated MLP block on packed weights: Y = SiLU(A W1) * (A W2), then
+    Z = Y @ W3 (W3 [N,K] row-major, the down projection).  Returns (Y, Z)."""
+    M, K = A.shape
+    if isinstance(variant, str):
+        variant = VARIANTS[variant]
+    s = _stream(stream)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=A.device) if Y is None else Y
+    Z = torch.empty((M, K), dtype=torch.bfloat16, device=A.device) if Z is None else Z
+    need = swiglu_workspace_bytes(M, K, N, variant)
+    if isinstance(workspace, Workspace):
+        ws = workspace.get(need)
+    elif workspace is None:
+        ws = _workspace_for(A.device, s).get(need)
+    else:
+        ws = workspace
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().swiglu_mlp_packed(_dev_bf16(A, "A"), _dev_bf16(Wp, "Wp"), _dev_bf16(W3, "W3"),
+                                 _dev_bf16(Y, "Y"), _dev_bf16(Z, "Z"), M, K, N, _ptr(ws), ws_bytes,
+                                 int(variant), s)
+    _check("swiglu_mlp_packed", st)
+    return Y, Z
+
+
+def swiglu_mlp_down(Y: torch.Tensor, W3: torch.Tensor, Z: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """The MLP block's down projection alone: Z[M,K] = Y[M,N] @ W3[N,K]."""
+    M, N = Y.shape
+    K = W3.shape[1]
+    Z = torch.empty((M, K), dtype=torch.bfloat16, device=Y.device) if Z is None else Z
+    st = lib().swiglu_mlp_down(_dev_bf16(Y, "Y"), _dev_bf16(W3, "W3"), _dev_bf16(Z, "Z"), M, K, N,
+                               _stream(stream))
+    _check("swiglu_mlp_down", st)
+    return Z
+
+
+def swiglu_mlp_unfused(A: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor, W3: torch.Tensor,
+                       G: torch.Tensor | None = None, U: torch.Tensor | None = None,
+                       Y: torch.Tensor | None = None, Z: torch.Tensor | None = None, stream=None):
+    """The gated MLP block, unfused: G, U through memory, Y = SiLU(G)*U, then
+    Z = Y @ W3.  Returns (Y, Z)."""
+    M, K = A.shape
+    N = W1.shape[1]
+    mk = lambda r, c: torch.empty((r, c), dtype=torch.bfloat16, device=A.device)  # noqa: E731
+    G = mk(M, N) if G is None else G
+    U = mk(M, N) if U is None else U
+    Y = mk(M, N) if Y is None else Y
+    Z = mk(M, K) if Z is None else Z
+    st = lib().swiglu_mlp_unfused(_dev_bf16(A, "A"), _dev_bf16(W1, "W1"), _dev_bf16(W2, "W2"),
+                                  _dev_bf16(W3, "W3"), _dev_bf16(G, "G"), _dev_bf16(U, "U"),
+                                  _dev_bf16(Y, "Y"), _dev_bf16(Z, "Z"), M, K, N, _stream(stream))
+    _check("swiglu_mlp_unfused", st)
+    return Y, Z
 
 
 # ---------------------------------------------------------------------------

@@ -38,10 +38,16 @@ def compile_flags():
     ]
 
 
+def link_flags():
+    # rocBLAS serves the MLP block's down projection (a plain GEMM)
+    lib = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
+    return ["-L", lib, "-Wl,-rpath," + lib, "-lrocblas"]
+
+
 def build(verbose: bool = False) -> str:
     """Compile the library (always recompiles) and return its path."""
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *compile_flags(), "-o", tmp, *SOURCES]
+    cmd = [hipcc(), *compile_flags(), "-o", tmp, *SOURCES, *link_flags()]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

@@ -7,6 +7,7 @@
 #include "swiglu_probe.h"
 
 #include <hip/hip_runtime.h>
+#include <rocblas/rocblas.h>
 
 #include <algorithm>
 #include <atomic>
@@ -536,6 +537,91 @@ swiglu_status swiglu_unfused(const swiglu_bf16* A, const swiglu_bf16* W1, const 
     st = swiglu_gemm_bf16(A, W2, U_scratch, M, K, N, stream);
     if (st != SWIGLU_OK) return st;
     return swiglu_silu_mul(G_scratch, U_scratch, Y, M * N, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Down projection of the MLP block, Z[M,K] = bf16(Y[M,N] x W3[N,K]): a plain
+// GEMM outside the fused product, so it goes to rocBLAS (bf16 in and out,
+// fp32 compute).  Row-major Z = Y W3 is, column-major, Z^T[K,M] = W3^T[K,N]
+// Y^T[N,M] with no transposes.  One handle per device for the process; the
+// stream is set per call under the lock, so calls on different streams do
+// not race on the handle.
+// ---------------------------------------------------------------------------
+swiglu_status down_projection(const swiglu_bf16* Y, const swiglu_bf16* W3, swiglu_bf16* Z, int64_t M,
+                              int64_t N, int64_t K, void* stream) {
+    static std::mutex mu;
+    static rocblas_handle handles[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= 64) return hip_fail(hipErrorInvalidDevice);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!handles[dev] && rocblas_create_handle(&handles[dev]) != rocblas_status_success) {
+        handles[dev] = nullptr;
+        return hip_fail(hipErrorNotInitialized);
+    }
+    rocblas_handle h = handles[dev];
+    if (rocblas_set_stream(h, (hipStream_t)stream) != rocblas_status_success) return hip_fail(hipErrorInvalidHandle);
+    const float alpha = 1.0f, beta = 0.0f;
+    const rocblas_status rs = rocblas_gemm_ex_64(
+        h, rocblas_operation_none, rocblas_operation_none, K, M, N, &alpha, W3, rocblas_datatype_bf16_r, K, Y,
+        rocblas_datatype_bf16_r, N, &beta, Z, rocblas_datatype_bf16_r, K, Z, rocblas_datatype_bf16_r, K,
+        rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+    return rs == rocblas_status_success ? SWIGLU_OK : hip_fail(hipErrorLaunchFailure);
+}
+
+swiglu_status swiglu_mlp_down(const swiglu_bf16* Y, const swiglu_bf16* W3, swiglu_bf16* Z, int64_t M, int64_t K,
+                             int64_t N, void* stream) {
+    swiglu_status st = check_shape(M, K, N);
+    if (st != SWIGLU_OK) return st;
+    if (M == 0) return SWIGLU_OK;
+    if (!Y || !W3 || !Z) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(Y) || !aligned16(W3) || !aligned16(Z)) return SWIGLU_ERR_MISALIGNED;
+    const Range z = range_of(Z, M * K * 2);
+    if (overlap(z, range_of(Y, M * N * 2)) || overlap(z, range_of(W3, N * K * 2))) return SWIGLU_ERR_ALIASING;
+    return down_projection(Y, W3, Z, M, N, K, stream);
+}
+
+swiglu_status swiglu_mlp_packed(const swiglu_bf16* A, const swiglu_bf16* Wp, const swiglu_bf16* W3,
+                                swiglu_bf16* Y, swiglu_bf16* Z, int64_t M, int64_t K, int64_t N,
+                                void* workspace, size_t workspace_bytes, int variant, void* stream) {
+    swiglu_status st = check_shape(M, K, N);
+    if (st != SWIGLU_OK) return st;
+    if (!variant_known(variant)) return SWIGLU_ERR_BAD_VARIANT;
+    if (M == 0) return SWIGLU_OK;
+    if (!A || !Wp || !W3 || !Y || !Z) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(W3) || !aligned16(Z)) return SWIGLU_ERR_MISALIGNED;
+    const Range z = range_of(Z, M * K * 2), w3 = range_of(W3, N * K * 2), y = range_of(Y, M * N * 2);
+    if (overlap(z, range_of(A, M * K * 2)) || overlap(z, range_of(Wp, packed_elems(K, N) * 2)) ||
+        overlap(z, w3) || overlap(z, y) || overlap(y, w3))
+        return SWIGLU_ERR_ALIASING;
+    if (workspace && workspace_bytes > 0 && overlap(z, range_of(workspace, (int64_t)workspace_bytes)))
+        return SWIGLU_ERR_ALIASING;
+    st = swiglu_fused_packed(A, Wp, Y, M, K, N, workspace, workspace_bytes, variant, stream);
+    if (st != SWIGLU_OK) return st;
+    return down_projection(Y, W3, Z, M, N, K, stream);
+}
+
+swiglu_status swiglu_mlp_unfused(const swiglu_bf16* A, const swiglu_bf16* W1, const swiglu_bf16* W2,
+                                 const swiglu_bf16* W3, swiglu_bf16* G_scratch, swiglu_bf16* U_scratch,
+                                 swiglu_bf16* Y, swiglu_bf16* Z, int64_t M, int64_t K, int64_t N,
+                                 void* stream) {
+    swiglu_status st = check_shape(M, K, N);
+    if (st != SWIGLU_OK) return st;
+    if (M == 0) return SWIGLU_OK;
+    if (!A || !W1 || !W2 || !W3 || !G_scratch || !U_scratch || !Y || !Z) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(W3) || !aligned16(Z)) return SWIGLU_ERR_MISALIGNED;
+    const Range z = range_of(Z, M * K * 2), w3 = range_of(W3, N * K * 2);
+    const Range others[7] = {range_of(A, M * K * 2), range_of(W1, K * N * 2), range_of(W2, K * N * 2), w3,
+                             range_of(G_scratch, M * N * 2), range_of(U_scratch, M * N * 2),
+                             range_of(Y, M * N * 2)};
+    for (const Range& r : others)
+        if (overlap(z, r)) return SWIGLU_ERR_ALIASING;
+    for (int i = 4; i < 7; ++i)
+        if (overlap(others[i], w3)) return SWIGLU_ERR_ALIASING;
+    st = swiglu_unfused(A, W1, W2, G_scratch, U_scratch, Y, M, K, N, stream);
+    if (st != SWIGLU_OK) return st;
+    return down_projection(Y, W3, Z, M, N, K, stream);
 }
 
 swiglu_status swiglu_probe_mfma(float* sink, int blocks, int iters, void* stream) {

@@ -38,7 +38,7 @@ class Workload:
 
     def seeds(self) -> Dict[str, int]:
         return {"A": 1000 * self.index + 1, "W1": 1000 * self.index + 2,
-                "W2": 1000 * self.index + 3}
+                "W2": 1000 * self.index + 3, "W3": 1000 * self.index + 4}
 
 
 #: The five workloads, indexed 0..4.
@@ -79,6 +79,11 @@ def workload_tensors(w: Workload, m: int | None = None):
             raise ValueError("m=%d exceeds the workload's largest height %d" % (m, w.m_max))
         A = A[:m].contiguous()
     return A, weight(w.K, w.N, s["W1"]), weight(w.K, w.N, s["W2"])
+
+
+def down_weight(w: Workload) -> torch.Tensor:
+    """W3[N,K] ~ N(0, 1/N): the workload's down projection (CPU bf16)."""
+    return weight(w.N, w.K, w.seeds()["W3"])
 
 
 def gaussian_case(M: int, K: int, N: int, seed: int):

@@ -109,6 +109,43 @@ def test_unfused_errors():
     assert L.swiglu_unfused(A_, W1_, W2_, None, WP_, WS_, 4, 64, 64, None) == NULLP
 
 
+Z_, W3_ = 0x70000000, 0x80000000
+
+
+def test_mlp_errors():
+    L = sw.lib()
+    P = L.swiglu_mlp_packed
+    # shapes, variants and the empty call come first
+    assert P(A_, WP_, W3_, Y_, Z_, 4, 60, 64, None, 0, 0, None) == UNSUP
+    assert P(A_, WP_, W3_, Y_, Z_, 4, 64, 64, None, 0, 9, None) == VARIANT
+    assert P(None, None, None, None, None, 0, 64, 64, None, 0, 0, None) == OK
+    # the down projection's own operands
+    assert P(A_, WP_, None, Y_, Z_, 4, 64, 64, None, 0, 0, None) == NULLP
+    assert P(A_, WP_, W3_, Y_, None, 4, 64, 64, None, 0, 0, None) == NULLP
+    assert P(A_, WP_, W3_ + 8, Y_, Z_, 4, 64, 64, None, 0, 0, None) == MISAL
+    assert P(A_, WP_, W3_, Y_, Z_ + 2, 4, 64, 64, None, 0, 0, None) == MISAL
+    # Z [4, 64] overlapping A, W3 or Y; Y overlapping W3
+    assert P(A_, WP_, W3_, Y_, A_ + 256, 4, 64, 64, None, 0, 0, None) == ALIAS
+    assert P(A_, WP_, W3_, Y_, W3_ + 16, 4, 64, 64, None, 0, 0, None) == ALIAS
+    assert P(A_, WP_, W3_, Y_, Y_ + 64, 4, 64, 64, None, 0, 0, None) == ALIAS
+    assert P(A_, WP_, W3_, W3_ + 4096, Z_, 4, 64, 64, None, 0, 0, None) == ALIAS
+    D = L.swiglu_mlp_down
+    assert D(Y_, W3_, Z_, 4, 64, 60, None) == UNSUP
+    assert D(None, None, None, 0, 64, 64, None) == OK
+    assert D(Y_, None, Z_, 4, 64, 64, None) == NULLP
+    assert D(Y_ + 2, W3_, Z_, 4, 64, 64, None) == MISAL
+    assert D(Y_, W3_, Y_ + 128, 4, 64, 64, None) == ALIAS
+    assert D(Y_, W3_, W3_ + 16, 4, 64, 64, None) == ALIAS
+    U = L.swiglu_mlp_unfused
+    G_, U_ = 0x90000000, 0xA0000000
+    assert U(A_, W1_, W2_, W3_, G_, U_, Y_, Z_, 4, 64, 60, None) == UNSUP
+    assert U(None, None, None, None, None, None, None, None, 0, 64, 64, None) == OK
+    assert U(A_, W1_, W2_, W3_, G_, U_, Y_, None, 4, 64, 64, None) == NULLP
+    assert U(A_, W1_, W2_, W3_, G_, U_, Y_, Z_ + 4, 4, 64, 64, None) == MISAL
+    assert U(A_, W1_, W2_, W3_, G_, U_, Y_, G_ + 32, 4, 64, 64, None) == ALIAS
+    assert U(A_, W1_, W2_, W3_, G_, W3_ + 128, Y_, Z_, 4, 64, 64, None) == ALIAS
+
+
 def test_workspace_holds_fp32_partials():
     L = sw.lib()
     # split-K workspace = splits x M x 2N fp32 partial sums; zero for the

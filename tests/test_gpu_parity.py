@@ -308,6 +308,43 @@ def test_panel_schedule(dev, M, K, N):
         assert np.array_equal(y, yf), "panels/%s != fused bitwise" % name
 
 
+@pytest.mark.parametrize("M,K,N", [
+    (96, 256, 520),       # panel schedule, partial last packed tile
+    (16, 3584, 18944),    # 7B decode width: decode schedule, long down-projection reduction
+    (256, 896, 4864),     # 0.5B shape, a slice of the prefill rows
+])
+def test_mlp_block(dev, M, K, N):
+    """The gated MLP block, fused and unfused: the fused Y against the
+    oracle's SwiGLU product, the unfused Y against the oracle's element-wise
+    step on the GPU's own bf16 Gate and Up (their one-ulp rounding
+    differences from summation order are checked by test_unfused_pipeline),
+    Z against the oracle's GEMM of the GPU's own Y (isolating the down
+    projection), and the fused block's Y bitwise equal to a plain
+    swiglu_fused_packed call."""
+    A, W1, W2 = inputs.gaussian_case(M, K, N, seed=7 * M + K + N)
+    W3 = inputs.weight(N, K, seed=M + K)
+    Ad, W1d, W2d, W3d = A.to(dev), W1.to(dev), W2.to(dev), W3.to(dev)
+    Wp = sw.swiglu_pack_weights(W1d, W2d)
+    say("[mlp] M=%d K=%d N=%d" % (M, K, N))
+    Yf, Zf = sw.swiglu_mlp_packed(Ad, Wp, W3d, N)
+    G = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    U = torch.empty_like(G)
+    Yu, Zu = sw.swiglu_mlp_unfused(Ad, W1d, W2d, W3d, G=G, U=U)
+    Y0 = sw.swiglu_fused_packed(Ad, Wp, N)
+    torch.cuda.synchronize()
+    yf, zf, yu, zu = gpu_bits(Yf), gpu_bits(Zf), gpu_bits(Yu), gpu_bits(Zu)
+    assert zf.shape == (M, K) and zu.shape == (M, K)
+    assert np.array_equal(yf, gpu_bits(Y0)), "MLP's Y != swiglu_fused_packed bitwise"
+    check_close(yf, oracle.swiglu(A, W1, W2), "mlp fused Y")
+    check_close(yu, oracle.silu_mul(gpu_bits(G), gpu_bits(U)), "mlp unfused Y")
+    W3b = inputs.as_bits(W3)
+    check_close(zf, oracle.gemm_bf16(yf, W3b), "mlp fused Z")
+    check_close(zu, oracle.gemm_bf16(yu, W3b), "mlp unfused Z")
+    Zd = sw.swiglu_mlp_down(Yf, W3d)
+    torch.cuda.synchronize()
+    check_close(gpu_bits(Zd), oracle.gemm_bf16(yf, W3b), "mlp down projection alone")
+
+
 def test_split_workspace_reused_across_shapes(dev):
     """One workspace serves split-K calls of different shapes in a row, and
     its earlier contents (partials of another shape, or garbage) never leak

@@ -343,6 +343,45 @@ def test_activation_before_reduction_matters(orc):
 
 
 # ---------------------------------------------------------------------------
+# Gated MLP block: SwiGLU product, then the down projection Z = Y x W3
+# ---------------------------------------------------------------------------
+
+def test_mlp_down_projection_pins(orc):
+    """Z = bf16(Y x W3) from the bf16 SwiGLU product Y: identity and one-hot
+    W3 select Y's columns exactly, doubling W3 doubles Z bitwise, an all-ones
+    column is the sequential fp32 sum of the bf16 Y row, and the whole of Z
+    sits within the fp32 summation bound of the fp64 product."""
+    M, K, N = 9, 24, 24
+    A, W1, W2 = inputs.gaussian_case(M, K, N, seed=71)
+    Ab, W1b, W2b = bits(A), bits(W1), bits(W2)
+    Y = orc.swiglu(Ab, W1b, W2b)
+    eye = bits(torch.eye(N, dtype=torch.bfloat16))
+    Y2, Z = orc.mlp(Ab, W1b, W2b, eye)
+    assert np.array_equal(Y2, Y) and np.array_equal(Z, Y)
+    sel = np.array([5, 0, 23, 7, 7, 12, 1, 19, 3, 3, 22, 9, 0, 15, 16, 2, 8, 11, 6, 4, 18, 20, 21, 13])
+    onehot = torch.zeros(N, K, dtype=torch.bfloat16)
+    onehot[torch.from_numpy(sel), torch.arange(K)] = 1.0
+    _, Z = orc.mlp(Ab, W1b, W2b, bits(onehot))
+    assert np.array_equal(Z, Y[:, sel]), "one-hot W3 must pick Y's columns (W3 is [N, K], not transposed)"
+    W3 = inputs.weight(N, K, seed=72)
+    _, Z1 = orc.mlp(Ab, W1b, W2b, bits(W3))
+    _, Z2 = orc.mlp(Ab, W1b, W2b, bits(W3 * 2))
+    assert np.array_equal(f32(Z2), 2 * f32(Z1))
+    W3c = W3.clone()
+    W3c[:, 0] = 1.0
+    _, Z = orc.mlp(Ab, W1b, W2b, bits(W3c))
+    acc = np.zeros(M, dtype=np.float32)
+    for n in range(N):
+        acc = (acc + f32(Y[:, n])).astype(np.float32)
+    assert np.array_equal(Z[:, 0], orc.bf16_rne(acc)), "the down projection reads the bf16 Y, summed in n order"
+    y64 = f32(Y).astype(np.float64)
+    w64 = f32(bits(W3)).astype(np.float64)
+    exact = y64 @ w64
+    bound = gamma(N - 1) * (np.abs(y64) @ np.abs(w64)) + np.abs(exact) * 2.0 ** -8 + 1e-30
+    assert np.all(np.abs(f32(Z1).astype(np.float64) - exact) <= bound)
+
+
+# ---------------------------------------------------------------------------
 # Input recipe
 # ---------------------------------------------------------------------------
 
