@@ -57,6 +57,9 @@ SMALL_SHAPES = [
     # streaming prefill kernel: ragged K (zero-chunk activation loads) with each
     # ring phase, 128- and 256-row tiles, M tails
     (200, 328, 384), (2600, 520, 256), (3000, 456, 640),
+    # 352 tiles of 256x128: the last 6 column tiles run as 128-row tiles in the
+    # same launch; partial last column tile, M tail, ragged K
+    (4000, 200, 2696),
 ]
 
 
