@@ -150,7 +150,7 @@ def cpu_baseline(w, M, target_s=12.0):
     }
 
 
-def bench_point(w, M, steps, warmup, variant, stream, prewarm_s=0.0):
+def bench_point(w, M, steps, warmup, variant, stream, prewarm_s=0.0, layout="per-tile"):
     import torch
     import swiglu_gated_mlp_amd as sw
     from swiglu_gated_mlp_amd import inputs
@@ -160,8 +160,9 @@ def bench_point(w, M, steps, warmup, variant, stream, prewarm_s=0.0):
     W1d, W2d = W1.to(dev), W2.to(dev)
     R = rotation_count(M, K, N)
     sets = []
+    pack = sw.swiglu_pack_weights_interleaved if layout == "interleaved" else sw.swiglu_pack_weights
     for r in range(R):
-        Wp = sw.swiglu_pack_weights(W1d, W2d)
+        Wp = pack(W1d, W2d)
         Ad = A.to(dev)
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         ws = sw.Workspace(dev)
@@ -169,8 +170,11 @@ def bench_point(w, M, steps, warmup, variant, stream, prewarm_s=0.0):
     del W1d, W2d
     torch.cuda.synchronize()
     v = sw.VARIANTS[variant]
-    fns = [(lambda s=s: sw.swiglu_fused_packed(s[0], s[1], N, Y=s[2], workspace=s[3], variant=v))
-           for s in sets]
+    if layout == "interleaved":
+        fns = [(lambda s=s: sw.swiglu_fused_packed_interleaved(s[0], s[1], N, Y=s[2])) for s in sets]
+    else:
+        fns = [(lambda s=s: sw.swiglu_fused_packed(s[0], s[1], N, Y=s[2], workspace=s[3], variant=v))
+               for s in sets]
     sec = time_gpu(fns, steps, warmup, stream, prewarm_s)
     per = sec / steps
     return {
@@ -295,6 +299,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--m", type=int, default=None, help="token count (default: the workload's largest)")
     ap.add_argument("--variant", default="auto", choices=["auto", "data_parallel", "split_k"])
+    ap.add_argument("--layout", default="per-tile", choices=["per-tile", "interleaved"],
+                    help="packed weight layout: per-128-column-tile [W1|W2] (default) or column-granular "
+                         "interleave (the data-parallel streaming schedule only)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--mlp", action="store_true",
                     help="also time the whole gated MLP block (with the down projection), fused and "
@@ -331,7 +338,7 @@ def main():
     w = inputs.BY_NAME[args.workload]
     M = args.m or w.m_max
 
-    res = bench_point(w, M, args.steps, args.warmup, args.variant, stream, args.prewarm)
+    res = bench_point(w, M, args.steps, args.warmup, args.variant, stream, args.prewarm, args.layout)
     per = res["per_launch_s"]
     bound = bound_of(M, w.K, w.N)
     if bound == "mfma":
@@ -343,7 +350,8 @@ def main():
     if args.all:
         for ww in inputs.WORKLOADS:
             for mm in ww.ms:
-                r = bench_point(ww, mm, max(10, args.steps // 2), 5, args.variant, stream, args.prewarm)
+                r = bench_point(ww, mm, max(10, args.steps // 2), 5, args.variant, stream, args.prewarm,
+                                args.layout)
                 tu = bench_unfused(ww, mm, max(5, args.steps // 4), 3, stream, args.prewarm)
                 b = bound_of(mm, ww.K, ww.N)
                 frac = r["tflops"] / MFMA_BF16_PEAK_TFLOPS if b == "mfma" else r["gbs"] / HBM_PEAK_GBS
@@ -380,7 +388,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/K) weights)",
         "config": {"workload": "%s M=%d K=%d N=%d" % (w.name, M, w.K, w.N), "M": M, "K": w.K,
-                   "N": w.N, "variant": args.variant, "rotation_sets": res["rotation"]},
+                   "N": w.N, "variant": args.variant, "layout": args.layout, "rotation_sets": res["rotation"]},
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 5),
                      "scope": "one swiglu_fused_packed call, all of its kernel launches",

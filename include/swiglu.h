@@ -168,6 +168,40 @@ swiglu_status swiglu_fused_packed(const swiglu_bf16 *A, const swiglu_bf16 *Wp,
 int swiglu_choose_variant(int64_t M, int64_t K, int64_t N);
 
 /* ------------------------------------------------------------------------
+ * Column-granular interleaved weights: the pages' W_fused with Gate in the
+ * even and Up in the odd columns ([Summary: Methodology], Kernel-2 "Fusion").
+ * Same block structure and size as the per-tile pack above (one 32 KiB block
+ * per 128 output columns and 64 k, 16-row groups of two 1 KiB halves in
+ * fragment lane order, padding zero), but packed row 2c of column tile jt
+ * holds W1 column jt*128 + c and row 2c + 1 holds W2 column jt*128 + c.
+ * With the weights as the MFMA's first operand, each lane then holds a
+ * column's Gate and Up in two adjacent accumulator registers, and the
+ * epilogue pairs them without moving data between lanes.  This layout is an
+ * ablation of the per-tile layout: the two compute bitwise-identical Y (the
+ * same MFMA chain per output element).
+ *
+ * swiglu_pack_weights_interleaved / swiglu_unpack_weights_interleaved: as
+ *   swiglu_pack_weights / swiglu_unpack_weights, in the interleaved layout;
+ *   the buffer size is swiglu_packed_bytes(K, N).
+ * swiglu_fused_packed_interleaved: Y = SiLU(A W1) * (A W2) from interleaved
+ *   packed weights on the data-parallel streaming schedule (no workspace, any
+ *   M >= 0); arguments, validation codes and stream semantics as
+ *   swiglu_fused_packed.
+ * ---------------------------------------------------------------------- */
+swiglu_status swiglu_pack_weights_interleaved(const swiglu_bf16 *W1,
+                                              const swiglu_bf16 *W2,
+                                              swiglu_bf16 *Wp, int64_t K,
+                                              int64_t N, void *stream);
+swiglu_status swiglu_unpack_weights_interleaved(const swiglu_bf16 *Wp,
+                                                swiglu_bf16 *W1, swiglu_bf16 *W2,
+                                                int64_t K, int64_t N,
+                                                void *stream);
+swiglu_status swiglu_fused_packed_interleaved(const swiglu_bf16 *A,
+                                              const swiglu_bf16 *Wp,
+                                              swiglu_bf16 *Y, int64_t M,
+                                              int64_t K, int64_t N, void *stream);
+
+/* ------------------------------------------------------------------------
  * The unfused pipeline the pages measure against ([Summary: Problem
  * Statement]: two GEMMs materialise Gate and Up in memory, then a separate
  * element-wise activation reads them back; [Summary: Results]: "PyTorch

@@ -45,6 +45,9 @@ SIGNATURES = {
     "swiglu_fused_packed": ([_P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, ctypes.c_int, _P],
                             ctypes.c_int),
     "swiglu_choose_variant": ([_I64, _I64, _I64], ctypes.c_int),
+    "swiglu_pack_weights_interleaved": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
+    "swiglu_unpack_weights_interleaved": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
+    "swiglu_fused_packed_interleaved": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "swiglu_gemm_bf16": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "swiglu_silu_mul": ([_P, _P, _P, _I64, _P], ctypes.c_int),
     "swiglu_unfused": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
@@ -177,6 +180,44 @@ def swiglu_unpack_weights(Wp: torch.Tensor, K: int, N: int, stream=None):
                                      K, N, _stream(stream))
     _check("swiglu_unpack_weights", st)
     return W1, W2
+
+
+def swiglu_pack_weights_interleaved(W1: torch.Tensor, W2: torch.Tensor, Wp: torch.Tensor | None = None,
+                                    stream=None) -> torch.Tensor:
+    """Pack W1, W2 [K,N] column-granular interleaved (Gate even, Up odd rows)."""
+    K, N = W1.shape
+    nbytes = swiglu_packed_bytes(K, N)
+    if nbytes == 0:
+        raise ValueError("invalid weight shape [%d,%d]" % (K, N))
+    if Wp is None:
+        Wp = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=W1.device)
+    elif Wp.numel() * Wp.element_size() < nbytes:
+        raise ValueError("Wp too small: need %d bytes" % nbytes)
+    st = lib().swiglu_pack_weights_interleaved(_dev_bf16(W1, "W1"), _dev_bf16(W2, "W2"), _dev_bf16(Wp, "Wp"),
+                                               K, N, _stream(stream))
+    _check("swiglu_pack_weights_interleaved", st)
+    return Wp
+
+
+def swiglu_unpack_weights_interleaved(Wp: torch.Tensor, K: int, N: int, stream=None):
+    """Inverse of swiglu_pack_weights_interleaved; returns (W1, W2)."""
+    W1 = torch.empty((K, N), dtype=torch.bfloat16, device=Wp.device)
+    W2 = torch.empty((K, N), dtype=torch.bfloat16, device=Wp.device)
+    st = lib().swiglu_unpack_weights_interleaved(_dev_bf16(Wp, "Wp"), _dev_bf16(W1, "W1"),
+                                                 _dev_bf16(W2, "W2"), K, N, _stream(stream))
+    _check("swiglu_unpack_weights_interleaved", st)
+    return W1, W2
+
+
+def swiglu_fused_packed_interleaved(A: torch.Tensor, Wp: torch.Tensor, N: int, Y: torch.Tensor | None = None,
+                                    stream=None) -> torch.Tensor:
+    """Y = SiLU(A W1) * (A W2) from column-interleaved packed weights."""
+    M, K = A.shape
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=A.device) if Y is None else Y
+    st = lib().swiglu_fused_packed_interleaved(_dev_bf16(A, "A"), _dev_bf16(Wp, "Wp"), _dev_bf16(Y, "Y"),
+                                               M, K, N, _stream(stream))
+    _check("swiglu_fused_packed_interleaved", st)
+    return Y
 
 
 def swiglu_workspace_bytes(M: int, K: int, N: int, variant: int = VARIANT_AUTO) -> int:

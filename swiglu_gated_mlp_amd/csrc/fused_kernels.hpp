@@ -880,9 +880,10 @@ constexpr int stream_smem_elems() {
 // next tile's first two stages are issued before the epilogue of the
 // current one, and its Y stores are left in flight while the next tile's K
 // loop starts.
-template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false>
+template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false, bool IL = false>
 __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_t* smem, int first, int stride,
                                                      int total) {
+    static_assert(!(IL && SPLIT), "the interleaved layout has no split-K schedule");
     constexpr int NW = 4;                       // waves, 32 output columns each
     constexpr int TM = BM / 32;                 // 32-row MFMA tiles per wave
     constexpr int A_INS = BM / 8 / NW;          // 1 KiB direct loads per wave per stage
@@ -958,7 +959,10 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
     // 8 k at chunk c = 2kk + (l >> 5) of each 64-deep block, i.e. packed
     // group t*8 + (wq & 3)*2 + ((l >> 4) & 1), half kk >> 1, fragment lane
     // (2(kk & 1) + (l >> 5))*16 + (l & 15): a lane byte offset plus a
-    // constant per (t, kk)
+    // constant per (t, kk).  Interleaved layout (IL): the wave's 64 packed
+    // rows (its 32 columns' Gate and Up, alternating) are groups
+    // 4(wq & 3) + 2t + ((l >> 4) & 1), so register set t holds Gate and Up
+    // of the columns 16t .. 16t + 15, each pair in two adjacent rows
     uint32_t w_off = 0;
     const char* w_tile = nullptr;
     // the item whose stages the loads below fetch (ld_ns = 0: none, every
@@ -978,7 +982,7 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
         }
         chunk_x = ((ll & 7) ^ (ll >> 3)) & 7;
         const int wq = it.n0 / 32 + wave;
-        w_off = (uint32_t)((((wq & 3) * 2 + ((ll >> 4) & 1)) * 1024 + (ll >> 5) * 128 + (ll & 15) * 8) * 2);
+        w_off = (uint32_t)((((wq & 3) * (IL ? 4 : 2) + ((ll >> 4) & 1)) * 1024 + (ll >> 5) * 128 + (ll & 15) * 8) * 2);
         w_tile = reinterpret_cast<const char*>(p.W1) + (size_t)(wq >> 2) * KB * (PACK_ROWS * PACK_BK * 2);
         ld_kb_first = it.kb_first;
         ld_ns = valid ? it.ns : 0;
@@ -1055,7 +1059,8 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
             dma16(src, smem + buf * ASTAGE + (wave * A_INS + j) * 512);
         } else {
             const int t = (j - A_INS) >> 2, kk = (j - A_INS) & 3;
-            const char* base = valid ? w_tile + (size_t)(ld_kb_first + ls) * (PACK_ROWS * PACK_BK * 2) + t * 16384 +
+            const char* base = valid ? w_tile + (size_t)(ld_kb_first + ls) * (PACK_ROWS * PACK_BK * 2) +
+                                           t * (IL ? 4096 : 16384) +
                                            (kk >> 1) * 1024 + (kk & 1) * 512
                                      : reinterpret_cast<const char*>(g_zero_chunk);
             wf[SET][t][kk] = *reinterpret_cast<const bf16x8*>(base + (w_off & keep));
@@ -1215,17 +1220,35 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int r = i * 32 + (el & 31);
+            if constexpr (IL) {
+                // accumulator register 4q + 2e + g of set t is packed row
+                // 32t + 8q + 4(l >> 5) + 2e + g: Gate (g = 0) and Up (g = 1)
+                // of column 16t + 4q + 2(l >> 5) + e, so each lane pairs
+                // adjacent registers and writes two columns (4 bytes) per (t, q)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float v[4];
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = silu_f(acc[0][i][0][4 * q + e]) * acc[1][i][0][4 * q + e];
-                u32x2 out;
-                out[0] = pack2(v[0], v[1]);
-                out[1] = pack2(v[2], v[3]);
-                const int chunk = wave * 4 + q;
-                *reinterpret_cast<u32x2*>(sY + r * PACK_BN + 8 * (chunk ^ (r & 15)) +
-                                          4 * ((el >> 5) ^ ((r >> 4) & 1))) = out;
+                    for (int q = 0; q < 4; ++q) {
+                        const unsigned out =
+                            pack2(silu_f(acc[t][i][0][4 * q]) * acc[t][i][0][4 * q + 1],
+                                  silu_f(acc[t][i][0][4 * q + 2]) * acc[t][i][0][4 * q + 3]);
+                        const int chunk = wave * 4 + 2 * t + (q >> 1);
+                        *reinterpret_cast<unsigned*>(sY + r * PACK_BN + 8 * (chunk ^ (r & 15)) +
+                                                     4 * ((q & 1) ^ ((r >> 4) & 1)) + 2 * (el >> 5)) = out;
+                    }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = silu_f(acc[0][i][0][4 * q + e]) * acc[1][i][0][4 * q + e];
+                    u32x2 out;
+                    out[0] = pack2(v[0], v[1]);
+                    out[1] = pack2(v[2], v[3]);
+                    const int chunk = wave * 4 + q;
+                    *reinterpret_cast<u32x2*>(sY + r * PACK_BN + 8 * (chunk ^ (r & 15)) +
+                                              4 * ((el >> 5) ^ ((r >> 4) & 1))) = out;
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1273,28 +1296,28 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
             for (int kk = 0; kk < 4; ++kk) asm volatile("" ::"v"(wf[q][t][kk]));
 }
 
-template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false>
+template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false, bool IL = false>
 __global__ __launch_bounds__(256) void stream_prefill_kernel(FusedArgs p, int total) {
     static_assert(!PANELS || (BM == 128 && !SPLIT), "panel schedule: one 128-row tile, data-parallel");
     __shared__ __attribute__((aligned(16))) uint16_t smem[stream_smem_elems<BM>()];
-    stream_prefill_tiles<BM, SPLIT, RAGGED, PANELS>(p, smem, blockIdx.x, gridDim.x, total);
+    stream_prefill_tiles<BM, SPLIT, RAGGED, PANELS, IL>(p, smem, blockIdx.x, gridDim.x, total);
 }
 
 // The 256-row tiles and the 128-row tail column tiles in one launch: blocks
 // 0 .. n_pers-1 work through the n_big 256-row tiles of `big` (block b takes
 // tiles b, b + n_pers, ...), the remaining blocks take one 128-row tile of
 // `tail` each and start on CUs as the 256-row work drains.
-template <bool RAGGED>
+template <bool RAGGED, bool IL = false>
 __global__ __launch_bounds__(256) void stream_prefill_mixed_kernel(FusedArgs big, FusedArgs tail, int n_pers,
                                                                    int n_big) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[stream_smem_elems<256>()];
     static_assert(stream_smem_elems<256>() >= stream_smem_elems<128>(), "one LDS block serves both tiles");
     const int b = blockIdx.x;
     if (b < n_pers) {
-        stream_prefill_tiles<256, false, RAGGED>(big, smem, b, n_pers, n_big);
+        stream_prefill_tiles<256, false, RAGGED, false, IL>(big, smem, b, n_pers, n_big);
     } else {
         const int n_tail = gridDim.x - n_pers;
-        stream_prefill_tiles<128, false, RAGGED>(tail, smem, b - n_pers, n_tail, n_tail);
+        stream_prefill_tiles<128, false, RAGGED, false, IL>(tail, smem, b - n_pers, n_tail, n_tail);
     }
 }
 
@@ -1438,6 +1461,10 @@ struct PackChunk {
     int k0;         // first of the chunk's 8 consecutive k (may be >= K: padding)
 };
 
+// IL = false: per-tile [W1 | W2] (packed rows 0-127 the tile's W1 columns,
+// 128-255 its W2 columns).  IL = true: column-granular interleave (packed row
+// 2c the tile's W1 column c, row 2c + 1 its W2 column c).
+template <bool IL>
 __device__ __forceinline__ PackChunk pack_chunk(long long q, int KB) {
     const long long blk = q >> 11;                  // jt * KB + kb
     const int within = (int)(q & 2047);
@@ -1448,19 +1475,25 @@ __device__ __forceinline__ PackChunk pack_chunk(long long q, int KB) {
     const int kb = (int)(blk % KB);
     const int jt = (int)(blk / KB);
     PackChunk c;
-    c.up = prow >= PACK_BN;
-    c.n = jt * PACK_BN + (c.up ? prow - PACK_BN : prow);
+    if constexpr (IL) {
+        c.up = (prow & 1) != 0;
+        c.n = jt * PACK_BN + (prow >> 1);
+    } else {
+        c.up = prow >= PACK_BN;
+        c.n = jt * PACK_BN + (c.up ? prow - PACK_BN : prow);
+    }
     c.k0 = kb * PACK_BK + half * 32 + (lane >> 4) * 8;
     return c;
 }
 
+template <bool IL>
 __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ W1,
                                                    const uint16_t* __restrict__ W2,
                                                    uint16_t* __restrict__ Wp, int K, int N,
                                                    int KB, long long nchunks) {
     const long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= nchunks) return;
-    const PackChunk c = pack_chunk(q, KB);
+    const PackChunk c = pack_chunk<IL>(q, KB);
     const uint16_t* W = c.up ? W2 : W1;
     unsigned short v[8];
 #pragma unroll
@@ -1474,13 +1507,14 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
     *reinterpret_cast<u32x4*>(Wp + q * 8) = out;
 }
 
+template <bool IL>
 __global__ __launch_bounds__(256) void unpack_kernel(const uint16_t* __restrict__ Wp,
                                                      uint16_t* __restrict__ W1,
                                                      uint16_t* __restrict__ W2, int K, int N,
                                                      int KB, long long nchunks) {
     const long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= nchunks) return;
-    const PackChunk c = pack_chunk(q, KB);
+    const PackChunk c = pack_chunk<IL>(q, KB);
     if (c.n >= N) return;
     uint16_t* W = c.up ? W2 : W1;
     const u32x4 in = *reinterpret_cast<const u32x4*>(Wp + q * 8);

@@ -223,14 +223,61 @@ hipError_t launch_prefill(const swk::FusedArgs& a, int grid, hipStream_t s) {
 
 // `total` work items (tiles, or tile x K split) on `grid` <= total workgroups;
 // each workgroup takes items b, b + grid, ...
-template <int BM, bool SPLIT, bool PANELS = false>
+template <int BM, bool SPLIT, bool PANELS = false, bool IL = false>
 hipError_t launch_stream(const swk::FusedArgs& a, int total, int grid, hipStream_t s) {
     const void* fn = (a.K % swk::BK) != 0
-                         ? reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, true, PANELS>)
-                         : reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, false, PANELS>);
+                         ? reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, true, PANELS, IL>)
+                         : reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, false, PANELS, IL>);
     swk::FusedArgs args = a;
     void* kargs[] = {&args, &total};
     return hipLaunchKernel(fn, dim3(grid), dim3(256), kargs, 0, s);
+}
+
+// The data-parallel streaming schedules (128- or 256-row tiles, the panel
+// schedule, the mixed 256/128-row launch) on either weight layout.
+template <bool IL>
+hipError_t launch_stream_dp(const swk::FusedArgs& a, const Plan& p, hipStream_t s) {
+    const int grid = p.tiles;
+    if (p.t.BM == 128) {
+        if (p.panels > 0) {
+            swk::FusedArgs pa = a;
+            pa.panels = p.panels;
+            const int g = std::min(p.panels, p.cus);
+            return launch_stream<128, false, true, IL>(pa, g, g, s);
+        }
+        return launch_stream<128, false, false, IL>(a, grid, grid, s);
+    }
+    // one workgroup per CU works through the 256-row tiles
+    if (p.tail_ntiles == 0) return launch_stream<256, false, false, IL>(a, grid, std::min(grid, p.cus), s);
+    // one launch: the 256-row tiles of the first column tiles, then
+    // the last tail_ntiles column tiles as 128-row tiles
+    swk::FusedArgs big = a, tail = a;
+    big.tiles_n = p.tiles_n - p.tail_ntiles;
+    tail.tiles_m = (int)ceil_div(a.M, 128);
+    tail.tiles_n = p.tail_ntiles;
+    tail.n_tile0 = big.tiles_n;
+    int n_big = big.tiles_m * big.tiles_n;
+    int n_pers = std::min(n_big, p.cus);
+    const int grid_all = n_pers + tail.tiles_m * tail.tiles_n;
+    const void* fn = (a.K % swk::BK) != 0
+                         ? reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<true, IL>)
+                         : reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<false, IL>);
+    void* kargs[] = {&big, &tail, &n_pers, &n_big};
+    return hipLaunchKernel(fn, dim3(grid_all), dim3(256), kargs, 0, s);
+}
+
+// The data-parallel streaming plan for any M (small M included: one row of
+// 128-row tiles, on the panel schedule when it leaves CUs idle).
+Plan stream_dp_plan(int64_t M, int64_t K, int64_t N, int cus) {
+    Plan p = make_plan(M, K, N, SWIGLU_VARIANT_DATA_PARALLEL, cus);
+    if (p.t.BM < 128) {
+        p.t = {128, 128};
+        p.tiles_m = (int)ceil_div(M, 128);
+        p.tiles = p.tiles_m * p.tiles_n;
+        p.tail_ntiles = 0;
+        p.panels = (p.tiles_m == 1 && p.tiles_n < p.cus) ? 4 * p.tiles_n : 0;
+    }
+    return p;
 }
 
 hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) {
@@ -268,33 +315,10 @@ hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) 
                          : launch_tile<64, 128, 2, 2, true, true, false>(a, grid, s);
         case 128:
             if (split) return launch_stream<128, true>(a, grid, grid, s);
-            if (p.panels > 0) {
-                swk::FusedArgs pa = a;
-                pa.panels = p.panels;
-                const int g = std::min(p.panels, p.cus);
-                return launch_stream<128, false, true>(pa, g, g, s);
-            }
-            return launch_stream<128, false>(a, grid, grid, s);
-        default: {
+            return launch_stream_dp<false>(a, p, s);
+        default:
             if (split) return launch_stream<256, true>(a, grid, grid, s);
-            // one workgroup per CU works through the 256-row tiles
-            if (p.tail_ntiles == 0) return launch_stream<256, false>(a, grid, std::min(grid, p.cus), s);
-            // one launch: the 256-row tiles of the first column tiles, then
-            // the last tail_ntiles column tiles as 128-row tiles
-            swk::FusedArgs big = a, tail = a;
-            big.tiles_n = p.tiles_n - p.tail_ntiles;
-            tail.tiles_m = (int)ceil_div(a.M, 128);
-            tail.tiles_n = p.tail_ntiles;
-            tail.n_tile0 = big.tiles_n;
-            int n_big = big.tiles_m * big.tiles_n;
-            int n_pers = std::min(n_big, p.cus);
-            const int grid_all = n_pers + tail.tiles_m * tail.tiles_n;
-            const void* fn = (a.K % swk::BK) != 0
-                                 ? reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<true>)
-                                 : reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<false>);
-            void* kargs[] = {&big, &tail, &n_pers, &n_big};
-            return hipLaunchKernel(fn, dim3(grid_all), dim3(256), kargs, 0, s);
-        }
+            return launch_stream_dp<false>(a, p, s);
     }
 }
 
@@ -331,8 +355,13 @@ size_t swiglu_packed_bytes(int64_t K, int64_t N) {
     return (size_t)packed_elems(K, N) * sizeof(swiglu_bf16);
 }
 
-swiglu_status swiglu_pack_weights(const swiglu_bf16* W1, const swiglu_bf16* W2, swiglu_bf16* Wp,
-                                  int64_t K, int64_t N, void* stream) {
+}  // extern "C"
+
+namespace {
+
+template <bool IL>
+swiglu_status pack_impl(const swiglu_bf16* W1, const swiglu_bf16* W2, swiglu_bf16* Wp, int64_t K, int64_t N,
+                        void* stream) {
     swiglu_status st = check_shape(0, K, N);
     if (st != SWIGLU_OK) return st;
     if (!W1 || !W2 || !Wp) return SWIGLU_ERR_NULL_POINTER;
@@ -345,13 +374,14 @@ swiglu_status swiglu_pack_weights(const swiglu_bf16* W1, const swiglu_bf16* W2, 
     int Ki = (int)K, Ni = (int)N;
     void* args[] = {(void*)&W1, (void*)&W2, (void*)&Wp, &Ki, &Ni, (void*)&KB, (void*)&nchunks};
     const dim3 grid((unsigned)ceil_div(nchunks, 256));
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&swk::pack_kernel), grid, dim3(256),
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&swk::pack_kernel<IL>), grid, dim3(256),
                                    args, 0, (hipStream_t)stream);
     return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
 }
 
-swiglu_status swiglu_unpack_weights(const swiglu_bf16* Wp, swiglu_bf16* W1, swiglu_bf16* W2,
-                                    int64_t K, int64_t N, void* stream) {
+template <bool IL>
+swiglu_status unpack_impl(const swiglu_bf16* Wp, swiglu_bf16* W1, swiglu_bf16* W2, int64_t K, int64_t N,
+                          void* stream) {
     swiglu_status st = check_shape(0, K, N);
     if (st != SWIGLU_OK) return st;
     if (!W1 || !W2 || !Wp) return SWIGLU_ERR_NULL_POINTER;
@@ -364,8 +394,52 @@ swiglu_status swiglu_unpack_weights(const swiglu_bf16* Wp, swiglu_bf16* W1, swig
     int Ki = (int)K, Ni = (int)N;
     void* args[] = {(void*)&Wp, (void*)&W1, (void*)&W2, &Ki, &Ni, (void*)&KB, (void*)&nchunks};
     const dim3 grid((unsigned)ceil_div(nchunks, 256));
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&swk::unpack_kernel), grid, dim3(256),
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&swk::unpack_kernel<IL>), grid, dim3(256),
                                    args, 0, (hipStream_t)stream);
+    return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+swiglu_status swiglu_pack_weights(const swiglu_bf16* W1, const swiglu_bf16* W2, swiglu_bf16* Wp,
+                                  int64_t K, int64_t N, void* stream) {
+    return pack_impl<false>(W1, W2, Wp, K, N, stream);
+}
+
+swiglu_status swiglu_unpack_weights(const swiglu_bf16* Wp, swiglu_bf16* W1, swiglu_bf16* W2,
+                                    int64_t K, int64_t N, void* stream) {
+    return unpack_impl<false>(Wp, W1, W2, K, N, stream);
+}
+
+swiglu_status swiglu_pack_weights_interleaved(const swiglu_bf16* W1, const swiglu_bf16* W2, swiglu_bf16* Wp,
+                                              int64_t K, int64_t N, void* stream) {
+    return pack_impl<true>(W1, W2, Wp, K, N, stream);
+}
+
+swiglu_status swiglu_unpack_weights_interleaved(const swiglu_bf16* Wp, swiglu_bf16* W1, swiglu_bf16* W2,
+                                                int64_t K, int64_t N, void* stream) {
+    return unpack_impl<true>(Wp, W1, W2, K, N, stream);
+}
+
+swiglu_status swiglu_fused_packed_interleaved(const swiglu_bf16* A, const swiglu_bf16* Wp, swiglu_bf16* Y,
+                                              int64_t M, int64_t K, int64_t N, void* stream) {
+    swiglu_status st = check_shape(M, K, N);
+    if (st != SWIGLU_OK) return st;
+    if (M == 0) return SWIGLU_OK;
+    if (!A || !Wp || !Y) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(A) || !aligned16(Wp) || !aligned16(Y)) return SWIGLU_ERR_MISALIGNED;
+    const Range y = range_of(Y, M * N * 2);
+    if (overlap(y, range_of(A, M * K * 2)) || overlap(y, range_of(Wp, packed_elems(K, N) * 2)))
+        return SWIGLU_ERR_ALIASING;
+    const Plan p = stream_dp_plan(M, K, N, cu_count_now());
+    swk::FusedArgs a{};
+    a.A = A; a.W1 = Wp; a.W2 = nullptr; a.Y = Y;
+    a.M = (int)M; a.K = (int)K; a.N = (int)N;
+    a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n;
+    a.splits = 1; a.kb_per_split = p.KB; a.KB = p.KB;
+    const hipError_t e = launch_stream_dp<true>(a, p, (hipStream_t)stream);
     return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
 }
 

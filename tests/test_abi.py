@@ -146,6 +146,22 @@ def test_mlp_errors():
     assert U(A_, W1_, W2_, W3_, G_, W3_ + 128, Y_, Z_, 4, 64, 64, None) == ALIAS
 
 
+def test_interleaved_errors():
+    L = sw.lib()
+    assert L.swiglu_pack_weights_interleaved(W1_, W2_, W1_ + 16, 64, 64, None) == ALIAS
+    assert L.swiglu_pack_weights_interleaved(W1_, W2_, WP_, 63, 64, None) == UNSUP
+    assert L.swiglu_pack_weights_interleaved(W1_, None, WP_, 64, 64, None) == NULLP
+    assert L.swiglu_unpack_weights_interleaved(WP_, W1_, W1_, 64, 64, None) == ALIAS
+    assert L.swiglu_unpack_weights_interleaved(WP_ + 4, W1_, W2_, 64, 64, None) == MISAL
+    F = L.swiglu_fused_packed_interleaved
+    assert F(None, None, None, 0, 64, 64, None) == OK
+    assert F(A_, WP_, Y_, 4, 64, 60, None) == UNSUP
+    assert F(A_, None, Y_, 4, 64, 64, None) == NULLP
+    assert F(A_, WP_, Y_ + 2, 4, 64, 64, None) == MISAL
+    assert F(A_, WP_, WP_ + 64, 4, 64, 64, None) == ALIAS
+    assert F(A_, WP_, A_ + 16, 4, 64, 64, None) == ALIAS
+
+
 def test_workspace_holds_fp32_partials():
     L = sw.lib()
     # split-K workspace = splits x M x 2N fp32 partial sums; zero for the

@@ -348,6 +348,61 @@ def test_mlp_block(dev, M, K, N):
     check_close(gpu_bits(Zd), oracle.gemm_bf16(yf, W3b), "mlp down projection alone")
 
 
+def test_interleaved_pack_roundtrip_and_layout(dev):
+    """Column-granular interleaved pack: unpack(pack(W)) == W bitwise, packed
+    row 2c of a tile holds W1 column c and row 2c + 1 holds W2 column c, and
+    the padding (columns past N, k past K) is zero."""
+    for K, N in [(64, 128), (72, 136), (200, 520)]:
+        _, W1, W2 = inputs.gaussian_case(1, K, N, seed=3 * K + N)
+        W1d, W2d = W1.to(dev), W2.to(dev)
+        Wp = sw.swiglu_pack_weights_interleaved(W1d, W2d)
+        V1, V2 = sw.swiglu_unpack_weights_interleaved(Wp, K, N)
+        torch.cuda.synchronize()
+        assert torch.equal(V1.view(torch.int16), W1d.view(torch.int16))
+        assert torch.equal(V2.view(torch.int16), W2d.view(torch.int16))
+        P = inputs.as_bits(Wp.cpu())
+        KB = (K + 63) // 64
+        w1, w2 = inputs.as_bits(W1), inputs.as_bits(W2)
+
+        def pos(jt, kb, prow, k):
+            g, r, h, kk = prow // 16, prow % 16, k // 32, k % 32
+            return ((((jt * KB + kb) * 16 + g) * 2 + h) * 64 + (kk // 8) * 16 + r) * 8 + kk % 8
+
+        for n in range(0, N, 3):
+            for k in range(0, K, 5):
+                jt, c = n // 128, n % 128
+                assert P[pos(jt, k // 64, 2 * c, k % 64)] == w1[k, n]
+                assert P[pos(jt, k // 64, 2 * c + 1, k % 64)] == w2[k, n]
+        JT = (N + 127) // 128
+        for c in range(N % 128 or 128, 128):
+            for k in range(0, 64, 9):
+                assert P[pos(JT - 1, 0, 2 * c, k)] == 0 and P[pos(JT - 1, 0, 2 * c + 1, k)] == 0
+        if K % 64:
+            for n in range(0, N, 11):
+                for k in range(K % 64, 64, 5):
+                    assert P[pos(n // 128, KB - 1, 2 * (n % 128), k)] == 0
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (1, 64, 128), (40, 200, 520), (128, 512, 4096), (300, 136, 264),
+    (2100, 72, 256), (4000, 200, 2696),
+])
+def test_interleaved_layout_matches(dev, M, K, N):
+    """The interleaved-layout path against the oracle and bitwise against the
+    per-tile layout on the same schedule (one decode-sized M, panel schedule,
+    128-row tiles, 256-row tiles with the mixed tail; ragged K and N)."""
+    A, W1, W2 = inputs.gaussian_case(M, K, N, seed=5 * M + K + N)
+    Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
+    say("[interleaved] M=%d K=%d N=%d" % (M, K, N))
+    Wi = sw.swiglu_pack_weights_interleaved(W1d, W2d)
+    Yi = gpu_bits(sw.swiglu_fused_packed_interleaved(Ad, Wi, N))
+    check_close(Yi, oracle.swiglu(A, W1, W2), "interleaved %s" % ((M, K, N),))
+    if M > 64:
+        Wp = sw.swiglu_pack_weights(W1d, W2d)
+        Yp = gpu_bits(sw.swiglu_fused_packed(Ad, Wp, N, variant=DP))
+        assert np.array_equal(Yi, Yp), "interleaved != per-tile layout bitwise"
+
+
 def test_split_workspace_reused_across_shapes(dev):
     """One workspace serves split-K calls of different shapes in a row, and
     its earlier contents (partials of another shape, or garbage) never leak
