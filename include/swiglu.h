@@ -64,8 +64,11 @@ typedef enum {
 } swiglu_status;
 
 /* Schedules of the fused packed entry point.
- *  DATA_PARALLEL: one workgroup per output tile, full K per tile; for large M
- *                 (the pages' Kernel-1 regime, [Summary: Methodology] Kernel-1).
+ *  DATA_PARALLEL: the streaming kernel, full K per work item: 256- or
+ *                 128-row tiles for large M (the pages' Kernel-1 regime,
+ *                 [Summary: Methodology] Kernel-1); for one row of 128-row
+ *                 tiles with fewer column tiles than CUs, the tiles' 32-column
+ *                 weight panels spread over the CUs instead.
  *  SPLIT_K:       the K range is split across workgroups; each split writes
  *                 its fp32 Gate/Up partial sums to the workspace and a second
  *                 kernel adds them in fixed split order 0..S-1 BEFORE SiLU,
@@ -77,7 +80,11 @@ typedef enum {
  *                 split K and add their fp32 partials in LDS in fixed order
  *                 BEFORE SiLU; needs no workspace.  The product is then bound
  *                 by reading the weights from HBM.
- *  AUTO:          the library picks from M, K, N and the device's CU count. */
+ *  AUTO:          the library picks from M, K, N and the device's CU count:
+ *                 DECODE up to 32 rows, and up to 64 rows while the weight
+ *                 panels (4 per 128 columns) number fewer than the CUs;
+ *                 otherwise DATA_PARALLEL, or SPLIT_K when the data-parallel
+ *                 tiles would fill under half the CUs (and K >= 32 M). */
 typedef enum {
     SWIGLU_VARIANT_AUTO = 0,
     SWIGLU_VARIANT_DATA_PARALLEL = 1,

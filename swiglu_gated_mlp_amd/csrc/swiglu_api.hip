@@ -101,10 +101,15 @@ struct TileCfg {
     int BM, BN;
 };
 
+// Split-K keeps small row tiles for small M; the data-parallel schedule is
+// the streaming kernel at every M (one row of 128-row tiles for M <= 128, on
+// the panel schedule when its column tiles leave CUs idle).
 TileCfg packed_tile_for(int64_t M, int variant) {
-    if (M <= 32) return {32, 128};
-    if (M <= 64) return {64, 128};
-    if (variant == SWIGLU_VARIANT_SPLIT_K) return {128, 128};
+    if (variant == SWIGLU_VARIANT_SPLIT_K) {
+        if (M <= 32) return {32, 128};
+        if (M <= 64) return {64, 128};
+        return {128, 128};
+    }
     if (M <= 2048) return {128, 128};
     return {256, 128};
 }
@@ -138,8 +143,15 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int variant, int cus) {
     int v = variant;
     int auto_split_cap = 0;   // AUTO's split-K: most splits worth their partial-sum traffic
     if (v == SWIGLU_VARIANT_AUTO) {
-        if (M <= kDecodeMaxM) {
+        // Decode up to 32 rows; from 33 to 64 rows only while the weight
+        // panels cannot fill the CUs (a small product, where the decode
+        // kernel's single pass wins), otherwise the panel schedule streams
+        // the weights faster (measured: 7B M=64 57 us against 76 us).
+        const int64_t panels = 4 * ceil_div(N, swk::PACK_BN);
+        if (M <= 32 || (M <= kDecodeMaxM && panels < cus)) {
             v = SWIGLU_VARIANT_DECODE;
+        } else if (M <= kDecodeMaxM) {
+            v = SWIGLU_VARIANT_DATA_PARALLEL;
         } else {
             // Split-K writes and re-reads S fp32 partial sums of Gate and Up,
             // 16*S*M*N bytes against the 4*K*N bytes of weights: worth it only
@@ -266,18 +278,9 @@ hipError_t launch_stream_dp(const swk::FusedArgs& a, const Plan& p, hipStream_t 
     return hipLaunchKernel(fn, dim3(grid_all), dim3(256), kargs, 0, s);
 }
 
-// The data-parallel streaming plan for any M (small M included: one row of
-// 128-row tiles, on the panel schedule when it leaves CUs idle).
+// The data-parallel streaming plan (any M).
 Plan stream_dp_plan(int64_t M, int64_t K, int64_t N, int cus) {
-    Plan p = make_plan(M, K, N, SWIGLU_VARIANT_DATA_PARALLEL, cus);
-    if (p.t.BM < 128) {
-        p.t = {128, 128};
-        p.tiles_m = (int)ceil_div(M, 128);
-        p.tiles = p.tiles_m * p.tiles_n;
-        p.tail_ntiles = 0;
-        p.panels = (p.tiles_m == 1 && p.tiles_n < p.cus) ? 4 * p.tiles_n : 0;
-    }
-    return p;
+    return make_plan(M, K, N, SWIGLU_VARIANT_DATA_PARALLEL, cus);
 }
 
 hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) {

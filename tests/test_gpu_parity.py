@@ -268,23 +268,27 @@ def test_edge_cases(dev):
     assert np.all((gpu_bits(Y) & 0x7FFF) == 0)
 
 
-@pytest.mark.parametrize("M,K,N", [
-    (1, 6144, 24576),    # long K, >= 192 column tiles: 8 column groups per workgroup
-    (16, 3584, 4096),    # short K: one column group, 8 K blocks in flight per wave
-    (32, 6144, 12288),   # long K, M <= 32: 4 column groups
-    (32, 512, 16384),    # short K, wide N: 8 column groups
-    (48, 6144, 12288),   # long K, M <= 64: 4 column groups
-    (64, 1024, 2048),    # short K, M <= 64: 2 column groups
+@pytest.mark.parametrize("M,K,N,auto_decode", [
+    (1, 6144, 24576, True),    # long K, >= 192 column tiles: 8 column groups per workgroup
+    (16, 3584, 4096, True),    # short K: one column group, 8 K blocks in flight per wave
+    (32, 6144, 12288, True),   # long K, M <= 32: 4 column groups
+    (32, 512, 16384, True),    # short K, wide N: 8 column groups
+    (48, 6144, 12288, False),  # long K, M <= 64: 4 column groups (AUTO takes the panel schedule)
+    (64, 1024, 2048, True),    # short K, M <= 64, few panels: 2 column groups
 ])
-def test_decode_configurations(dev, M, K, N):
-    """Every decode configuration the library picks by M, K and N (column
-    groups per workgroup, K blocks in flight) against the oracle, all rows."""
+def test_decode_configurations(dev, M, K, N, auto_decode):
+    """Every decode configuration by M, K and N (column groups per workgroup,
+    K blocks in flight) against the oracle, all rows; AUTO picks decode for
+    the shapes it should."""
     A, W1, W2 = inputs.gaussian_case(M, K, N, seed=M + K + N)
     Wp = sw.swiglu_pack_weights(W1.to(dev), W2.to(dev))
-    Y = sw.swiglu_fused_packed(A.to(dev), Wp, N, variant=AUTO)
+    Y = sw.swiglu_fused_packed(A.to(dev), Wp, N, variant=DECODE)
+    Ya = sw.swiglu_fused_packed(A.to(dev), Wp, N, variant=AUTO)
     torch.cuda.synchronize()
-    assert sw.swiglu_choose_variant(M, K, N) == DECODE
-    check_close(gpu_bits(Y), oracle.swiglu(A, W1, W2), "decode %s" % ((M, K, N),))
+    assert (sw.swiglu_choose_variant(M, K, N) == DECODE) == auto_decode
+    ref = oracle.swiglu(A, W1, W2)
+    check_close(gpu_bits(Y), ref, "decode %s" % ((M, K, N),))
+    check_close(gpu_bits(Ya), ref, "auto %s" % ((M, K, N),))
 
 
 @pytest.mark.parametrize("M,K,N", [
