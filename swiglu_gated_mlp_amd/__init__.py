@@ -101,15 +101,17 @@ def _check(fn: str, status: int) -> None:
 
 
 def _dev_bf16(t: torch.Tensor, name: str) -> int:
+    # fast path first (a call's host time matters for small shapes); the
+    # checks below only name what is wrong
+    if isinstance(t, torch.Tensor) and t.is_cuda and t.dtype is torch.bfloat16 and t.is_contiguous():
+        return t.data_ptr()
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch tensor" % name)
     if t.device.type != "cuda":
         raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
     if t.dtype != torch.bfloat16:
         raise TypeError("%s must be bfloat16 (got %s)" % (name, t.dtype))
-    if not t.is_contiguous():
-        raise ValueError("%s must be contiguous" % name)
-    return t.data_ptr()
+    raise ValueError("%s must be contiguous" % name)
 
 
 def _stream(stream) -> int:
@@ -224,6 +226,19 @@ def swiglu_workspace_bytes(M: int, K: int, N: int, variant: int = VARIANT_AUTO) 
     return int(lib().swiglu_workspace_bytes(M, K, N, int(variant)))
 
 
+_ws_need: dict = {}
+
+
+def _workspace_need(M: int, K: int, N: int, variant: int, device: torch.device) -> int:
+    """swiglu_workspace_bytes, remembered per (shape, variant, device): the
+    plan depends only on these and the device's CU count."""
+    key = (M, K, N, variant, device.index)
+    need = _ws_need.get(key)
+    if need is None:
+        need = _ws_need[key] = swiglu_workspace_bytes(M, K, N, variant)
+    return need
+
+
 def swiglu_choose_variant(M: int, K: int, N: int) -> int:
     return int(lib().swiglu_choose_variant(M, K, N))
 
@@ -269,8 +284,10 @@ def swiglu_fused_packed(A: torch.Tensor, Wp: torch.Tensor, N: int, Y: torch.Tens
     s = _stream(stream)
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
-    need = swiglu_workspace_bytes(M, K, N, variant)
-    if isinstance(workspace, Workspace):
+    need = _workspace_need(M, K, N, int(variant), A.device)
+    if need == 0 and not isinstance(workspace, torch.Tensor):
+        ws = None
+    elif isinstance(workspace, Workspace):
         ws = workspace.get(need)
     elif workspace is None:
         ws = _workspace_for(A.device, s).get(need)

@@ -180,3 +180,15 @@ def test_probe_argument_errors():
     assert L.swiglu_probe_mfma(Y_, 0, 1, None) == SHAPE
     assert L.swiglu_probe_read(A_, 15, Y_, 1, None) == SHAPE
     assert L.swiglu_probe_read(A_ + 4, 64, Y_, 1, None) == MISAL
+
+
+def test_binding_argument_errors():
+    """The binding names what is wrong before any call into the library."""
+    import torch
+    a = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        sw._dev_bf16([1, 2], "A")
+    with pytest.raises(ValueError, match="GPU tensor"):
+        sw._dev_bf16(a, "A")
+    with pytest.raises(ValueError, match="GPU tensor"):
+        sw._dev_bf16(a.float(), "A")
