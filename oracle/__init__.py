@@ -19,6 +19,9 @@ Inference" as summarised on gist.science ("Summary"):
 * ``silu``        -- SiLU(x) = x / (1 + e^-x), the Swish applied to Gate;
   Summary, "Methodology", Kernel-1.
 * ``bf16_rne``    -- rounding of the fp32 result to the bf16 output type.
+* ``swiglu_fp8``  -- the product from FP8 E4M3 operands with per-tensor
+  scales (the pages' remark that quantised GEMMs raise SwiGLU's relative cost,
+  Summary, "Problem Statement"; the scale convention is this build's reading).
 * ``mlp``         -- the gated MLP block the pages' "share of MLP time" refers
   to: the bf16 SwiGLU product Y, then the down projection Z = bf16(Y x W3) with
   fp32 accumulation (Summary, "Problem Statement"; the pages do not spell the
@@ -94,6 +97,7 @@ class Oracle:
         lib = ctypes.CDLL(lib_path)
         u16p = ctypes.POINTER(ctypes.c_uint16)
         f32p = ctypes.POINTER(ctypes.c_float)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
         i64 = ctypes.c_int64
         sig = {
             "oracle_bf16_rne": ([ctypes.c_float], ctypes.c_uint16),
@@ -106,6 +110,9 @@ class Oracle:
             "oracle_unfused": ([u16p, u16p, u16p, i64, i64, i64, u16p, u16p, u16p], ctypes.c_int),
             "oracle_bf16_rne_array": ([f32p, u16p, i64], None),
             "oracle_silu_array": ([f32p, f32p, i64], None),
+            "oracle_e4m3_to_f32": ([ctypes.c_uint8], ctypes.c_float),
+            "oracle_swiglu_fp8": ([u8p, u8p, u8p, i64, i64, i64, ctypes.c_float, ctypes.c_float, u16p, f32p],
+                                  ctypes.c_int),
             "oracle_set_threads": ([ctypes.c_int], None),
             "oracle_max_threads": ([], ctypes.c_int),
         }
@@ -173,6 +180,32 @@ class Oracle:
         if want_gu:
             out += [G, U]
         return out[0] if len(out) == 1 else tuple(out)
+
+    def e4m3_to_f32(self, b) -> np.ndarray:
+        """FP8 E4M3 bytes -> fp32 values (exact)."""
+        b = np.asarray(b, dtype=np.uint8)
+        return np.array([self.lib.oracle_e4m3_to_f32(int(x)) for x in b.ravel()],
+                        dtype=np.float32).reshape(b.shape)
+
+    def swiglu_fp8(self, A8, W1_8, W2_8, sg: float, su: float, want_p: bool = False):
+        """FP8 variant: Y = bf16_RNE(SiLU(sg * A8 W1_8) * (su * A8 W2_8)),
+        E4M3 bytes in, per-tensor scale products sg = fp32(sA*s1), su =
+        fp32(sA*s2).  Returns Y (uint16 bits [M,N]), and with ``want_p`` the
+        fp32 product P."""
+        A8, W1_8, W2_8 = (np.ascontiguousarray(np.asarray(x, dtype=np.uint8)) for x in (A8, W1_8, W2_8))
+        M, K = A8.shape
+        if W1_8.shape != W2_8.shape or W1_8.shape[0] != K:
+            raise ValueError("shape mismatch: A %s W1 %s W2 %s" % (A8.shape, W1_8.shape, W2_8.shape))
+        N = W1_8.shape[1]
+        Y = np.empty((M, N), dtype=np.uint16)
+        P = np.empty((M, N), dtype=np.float32) if want_p else None
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        rc = self.lib.oracle_swiglu_fp8(A8.ctypes.data_as(u8p), W1_8.ctypes.data_as(u8p),
+                                        W2_8.ctypes.data_as(u8p), M, K, N, float(sg), float(su), _p16(Y),
+                                        _pf(P) if P is not None else None)
+        if rc != 0:
+            raise RuntimeError("oracle_swiglu_fp8 failed with code %d" % rc)
+        return (Y, P) if want_p else Y
 
     def silu_mul(self, Gb, Ub) -> np.ndarray:
         """Elementwise bf16_RNE(SiLU(g) * u) from bf16 Gate and Up."""
@@ -262,3 +295,11 @@ def unfused(A, W1, W2):
 
 def mlp(A, W1, W2, W3):
     return default().mlp(A, W1, W2, W3)
+
+
+def e4m3_to_f32(b) -> np.ndarray:
+    return default().e4m3_to_f32(b)
+
+
+def swiglu_fp8(A8, W1_8, W2_8, sg: float, su: float, want_p: bool = False):
+    return default().swiglu_fp8(A8, W1_8, W2_8, sg, su, want_p=want_p)

@@ -179,6 +179,77 @@ int oracle_unfused(const uint16_t *A, const uint16_t *W1, const uint16_t *W2,
     return 0;
 }
 
+/* ---- FP8 (E4M3) variant -------------------------------------------------
+ * The pages argue that quantised GEMMs (FP8) make SwiGLU's memory cost
+ * relatively larger (Summary, "Problem Statement") but give no scale
+ * convention.  This oracle takes the plainest reading: per-tensor scales,
+ * A = sA * A8, W1 = s1 * W1_8, W2 = s2 * W2_8, with A8, W1_8, W2_8 in the
+ * OCP FP8 E4M3 format (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * exponent field 0 is subnormal, no infinities, S.1111.111 is NaN).
+ *   1. decode each byte exactly to fp32;
+ *   2. g = sum_k a8*w1_8, u = sum_k a8*w2_8 in fp32, k increasing (every
+ *      product of two E4M3 values is exact in fp32);
+ *   3. G = g * sg, U = u * su in fp32, with sg = fp32(sA*s1), su = fp32(sA*s2)
+ *      computed by the caller;
+ *   4.-5. Y = RNE_bf16(SiLU(G) * U) as in the bf16 product. */
+float oracle_e4m3_to_f32(uint8_t b) {
+    const int sign = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    float v;
+    if (e == 15 && m == 7) {
+        v = NAN;
+    } else if (e == 0) {
+        v = ldexpf((float)m, -9);                  /* m/8 * 2^(1-7) */
+    } else {
+        v = ldexpf((float)(8 + m), e - 7 - 3);     /* (1 + m/8) * 2^(e-7) */
+    }
+    return sign ? -v : v;
+}
+
+int oracle_swiglu_fp8(const uint8_t *A, const uint8_t *W1, const uint8_t *W2,
+                      int64_t M, int64_t K, int64_t N, float sg, float su,
+                      uint16_t *Y, float *P) {
+    if (M < 0 || K < 0 || N < 0) return 1;
+    if (M == 0 || N == 0) return 0;
+    float table[256];
+    for (int t = 0; t < 256; ++t) table[t] = oracle_e4m3_to_f32((uint8_t)t);
+    int err = 0;
+#pragma omp parallel
+    {
+        float *g = (float *)malloc(sizeof(float) * (size_t)N);
+        float *u = (float *)malloc(sizeof(float) * (size_t)N);
+        if (!g || !u) {
+#pragma omp atomic write
+            err = 2;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t i = 0; i < M; ++i) {
+                for (int64_t j = 0; j < N; ++j) { g[j] = 0.0f; u[j] = 0.0f; }
+                for (int64_t k = 0; k < K; ++k) {
+                    const float a = table[A[i * K + k]];
+                    const uint8_t *w1 = W1 + k * N;
+                    const uint8_t *w2 = W2 + k * N;
+                    for (int64_t j = 0; j < N; ++j) {
+                        const float pg = a * table[w1[j]];
+                        const float pu = a * table[w2[j]];
+                        g[j] = g[j] + pg;
+                        u[j] = u[j] + pu;
+                    }
+                }
+                for (int64_t j = 0; j < N; ++j) {
+                    const float G = g[j] * sg;
+                    const float U = u[j] * su;
+                    const float p = oracle_silu(G) * U;
+                    Y[i * N + j] = oracle_bf16_rne(p);
+                    if (P) P[i * N + j] = p;
+                }
+            }
+        }
+        free(g);
+        free(u);
+    }
+    return err;
+}
+
 /* ---- array forms of steps 3 and 5 (for the tests) ----------------------- */
 void oracle_bf16_rne_array(const float *p, uint16_t *y, int64_t n) {
     for (int64_t t = 0; t < n; ++t) y[t] = oracle_bf16_rne(p[t]);

@@ -15,6 +15,7 @@ from __future__ import annotations
 from dataclasses import dataclass, field
 from typing import Dict, List, Tuple
 
+import numpy as np
 import torch
 
 
@@ -106,6 +107,30 @@ def integer_case(M: int, K: int, N: int, seed: int, a_vals=(1, 2, 3), w1_vals=(1
         return v[idx].to(torch.bfloat16)
 
     return pick((M, K), a_vals), pick((K, N), w1_vals), pick((K, N), w2_vals)
+
+
+def quantize_e4m3(t: torch.Tensor):
+    """Per-tensor FP8 E4M3 quantisation: scale = amax / 448 (the largest finite
+    E4M3 value), bytes = E4M3(t / scale) with torch's round-to-nearest-even
+    conversion.  Returns (uint8 tensor of E4M3 bytes, scale as a Python float
+    that is exactly an fp32 value)."""
+    amax = float(t.float().abs().max()) if t.numel() else 0.0
+    scale = float(np.float32(amax / 448.0)) if amax > 0 else 1.0
+    q = (t.float() / scale).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).contiguous(), scale
+
+
+def fp8_case(M: int, K: int, N: int, seed: int):
+    """The seeded Gaussian case quantised per tensor: (A8, W1_8, W2_8, sg, su)
+    with sg = fp32(sA * s1) and su = fp32(sA * s2), the scale products both
+    sides apply to the fp32 Gate and Up sums."""
+    A, W1, W2 = gaussian_case(M, K, N, seed)
+    A8, sa = quantize_e4m3(A)
+    W18, s1 = quantize_e4m3(W1)
+    W28, s2 = quantize_e4m3(W2)
+    sg = float(np.float32(sa) * np.float32(s1))
+    su = float(np.float32(sa) * np.float32(s2))
+    return A8, W18, W28, sg, su
 
 
 def as_bits(t: torch.Tensor):

@@ -343,6 +343,89 @@ def test_activation_before_reduction_matters(orc):
 
 
 # ---------------------------------------------------------------------------
+# FP8 (E4M3) variant with per-tensor scales
+# ---------------------------------------------------------------------------
+
+def test_e4m3_decode_matches_library(orc):
+    """Every one of the 256 E4M3 codes decodes like torch's float8_e4m3fn
+    (an independent implementation of the OCP format): sign, bias-7 exponent,
+    subnormals, the maximum 448, the NaN codes and -0."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = orc.e4m3_to_f32(codes)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok].view(np.uint32), want[ok].view(np.uint32))
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+    assert np.signbit(got[0x80]) and got[0x80] == 0.0
+
+
+def fp8_bound_check(orc, A8, W18, W28, sg, su, Y):
+    """The fp32 sums, the scale multiplies, SiLU, the product and the bf16
+    rounding, each within its closed-form bound of the fp64 value."""
+    a = orc.e4m3_to_f32(A8).astype(np.float64)
+    w1 = orc.e4m3_to_f32(W18).astype(np.float64)
+    w2 = orc.e4m3_to_f32(W28).astype(np.float64)
+    K = a.shape[1]
+    G64, U64 = sg * (a @ w1), su * (a @ w2)
+    dG = sg * gamma(max(K - 1, 0)) * (np.abs(a) @ np.abs(w1))
+    dU = su * gamma(max(K - 1, 0)) * (np.abs(a) @ np.abs(w2))
+    dG = dG + U32 * (np.abs(G64) + dG) + 1e-300
+    dU = dU + U32 * (np.abs(U64) + dU) + 1e-300
+    s64 = silu64(G64)
+    y64 = s64 * U64
+    E = (1.0999 * dG + 8 * U32 * np.abs(s64)) * (np.abs(U64) + dU) + np.abs(s64) * dU \
+        + 2 * U32 * np.abs(y64) + 1e-38
+    y = f32(Y).astype(np.float64)
+    lim = 2.0 ** -8 * (np.abs(y64) + E) + E + 1e-38
+    bad = np.argwhere(np.abs(y - y64) > lim)
+    assert bad.size == 0, "FP8 Y outside the bound at %s" % bad[:3].tolist()
+
+
+def test_fp8_bruteforce_bound(orc):
+    for idx, (m, k, n) in enumerate([(1, 1, 1), (3, 16, 7), (7, 64, 33), (16, 257, 16), (33, 100, 9)]):
+        A8, W18, W28, sg, su = inputs.fp8_case(m, k, n, seed=50 + idx)
+        Y, P = orc.swiglu_fp8(A8, W18, W28, sg, su, want_p=True)
+        fp8_bound_check(orc, A8, W18, W28, sg, su, Y)
+        assert np.array_equal(orc.bf16_rne(P), Y)
+
+
+def test_fp8_exact_regime(orc):
+    """Positive E4M3 integers 1..4 with unit scales: Gate and Up are exact
+    integers >= 17, so SiLU(Gate) == Gate in fp32 and Y = RNE_bf16(fp32(G*U)),
+    built here from Python integers."""
+    rng = np.random.default_rng(7)
+    codes = np.array([0x38, 0x40, 0x44, 0x48], dtype=np.uint8)     # 1, 2, 3, 4
+    M, K, N = 5, 48, 11
+    A8 = codes[rng.integers(0, 4, (M, K))]
+    W18 = codes[rng.integers(0, 4, (K, N))]
+    W28 = codes[rng.integers(0, 4, (K, N))]
+    val = {0x38: 1, 0x40: 2, 0x44: 3, 0x48: 4}
+    a = np.vectorize(val.get)(A8).astype(np.int64)
+    g = a @ np.vectorize(val.get)(W18).astype(np.int64)
+    u = a @ np.vectorize(val.get)(W28).astype(np.int64)
+    assert g.min() >= 17
+    want = bits(torch.from_numpy((g * u).astype(np.float64)).float().to(torch.bfloat16))
+    assert np.array_equal(orc.swiglu_fp8(A8, W18, W28, 1.0, 1.0), want)
+
+
+def test_fp8_scale_and_zero_invariants(orc):
+    A8, W18, W28, sg, su = inputs.fp8_case(6, 96, 40, seed=61)
+    Y = orc.swiglu_fp8(A8, W18, W28, sg, su)
+    # doubling the Up scale doubles every output exactly (a power of two)
+    assert np.array_equal(f32(orc.swiglu_fp8(A8, W18, W28, sg, 2 * su)), 2 * f32(Y))
+    # zero Gate weights give SiLU(0) * Up = 0
+    assert np.all(f32(orc.swiglu_fp8(A8, np.zeros_like(W18), W28, sg, su)) == 0)
+    # the bytes are the E4M3 values the oracle decodes: swapping in the decoded
+    # bf16 values (exact in bf16) with the scales folded into W1, W2 is not
+    # exact, but with unit scales the bf16 product of the decoded values is
+    a16 = bits(torch.from_numpy(orc.e4m3_to_f32(A8)).to(torch.bfloat16))
+    w1 = bits(torch.from_numpy(orc.e4m3_to_f32(W18)).to(torch.bfloat16))
+    w2 = bits(torch.from_numpy(orc.e4m3_to_f32(W28)).to(torch.bfloat16))
+    assert np.array_equal(orc.swiglu_fp8(A8, W18, W28, 1.0, 1.0), orc.swiglu(a16, w1, w2))
+
+
+# ---------------------------------------------------------------------------
 # Gated MLP block: SwiGLU product, then the down projection Z = Y x W3
 # ---------------------------------------------------------------------------
 

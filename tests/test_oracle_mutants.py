@@ -37,6 +37,14 @@ MUTANTS = {
                           "for (int64_t k = K - 1; k >= 0; --k) {\n            const float a")],
     "unfused_skips_gate_rounding": [("oracle_silu(bf16_to_f32(Gb[t]))",
                                      "oracle_silu(bf16_to_f32(Gb[t]) + 0x1p-9f * bf16_to_f32(Gb[t]))")],
+    # FP8 variant
+    "e4m3_exponent_bias_8": [("e - 7 - 3", "e - 8 - 3")],
+    "e4m3_subnormal_scale": [("ldexpf((float)m, -9)", "ldexpf((float)m, -10)")],
+    "e4m3_nan_codes_wrong": [("e == 15 && m == 7", "e == 15")],
+    "fp8_scales_swapped": [("const float G = g[j] * sg;\n                    const float U = u[j] * su;",
+                            "const float G = g[j] * su;\n                    const float U = u[j] * sg;")],
+    "fp8_up_scale_dropped": [("const float U = u[j] * su;", "const float U = u[j];")],
+    "fp8_gate_uses_w2": [("const float pg = a * table[w1[j]];", "const float pg = a * table[w2[j]];")],
 }
 
 CHECKS = [
@@ -50,6 +58,10 @@ CHECKS = [
     ("integer", lambda o: T.check_integer_regime(o)),
     ("invariants", lambda o: T.check_invariants(o)),
     ("unfused", lambda o: T.check_unfused(o)),
+    ("e4m3", lambda o: T.test_e4m3_decode_matches_library(o)),
+    ("fp8_bound", lambda o: T.test_fp8_bruteforce_bound(o)),
+    ("fp8_exact", lambda o: T.test_fp8_exact_regime(o)),
+    ("fp8_invariants", lambda o: T.test_fp8_scale_and_zero_invariants(o)),
 ]
 
 
