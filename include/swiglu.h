@@ -175,6 +175,39 @@ swiglu_status swiglu_fused_packed(const swiglu_bf16 *A, const swiglu_bf16 *Wp,
 int swiglu_choose_variant(int64_t M, int64_t K, int64_t N);
 
 /* ------------------------------------------------------------------------
+ * FP8 operands.  The pages note that quantised GEMMs (FP8, INT4) raise the
+ * relative cost of SwiGLU's memory traffic ([Summary: Problem Statement]) but
+ * give no scale convention; this library takes per-tensor scales:
+ * A = sA * A8, W1 = s1 * W1_8, W2 = s2 * W2_8, with A8, W1_8, W2_8 in the
+ * OCP FP8 E4M3 format (raw bytes, row-major), and computes
+ *   Gate = fp32(sum_k a8 w1_8) * sg,  Up = fp32(sum_k a8 w2_8) * su,
+ *   Y = bf16_RNE(SiLU(Gate) * Up)
+ * with the caller's sg = fp32(sA * s1), su = fp32(sA * s2), on
+ * v_mfma_f32_32x32x64_f8f6f4 (fp32 accumulation).
+ *
+ * swiglu_packed_bytes_fp8: bytes of the packed FP8 weights (0 for an invalid
+ *   or unsupported shape): one 32 KiB block per 128 output columns and 128 k,
+ *   [32-row block rb][64-k step][lane][32 bytes] holding packed row
+ *   rb*32 + (lane & 31) (rows 0-127 W1, 128-255 W2 columns of the tile) at
+ *   k = 64*step + 32*(lane >> 5) + 0..31; padding is zero.
+ * swiglu_pack_weights_fp8: W1_8, W2_8 [K,N] bytes -> that layout.
+ * swiglu_fused_packed_fp8: Y[M,N] bf16 from A8 [M,K] and the packed weights
+ *   on the data-parallel streaming schedule (no workspace, any M >= 0).
+ * Shapes: K a multiple of 16 and N a multiple of 8 (else
+ * SWIGLU_ERR_UNSUPPORTED_SHAPE); pointers 16-byte aligned; Y must not
+ * overlap A8 or the packed weights; validation codes return before any
+ * launch; work is enqueued on `stream` with no synchronisation.
+ * ---------------------------------------------------------------------- */
+size_t swiglu_packed_bytes_fp8(int64_t K, int64_t N);
+swiglu_status swiglu_pack_weights_fp8(const uint8_t *W1, const uint8_t *W2,
+                                      uint8_t *Wp, int64_t K, int64_t N,
+                                      void *stream);
+swiglu_status swiglu_fused_packed_fp8(const uint8_t *A, const uint8_t *Wp,
+                                      swiglu_bf16 *Y, int64_t M, int64_t K,
+                                      int64_t N, float sg, float su,
+                                      void *stream);
+
+/* ------------------------------------------------------------------------
  * Column-granular interleaved weights: the pages' W_fused with Gate in the
  * even and Up in the odd columns ([Summary: Methodology], Kernel-2 "Fusion").
  * Same block structure and size as the per-tile pack above (one 32 KiB block

@@ -45,6 +45,9 @@ SIGNATURES = {
     "swiglu_fused_packed": ([_P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, ctypes.c_int, _P],
                             ctypes.c_int),
     "swiglu_choose_variant": ([_I64, _I64, _I64], ctypes.c_int),
+    "swiglu_packed_bytes_fp8": ([_I64, _I64], ctypes.c_size_t),
+    "swiglu_pack_weights_fp8": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
+    "swiglu_fused_packed_fp8": ([_P, _P, _P, _I64, _I64, _I64, ctypes.c_float, ctypes.c_float, _P], ctypes.c_int),
     "swiglu_pack_weights_interleaved": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
     "swiglu_unpack_weights_interleaved": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
     "swiglu_fused_packed_interleaved": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
@@ -182,6 +185,42 @@ def swiglu_unpack_weights(Wp: torch.Tensor, K: int, N: int, stream=None):
                                      K, N, _stream(stream))
     _check("swiglu_unpack_weights", st)
     return W1, W2
+
+
+def _dev_u8(t: torch.Tensor, name: str) -> int:
+    if isinstance(t, torch.Tensor) and t.is_cuda and t.dtype is torch.uint8 and t.is_contiguous():
+        return t.data_ptr()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if t.dtype != torch.uint8:
+        raise TypeError("%s must be uint8 FP8 E4M3 bytes (got %s)" % (name, t.dtype))
+    raise ValueError("%s must be contiguous" % name)
+
+
+def swiglu_pack_weights_fp8(W1: torch.Tensor, W2: torch.Tensor, stream=None) -> torch.Tensor:
+    """Pack FP8 E4M3 weight bytes W1, W2 [K,N] (uint8) for swiglu_fused_packed_fp8."""
+    K, N = W1.shape
+    nbytes = int(lib().swiglu_packed_bytes_fp8(K, N))
+    if nbytes == 0:
+        raise ValueError("invalid FP8 weight shape [%d,%d] (K must be a multiple of 16)" % (K, N))
+    Wp = torch.empty(nbytes, dtype=torch.uint8, device=W1.device)
+    st = lib().swiglu_pack_weights_fp8(_dev_u8(W1, "W1"), _dev_u8(W2, "W2"), _dev_u8(Wp, "Wp"), K, N,
+                                       _stream(stream))
+    _check("swiglu_pack_weights_fp8", st)
+    return Wp
+
+
+def swiglu_fused_packed_fp8(A8: torch.Tensor, Wp: torch.Tensor, N: int, sg: float, su: float,
+                            Y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y = bf16(SiLU(sg * A8 W1_8) * (su * A8 W2_8)) from FP8 E4M3 bytes."""
+    M, K = A8.shape
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=A8.device) if Y is None else Y
+    st = lib().swiglu_fused_packed_fp8(_dev_u8(A8, "A8"), _dev_u8(Wp, "Wp"), _dev_bf16(Y, "Y"), M, K, N,
+                                       float(sg), float(su), _stream(stream))
+    _check("swiglu_fused_packed_fp8", st)
+    return Y
 
 
 def swiglu_pack_weights_interleaved(W1: torch.Tensor, W2: torch.Tensor, Wp: torch.Tensor | None = None,

@@ -42,6 +42,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 64;             // K depth of one LDS stage (one 128-byte row)
@@ -141,6 +143,7 @@ struct FusedArgs {
     int panels;           // > 0: panel schedule over this many 32-column weight panels
                           // (streaming kernel, one row tile): work item w takes
                           // panels [w*panels/total, (w+1)*panels/total), one per wave
+    float sg, su;         // FP8 operands: scale products applied to the Gate and Up sums
 };
 
 // ---------------------------------------------------------------------------
@@ -880,10 +883,18 @@ constexpr int stream_smem_elems() {
 // next tile's first two stages are issued before the epilogue of the
 // current one, and its Y stores are left in flight while the next tile's K
 // loop starts.
-template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false, bool IL = false>
+// F8: FP8 E4M3 activations and packed weights (per-tensor scale products
+// p.sg, p.su applied to the fp32 sums): a stage is 128 k (the same 128-byte
+// activation rows), each 32-row block takes one v_mfma_f32_32x32x64_f8f6f4
+// per 64 k, and a sub-step covers one 64-k step for half of the row blocks.
+template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false, bool IL = false, bool F8 = false>
 __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_t* smem, int first, int stride,
                                                      int total) {
     static_assert(!(IL && SPLIT), "the interleaved layout has no split-K schedule");
+    static_assert(!(F8 && (IL || SPLIT)), "FP8 operands: per-tile layout, data-parallel only");
+    constexpr int EB = F8 ? 1 : 2;              // bytes per operand element
+    constexpr int KSTAGE = F8 ? 128 : BK;       // k per stage (128-byte activation rows)
+    constexpr int CE = 16 / EB;                 // elements per 16-byte chunk
     constexpr int NW = 4;                       // waves, 32 output columns each
     constexpr int TM = BM / 32;                 // 32-row MFMA tiles per wave
     constexpr int A_INS = BM / 8 / NW;          // 1 KiB direct loads per wave per stage
@@ -978,11 +989,17 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
         for (int i = 0; i < A_INS; ++i) {
             const int r = (wave * A_INS + i) * 8 + (ll >> 3);
             const int c = (ll & 7) ^ swz(r);
-            a_off[i] = (uint32_t)(((size_t)min(it.m0 + r, M - 1) * K + 8 * c) * 2);
+            a_off[i] = (uint32_t)((size_t)min(it.m0 + r, M - 1) * K * EB + 16 * c);
         }
         chunk_x = ((ll & 7) ^ (ll >> 3)) & 7;
         const int wq = it.n0 / 32 + wave;
-        w_off = (uint32_t)((((wq & 3) * (IL ? 4 : 2) + ((ll >> 4) & 1)) * 1024 + (ll >> 5) * 128 + (ll & 15) * 8) * 2);
+        if constexpr (F8)
+            // FP8 block: [32-row block rb][64-k step][lane][32 bytes]; Gate
+            // block wq & 3, Up block 4 + (wq & 3)
+            w_off = (uint32_t)((wq & 3) * 4096 + ll * 32);
+        else
+            w_off = (uint32_t)((((wq & 3) * (IL ? 4 : 2) + ((ll >> 4) & 1)) * 1024 + (ll >> 5) * 128 +
+                                (ll & 15) * 8) * 2);
         w_tile = reinterpret_cast<const char*>(p.W1) + (size_t)(wq >> 2) * KB * (PACK_ROWS * PACK_BK * 2);
         ld_kb_first = it.kb_first;
         ld_ns = valid ? it.ns : 0;
@@ -999,8 +1016,17 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
         asm volatile("" : "+v"(lr));
         const int lrow = lr & 31;
         const int hs = (lr >> 5) ^ swz(lrow);
+        if constexpr (F8) {
+            // a 32-byte fragment is logical chunks 4ks + 2(l >> 5) + e, e = 0, 1:
+            // physical chunk (2(l >> 5) ^ swz) ^ x with x = 4(ks ^ (i & 1)) + e
+            const int hs8 = (2 * (lr >> 5)) ^ swz(lrow);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) rd_base[x] = (uint32_t)((lrow * BK + ((hs ^ (2 * x)) << 3)) * 2);
+            for (int j = 0; j < 4; ++j)
+                rd_base[j] = (uint32_t)(lrow * 128 + ((hs8 ^ (4 * (j >> 1) + (j & 1))) << 4));
+        } else {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) rd_base[x] = (uint32_t)((lrow * BK + ((hs ^ (2 * x)) << 3)) * 2);
+        }
     };
 
     f32x16 acc[2][TM][1];
@@ -1014,6 +1040,7 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
     };
     zero_acc();
     bf16x8 fa[2][TM];
+    i32x8 fa8[2][TM / 2 > 0 ? TM / 2 : 1];
     bf16x8 wf[NBUF][2][4];
     // every register set defined on every path into the stage loop
 #pragma unroll
@@ -1035,6 +1062,16 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
         fa[set][i] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(smem) + so + i * 4096 +
                                                       rd_base[kk ^ (2 * (i & 1))]);
     };
+    // FP8: the fragment of sub-step q (64-k step q >> 1, row blocks
+    // (q & 1) * TM/2 + ii) into fa8[set][ii]
+    auto read_a8 = [&](uint32_t so, int q, int ii, int set) {
+        const int i = (q & 1) * (TM / 2) + ii;
+        const char* b = reinterpret_cast<const char*>(smem) + so + i * 4096;
+        const int j = 2 * ((q >> 1) ^ (i & 1));
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(b + rd_base[j]);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(b + rd_base[j + 1]);
+        fa8[set][ii] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
     // Stages past the last (ls >= ld_ns) are issued like any other, but every
     // lane then reads the 16-byte zero chunk (a single cache line): the
     // stage code stays the same for every stage, with no tail variants.
@@ -1049,19 +1086,19 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
         const bool valid = ls < (j < A_INS ? ld_ns : ld_ns_w);
         const uint32_t keep = valid ? 0xffffffffu : 0u;
         if (j < A_INS) {
-            const int k0 = (ld_kb_first + ls) * BK;
-            const char* base = valid ? reinterpret_cast<const char*>(p.A) + (size_t)k0 * 2
+            const int k0 = (ld_kb_first + ls) * KSTAGE;
+            const char* base = valid ? reinterpret_cast<const char*>(p.A) + (size_t)k0 * EB
                                      : reinterpret_cast<const char*>(g_zero_chunk);
             const uint16_t* src = reinterpret_cast<const uint16_t*>(base + (a_off[j] & keep));
             if constexpr (RAGGED) {
-                if (k0 + 8 * (chunk_x ^ ((wave * A_INS + j) & 7)) >= K) src = g_zero_chunk;
+                if (k0 + CE * (chunk_x ^ ((wave * A_INS + j) & 7)) >= K) src = g_zero_chunk;
             }
             dma16(src, smem + buf * ASTAGE + (wave * A_INS + j) * 512);
         } else {
             const int t = (j - A_INS) >> 2, kk = (j - A_INS) & 3;
             const char* base = valid ? w_tile + (size_t)(ld_kb_first + ls) * (PACK_ROWS * PACK_BK * 2) +
                                            t * (IL ? 4096 : 16384) +
-                                           (kk >> 1) * 1024 + (kk & 1) * 512
+                                           (kk >> 1) * (F8 ? 2048 : 1024) + (kk & 1) * (F8 ? 16 : 512)
                                      : reinterpret_cast<const char*>(g_zero_chunk);
             wf[SET][t][kk] = *reinterpret_cast<const bf16x8*>(base + (w_off & keep));
         }
@@ -1086,6 +1123,33 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
         // the previous one: wait for them here, before any new read, so no
         // later wait in this sub-step has to cover the new reads
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+        if constexpr (F8) {
+            // sub-step kk: 64-k step kk >> 1 on row blocks (kk & 1) * TM/2 + ii;
+            // the weight fragment is the register pieces 2ks, 2ks + 1
+            constexpr int TH = TM / 2;
+            constexpr int LPI8 = (LPS + TH - 1) / TH;
+            const int ks = kk >> 1;
+#pragma unroll
+            for (int ii = 0; ii < TH; ++ii) {
+                const int i = (kk & 1) * TH + ii;
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const i32x8 wv = __builtin_shufflevector(__builtin_bit_cast(i32x4, wf[WS][g][2 * ks]),
+                                                             __builtin_bit_cast(i32x4, wf[WS][g][2 * ks + 1]),
+                                                             0, 1, 2, 3, 4, 5, 6, 7);
+                    acc[g][i][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, fa8[cur][ii], acc[g][i][0],
+                                                                                   0, 0, 0, 0, 0, 0);
+                }
+                if constexpr (RD) read_a8(rso, rkk, ii, cur ^ 1);
+                if constexpr (LD) {
+#pragma unroll
+                    for (int j = ii * LPI8; j < (ii + 1) * LPI8; ++j)
+                        if (j < LPS) issue_one(lq * LPS + j, ls, lbuf, lsetc);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             acc[0][i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[WS][0][kk], fa[cur][i], acc[0][i][0], 0, 0, 0);
@@ -1162,7 +1226,10 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(A_INS, 0));
     __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int i = 0; i < TM; ++i) read_a(0u, 0, i, 0);
+    for (int i = 0; i < (F8 ? TM / 2 : TM); ++i) {
+        if constexpr (F8) read_a8(0u, 0, i, 0);
+        else read_a(0u, 0, i, 0);
+    }
 
     for (int w = first;;) {
         const int ns = cur.ns;
@@ -1241,7 +1308,14 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
                 for (int q = 0; q < 4; ++q) {
                     float v[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = silu_f(acc[0][i][0][4 * q + e]) * acc[1][i][0][4 * q + e];
+                    for (int e = 0; e < 4; ++e) {
+                        float gv = acc[0][i][0][4 * q + e], uv = acc[1][i][0][4 * q + e];
+                        if constexpr (F8) {
+                            gv *= p.sg;
+                            uv *= p.su;
+                        }
+                        v[e] = silu_f(gv) * uv;
+                    }
                     u32x2 out;
                     out[0] = pack2(v[0], v[1]);
                     out[1] = pack2(v[2], v[3]);
@@ -1284,7 +1358,10 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
         w = wn;
         set_rd_base();
 #pragma unroll
-        for (int i = 0; i < TM; ++i) read_a(0u, 0, i, 0);
+        for (int i = 0; i < (F8 ? TM / 2 : TM); ++i) {
+            if constexpr (F8) read_a8(0u, 0, i, 0);
+            else read_a(0u, 0, i, 0);
+        }
     }
     // the zero-chunk loads of the stages past the last item are in flight
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
@@ -1296,28 +1373,28 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
             for (int kk = 0; kk < 4; ++kk) asm volatile("" ::"v"(wf[q][t][kk]));
 }
 
-template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false, bool IL = false>
+template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false, bool IL = false, bool F8 = false>
 __global__ __launch_bounds__(256) void stream_prefill_kernel(FusedArgs p, int total) {
     static_assert(!PANELS || (BM == 128 && !SPLIT), "panel schedule: one 128-row tile, data-parallel");
     __shared__ __attribute__((aligned(16))) uint16_t smem[stream_smem_elems<BM>()];
-    stream_prefill_tiles<BM, SPLIT, RAGGED, PANELS, IL>(p, smem, blockIdx.x, gridDim.x, total);
+    stream_prefill_tiles<BM, SPLIT, RAGGED, PANELS, IL, F8>(p, smem, blockIdx.x, gridDim.x, total);
 }
 
 // The 256-row tiles and the 128-row tail column tiles in one launch: blocks
 // 0 .. n_pers-1 work through the n_big 256-row tiles of `big` (block b takes
 // tiles b, b + n_pers, ...), the remaining blocks take one 128-row tile of
 // `tail` each and start on CUs as the 256-row work drains.
-template <bool RAGGED, bool IL = false>
+template <bool RAGGED, bool IL = false, bool F8 = false>
 __global__ __launch_bounds__(256) void stream_prefill_mixed_kernel(FusedArgs big, FusedArgs tail, int n_pers,
                                                                    int n_big) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[stream_smem_elems<256>()];
     static_assert(stream_smem_elems<256>() >= stream_smem_elems<128>(), "one LDS block serves both tiles");
     const int b = blockIdx.x;
     if (b < n_pers) {
-        stream_prefill_tiles<256, false, RAGGED, false, IL>(big, smem, b, n_pers, n_big);
+        stream_prefill_tiles<256, false, RAGGED, false, IL, F8>(big, smem, b, n_pers, n_big);
     } else {
         const int n_tail = gridDim.x - n_pers;
-        stream_prefill_tiles<128, false, RAGGED, false, IL>(tail, smem, b - n_pers, n_tail, n_tail);
+        stream_prefill_tiles<128, false, RAGGED, false, IL, F8>(tail, smem, b - n_pers, n_tail, n_tail);
     }
 }
 
@@ -1523,6 +1600,38 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint16_t* __restrict_
         const int k = c.k0 + i;
         if (k < K) W[(size_t)k * N + c.n] = (uint16_t)((in[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
     }
+}
+
+// ---------------------------------------------------------------------------
+// FP8 weight pack: per (128-column tile jt, 128-k block kb) one 32 KiB block
+// [32-row block rb][64-k step ks][lane][32 bytes], holding packed row
+// rb*32 + (lane & 31) (rows 0-127: W1 column jt*128 + row, 128-255: W2 column
+// jt*128 + row - 128) at k = kb*128 + ks*64 + 32*(lane >> 5) + 0..31, the lane
+// order of a v_mfma_f32_32x32x64_f8f6f4 operand.  Padding is zero.  One
+// thread per 16-byte piece (piece index = byte offset / 16).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_fp8_kernel(const uint8_t* __restrict__ W1,
+                                                       const uint8_t* __restrict__ W2,
+                                                       uint8_t* __restrict__ Wp, int K, int N, int KB,
+                                                       long long npieces) {
+    const long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= npieces) return;
+    const long long blk = q >> 11;
+    const int within = (int)(q & 2047);
+    const int rb = within >> 8, ks = (within >> 7) & 1, lane = (within >> 1) & 63, half = within & 1;
+    const int kb = (int)(blk % KB), jt = (int)(blk / KB);
+    const int prow = rb * 32 + (lane & 31);
+    const bool up = prow >= PACK_BN;
+    const int n = jt * PACK_BN + (up ? prow - PACK_BN : prow);
+    const int k0 = kb * 128 + ks * 64 + 32 * (lane >> 5) + 16 * half;
+    const uint8_t* W = up ? W2 : W1;
+    u32x4 out = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const unsigned v = (n < N && k0 + i < K) ? W[(size_t)(k0 + i) * N + n] : 0u;
+        out[i >> 2] |= v << (8 * (i & 3));
+    }
+    *reinterpret_cast<u32x4*>(Wp + q * 16) = out;
 }
 
 // ---------------------------------------------------------------------------

@@ -68,6 +68,16 @@ swiglu_status check_shape(int64_t M, int64_t K, int64_t N) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// FP8 operands: K a multiple of 16 (16-byte activation rows), packed weights
+// in 32 KiB blocks per (128 columns, 128 k)
+swiglu_status check_shape_fp8(int64_t M, int64_t K, int64_t N) {
+    const swiglu_status st = check_shape(M, K, N);
+    if (st != SWIGLU_OK) return st;
+    return (K % 16) != 0 ? SWIGLU_ERR_UNSUPPORTED_SHAPE : SWIGLU_OK;
+}
+
+int64_t packed_bytes_fp8(int64_t K, int64_t N) { return ceil_div(N, swk::PACK_BN) * ceil_div(K, 128) * 32768; }
+
 int64_t packed_elems(int64_t K, int64_t N) {
     return ceil_div(N, swk::PACK_BN) * ceil_div(K, swk::PACK_BK) * swk::PACK_ROWS * swk::PACK_BK;
 }
@@ -235,11 +245,12 @@ hipError_t launch_prefill(const swk::FusedArgs& a, int grid, hipStream_t s) {
 
 // `total` work items (tiles, or tile x K split) on `grid` <= total workgroups;
 // each workgroup takes items b, b + grid, ...
-template <int BM, bool SPLIT, bool PANELS = false, bool IL = false>
+template <int BM, bool SPLIT, bool PANELS = false, bool IL = false, bool F8 = false>
 hipError_t launch_stream(const swk::FusedArgs& a, int total, int grid, hipStream_t s) {
-    const void* fn = (a.K % swk::BK) != 0
-                         ? reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, true, PANELS, IL>)
-                         : reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, false, PANELS, IL>);
+    const bool ragged = (a.K % (F8 ? 128 : swk::BK)) != 0;
+    const void* fn = ragged
+                         ? reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, true, PANELS, IL, F8>)
+                         : reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, false, PANELS, IL, F8>);
     swk::FusedArgs args = a;
     void* kargs[] = {&args, &total};
     return hipLaunchKernel(fn, dim3(grid), dim3(256), kargs, 0, s);
@@ -247,7 +258,7 @@ hipError_t launch_stream(const swk::FusedArgs& a, int total, int grid, hipStream
 
 // The data-parallel streaming schedules (128- or 256-row tiles, the panel
 // schedule, the mixed 256/128-row launch) on either weight layout.
-template <bool IL>
+template <bool IL, bool F8 = false>
 hipError_t launch_stream_dp(const swk::FusedArgs& a, const Plan& p, hipStream_t s) {
     const int grid = p.tiles;
     if (p.t.BM == 128) {
@@ -255,12 +266,12 @@ hipError_t launch_stream_dp(const swk::FusedArgs& a, const Plan& p, hipStream_t 
             swk::FusedArgs pa = a;
             pa.panels = p.panels;
             const int g = std::min(p.panels, p.cus);
-            return launch_stream<128, false, true, IL>(pa, g, g, s);
+            return launch_stream<128, false, true, IL, F8>(pa, g, g, s);
         }
-        return launch_stream<128, false, false, IL>(a, grid, grid, s);
+        return launch_stream<128, false, false, IL, F8>(a, grid, grid, s);
     }
     // one workgroup per CU works through the 256-row tiles
-    if (p.tail_ntiles == 0) return launch_stream<256, false, false, IL>(a, grid, std::min(grid, p.cus), s);
+    if (p.tail_ntiles == 0) return launch_stream<256, false, false, IL, F8>(a, grid, std::min(grid, p.cus), s);
     // one launch: the 256-row tiles of the first column tiles, then
     // the last tail_ntiles column tiles as 128-row tiles
     swk::FusedArgs big = a, tail = a;
@@ -271,9 +282,10 @@ hipError_t launch_stream_dp(const swk::FusedArgs& a, const Plan& p, hipStream_t 
     int n_big = big.tiles_m * big.tiles_n;
     int n_pers = std::min(n_big, p.cus);
     const int grid_all = n_pers + tail.tiles_m * tail.tiles_n;
-    const void* fn = (a.K % swk::BK) != 0
-                         ? reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<true, IL>)
-                         : reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<false, IL>);
+    const bool ragged = (a.K % (F8 ? 128 : swk::BK)) != 0;
+    const void* fn = ragged
+                         ? reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<true, IL, F8>)
+                         : reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<false, IL, F8>);
     void* kargs[] = {&big, &tail, &n_pers, &n_big};
     return hipLaunchKernel(fn, dim3(grid_all), dim3(256), kargs, 0, s);
 }
@@ -443,6 +455,52 @@ swiglu_status swiglu_fused_packed_interleaved(const swiglu_bf16* A, const swiglu
     a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n;
     a.splits = 1; a.kb_per_split = p.KB; a.KB = p.KB;
     const hipError_t e = launch_stream_dp<true>(a, p, (hipStream_t)stream);
+    return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
+}
+
+size_t swiglu_packed_bytes_fp8(int64_t K, int64_t N) {
+    if (check_shape_fp8(0, K, N) != SWIGLU_OK) return 0;
+    return (size_t)packed_bytes_fp8(K, N);
+}
+
+swiglu_status swiglu_pack_weights_fp8(const uint8_t* W1, const uint8_t* W2, uint8_t* Wp, int64_t K, int64_t N,
+                                      void* stream) {
+    swiglu_status st = check_shape_fp8(0, K, N);
+    if (st != SWIGLU_OK) return st;
+    if (!W1 || !W2 || !Wp) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(W1) || !aligned16(W2) || !aligned16(Wp)) return SWIGLU_ERR_MISALIGNED;
+    const Range out = range_of(Wp, packed_bytes_fp8(K, N));
+    if (overlap(out, range_of(W1, K * N)) || overlap(out, range_of(W2, K * N))) return SWIGLU_ERR_ALIASING;
+    const long long npieces = (long long)packed_bytes_fp8(K, N) / 16;
+    const int KB = (int)ceil_div(K, 128);
+    int Ki = (int)K, Ni = (int)N;
+    void* args[] = {(void*)&W1, (void*)&W2, (void*)&Wp, &Ki, &Ni, (void*)&KB, (void*)&npieces};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&swk::pack_fp8_kernel),
+                                   dim3((unsigned)ceil_div(npieces, 256)), dim3(256), args, 0, (hipStream_t)stream);
+    return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
+}
+
+swiglu_status swiglu_fused_packed_fp8(const uint8_t* A, const uint8_t* Wp, swiglu_bf16* Y, int64_t M, int64_t K,
+                                      int64_t N, float sg, float su, void* stream) {
+    swiglu_status st = check_shape_fp8(M, K, N);
+    if (st != SWIGLU_OK) return st;
+    if (M == 0) return SWIGLU_OK;
+    if (!A || !Wp || !Y) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(A) || !aligned16(Wp) || !aligned16(Y)) return SWIGLU_ERR_MISALIGNED;
+    const Range y = range_of(Y, M * N * 2);
+    if (overlap(y, range_of(A, M * K)) || overlap(y, range_of(Wp, packed_bytes_fp8(K, N))))
+        return SWIGLU_ERR_ALIASING;
+    const Plan p = stream_dp_plan(M, K, N, cu_count_now());
+    swk::FusedArgs a{};
+    a.A = reinterpret_cast<const uint16_t*>(A);
+    a.W1 = reinterpret_cast<const uint16_t*>(Wp);
+    a.W2 = nullptr; a.Y = Y;
+    a.M = (int)M; a.K = (int)K; a.N = (int)N;
+    a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n;
+    a.KB = (int)ceil_div(K, 128);
+    a.splits = 1; a.kb_per_split = a.KB;
+    a.sg = sg; a.su = su;
+    const hipError_t e = launch_stream_dp<false, true>(a, p, (hipStream_t)stream);
     return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
 }
 

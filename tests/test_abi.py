@@ -162,6 +162,24 @@ def test_interleaved_errors():
     assert F(A_, WP_, A_ + 16, 4, 64, 64, None) == ALIAS
 
 
+def test_fp8_errors():
+    L = sw.lib()
+    # one 32 KiB block per 128 columns and 128 k
+    assert L.swiglu_packed_bytes_fp8(896, 4864) == 38 * 7 * 32768
+    assert L.swiglu_packed_bytes_fp8(8, 64) == 0          # K not a multiple of 16
+    assert L.swiglu_packed_bytes_fp8(144, 136) == 2 * 2 * 32768
+    F = L.swiglu_fused_packed_fp8
+    assert F(None, None, None, 0, 64, 64, 1.0, 1.0, None) == OK
+    assert F(A_, WP_, Y_, 4, 72, 64, 1.0, 1.0, None) == UNSUP
+    assert F(A_, None, Y_, 4, 64, 64, 1.0, 1.0, None) == NULLP
+    assert F(A_ + 8, WP_, Y_, 4, 64, 64, 1.0, 1.0, None) == MISAL
+    assert F(A_, WP_, A_ + 128, 4, 64, 64, 1.0, 1.0, None) == ALIAS
+    P = L.swiglu_pack_weights_fp8
+    assert P(W1_, W2_, WP_, 72, 64, None) == UNSUP
+    assert P(W1_, None, WP_, 64, 64, None) == NULLP
+    assert P(W1_, W2_, W1_ + 16, 64, 64, None) == ALIAS
+
+
 def test_workspace_holds_fp32_partials():
     L = sw.lib()
     # split-K workspace = splits x M x 2N fp32 partial sums; zero for the

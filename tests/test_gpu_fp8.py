@@ -1,0 +1,92 @@
+"""GPU parity of the FP8 (E4M3, per-tensor scales) path against the oracle's
+swiglu_fp8, through the C ABI: the packed layout byte by byte, then the
+product on every streaming schedule (panel, 128-row tiles, persistent
+256-row tiles, the mixed 256/128-row launch) with ragged K and N, and
+sampled rows at the workload shapes.  Tolerance as everywhere:
+|y - ref| <= 1e-3 + 8e-3 |ref| (the sums differ only in fp32 order; every
+E4M3 product is exact in fp32)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import swiglu_gated_mlp_amd as sw
+from swiglu_gated_mlp_amd import inputs
+
+from _util import check_close, gpu_bits, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    sw.lib()
+    oracle.set_threads(16)
+    return torch.device("cuda:0")
+
+
+def test_fp8_pack_layout(dev):
+    for K, N in [(128, 128), (144, 136), (896, 520)]:
+        g = torch.Generator().manual_seed(K + N)
+        W1 = torch.randint(0, 256, (K, N), generator=g, dtype=torch.uint8)
+        W2 = torch.randint(0, 256, (K, N), generator=g, dtype=torch.uint8)
+        P = sw.swiglu_pack_weights_fp8(W1.to(dev), W2.to(dev)).cpu().numpy()
+        KB = (K + 127) // 128
+        assert P.size == ((N + 127) // 128) * KB * 32768
+
+        def pos(jt, kb, prow, k):
+            rb, r, ks, h, j = prow // 32, prow % 32, k // 64, (k % 64) // 32, k % 32
+            return (jt * KB + kb) * 32768 + ((rb * 2 + ks) * 64 + h * 32 + r) * 32 + j
+
+        w1, w2 = W1.numpy(), W2.numpy()
+        rng = np.random.default_rng(K)
+        for _ in range(400):
+            n, k = int(rng.integers(0, N)), int(rng.integers(0, K))
+            jt, c = n // 128, n % 128
+            assert P[pos(jt, k // 128, c, k % 128)] == w1[k, n]
+            assert P[pos(jt, k // 128, 128 + c, k % 128)] == w2[k, n]
+        JT = (N + 127) // 128
+        for c in range(N % 128 or 128, 128, 5):
+            assert P[pos(JT - 1, 0, c, 3)] == 0 and P[pos(JT - 1, 0, 128 + c, 70)] == 0
+        if K % 128:
+            for n in range(0, N, 13):
+                for k in range(K % 128, 128, 11):
+                    assert P[pos(n // 128, KB - 1, n % 128, k)] == 0
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (1, 64, 128),         # one row, half a stage
+    (40, 208, 520),       # panel schedule, ragged K, partial last column tile
+    (128, 512, 4096),     # panel schedule, 2-3 panels per workgroup
+    (300, 144, 264),      # 128-row tiles, ragged K
+    (2100, 128, 256),     # persistent 256-row tiles, M tail
+    (4000, 256, 2696),    # mixed 256/128-row launch, partial last column tile
+])
+def test_fp8_parity(dev, M, K, N):
+    A8, W18, W28, sg, su = inputs.fp8_case(M, K, N, seed=M + K + N)
+    say("[fp8] M=%d K=%d N=%d" % (M, K, N))
+    Wp = sw.swiglu_pack_weights_fp8(W18.to(dev), W28.to(dev))
+    Y = gpu_bits(sw.swiglu_fused_packed_fp8(A8.to(dev), Wp, N, sg, su))
+    ref = oracle.swiglu_fp8(A8.numpy(), W18.numpy(), W28.numpy(), sg, su)
+    check_close(Y, ref, "fp8 %s" % ((M, K, N),))
+
+
+@pytest.mark.parametrize("name,M", [("qwen2.5-0.5B-prefill", 4096), ("qwen2.5-7B-decode", 128),
+                                    ("qwen2.5-7B-prefill", 8192)])
+def test_fp8_workload_shapes(dev, name, M):
+    """The workload's own tensors quantised per tensor; sampled rows (every
+    column) against the oracle."""
+    w = inputs.BY_NAME[name]
+    A, W1, W2 = inputs.workload_tensors(w, M)
+    A8, sa = inputs.quantize_e4m3(A)
+    W18, s1 = inputs.quantize_e4m3(W1)
+    W28, s2 = inputs.quantize_e4m3(W2)
+    sg = float(np.float32(sa) * np.float32(s1))
+    su = float(np.float32(sa) * np.float32(s2))
+    say("[fp8-workload] %s M=%d" % (name, M))
+    Wp = sw.swiglu_pack_weights_fp8(W18.to(dev), W28.to(dev))
+    Y = gpu_bits(sw.swiglu_fused_packed_fp8(A8.to(dev), Wp, w.N, sg, su))
+    rows = sample_rows(M, 6)
+    ref = oracle.swiglu_fp8(A8.numpy()[rows], W18.numpy(), W28.numpy(), sg, su)
+    check_close(Y[rows], ref, "fp8 %s rows" % name)
