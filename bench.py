@@ -28,6 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 (256 CU x 4096 flop/clk x 2.4 GHz)
+MFMA_FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 (published)
 HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
 MALL_BYTES = 256 << 20
 DEFAULT_WORKLOAD = "qwen2.5-0.5B-prefill"
@@ -52,7 +53,16 @@ def unfused_extra_bytes(M, K, N):
     return 8.0 * M * N + 2.0 * M * K
 
 
-def bound_of(M, K, N):
+def fused_bytes_fp8(M, K, N):
+    """Algorithmic HBM bytes of the FP8 product: A and both weights as one
+    byte per element, Y as bf16."""
+    return 1.0 * (M * K + 2 * K * N) + 2.0 * M * N
+
+
+def bound_of(M, K, N, dtype="bf16"):
+    if dtype == "fp8":
+        ai = flops(M, K, N) / fused_bytes_fp8(M, K, N)
+        return "mfma" if ai >= MFMA_FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
     ai = flops(M, K, N) / fused_bytes(M, K, N)
     return "mfma" if ai >= MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
 
@@ -148,6 +158,33 @@ def cpu_baseline(w, M, target_s=12.0):
         "sample": "first %d of %d rows of A, all %d columns (K=%d), %d run(s); %.1f s"
                   % (m, M, w.N, w.K, reps, dt),
     }
+
+
+def bench_point_fp8(w, M, steps, warmup, stream, prewarm_s=0.0):
+    """The FP8 path on the workload's own tensors, quantised per tensor (E4M3,
+    scale = amax / 448), over rotated input sets."""
+    import numpy as np
+    import torch
+    import swiglu_gated_mlp_amd as sw
+    from swiglu_gated_mlp_amd import inputs
+    dev = torch.device("cuda:0")
+    K, N = w.K, w.N
+    A, W1, W2 = inputs.workload_tensors(w, M)
+    A8, sa = inputs.quantize_e4m3(A)
+    W18, s1 = inputs.quantize_e4m3(W1)
+    W28, s2 = inputs.quantize_e4m3(W2)
+    sg = float(np.float32(sa) * np.float32(s1))
+    su = float(np.float32(sa) * np.float32(s2))
+    R = max(1, math.ceil(2 * MALL_BYTES / fused_bytes_fp8(M, K, N)))
+    W18d, W28d = W18.to(dev), W28.to(dev)
+    sets = [(A8.to(dev), sw.swiglu_pack_weights_fp8(W18d, W28d),
+             torch.empty((M, N), dtype=torch.bfloat16, device=dev)) for _ in range(R)]
+    del W18d, W28d
+    torch.cuda.synchronize()
+    fns = [(lambda s=s: sw.swiglu_fused_packed_fp8(s[0], s[1], N, sg, su, Y=s[2])) for s in sets]
+    per = time_gpu(fns, steps, warmup, stream, prewarm_s) / steps
+    return {"M": M, "K": K, "N": N, "rotation": R, "per_launch_s": per,
+            "tflops": flops(M, K, N) / per / 1e12, "gbs": fused_bytes_fp8(M, K, N) / per / 1e9}
 
 
 def bench_point(w, M, steps, warmup, variant, stream, prewarm_s=0.0, layout="per-tile"):
@@ -299,6 +336,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--m", type=int, default=None, help="token count (default: the workload's largest)")
     ap.add_argument("--variant", default="auto", choices=["auto", "data_parallel", "split_k"])
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp8"],
+                    help="operand type: bf16 (default) or FP8 E4M3 with per-tensor scales (the workload's "
+                         "tensors quantised; data-parallel streaming schedule)")
     ap.add_argument("--layout", default="per-tile", choices=["per-tile", "interleaved"],
                     help="packed weight layout: per-128-column-tile [W1|W2] (default) or column-granular "
                          "interleave (the data-parallel streaming schedule only)")
@@ -338,11 +378,15 @@ def main():
     w = inputs.BY_NAME[args.workload]
     M = args.m or w.m_max
 
-    res = bench_point(w, M, args.steps, args.warmup, args.variant, stream, args.prewarm, args.layout)
+    if args.dtype == "fp8":
+        res = bench_point_fp8(w, M, args.steps, args.warmup, stream, args.prewarm)
+    else:
+        res = bench_point(w, M, args.steps, args.warmup, args.variant, stream, args.prewarm, args.layout)
     per = res["per_launch_s"]
-    bound = bound_of(M, w.K, w.N)
+    bound = bound_of(M, w.K, w.N, args.dtype)
     if bound == "mfma":
-        achieved, peak, unit = res["tflops"], MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+        achieved, unit = res["tflops"], "TFLOP/s"
+        peak = MFMA_FP8_PEAK_TFLOPS if args.dtype == "fp8" else MFMA_BF16_PEAK_TFLOPS
     else:
         achieved, peak, unit = res["gbs"], HBM_PEAK_GBS, "GB/s"
 
@@ -370,7 +414,7 @@ def main():
         log("MLP " + json.dumps(bench_mlp(w, M, args.steps, args.warmup, stream, args.prewarm)))
 
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and args.dtype == "bf16":
         log("timing the CPU oracle on a sample of the workload ...")
         cpu = cpu_baseline(w, M)
 
@@ -385,14 +429,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic (seeded N(0,1) activations, N(0,1/K) weights)",
         "config": {"workload": "%s M=%d K=%d N=%d" % (w.name, M, w.K, w.N), "M": M, "K": w.K,
                    "N": w.N, "variant": args.variant, "layout": args.layout, "rotation_sets": res["rotation"]},
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 5),
                      "scope": "one swiglu_fused_packed call, all of its kernel launches",
-                     "traffic": measured_traffic("%s M=%d K=%d N=%d" % (w.name, M, w.K, w.N))},
+                     "traffic": (measured_traffic("%s M=%d K=%d N=%d" % (w.name, M, w.K, w.N))
+                                 if args.dtype == "bf16" else None)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
