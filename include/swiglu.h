@@ -27,8 +27,13 @@
  *  - Streams: `stream` is a hipStream_t (NULL = the default stream).  Work is
  *    enqueued and the call returns without synchronising; device-side faults
  *    surface at the caller's next synchronisation.
- *  - Shapes: M >= 0; K > 0 and N > 0 must be multiples of 8 (16-byte rows).
- *    M == 0 is a valid empty call: SWIGLU_OK, nothing is launched.
+ *  - Shapes: M >= 0; K > 0 and N > 0 must be multiples of 8 (16-byte rows),
+ *    K at most 4194304 (else SWIGLU_ERR_UNSUPPORTED_SHAPE); every dimension
+ *    at most 2^30.  M == 0 is a valid empty call: SWIGLU_OK, nothing is
+ *    launched.  Products whose activations reach 2 GiB are run as several
+ *    equal row chunks on the same stream, each on the data-parallel schedule
+ *    (the streaming kernel addresses each activation tile with 32-bit
+ *    offsets).
  *  - Aliasing: inputs may alias each other (W1 == W2 is legal).  Outputs must
  *    not overlap any input or each other.
  *  - Errors: argument errors are detected on the host before any HIP call and
@@ -55,7 +60,7 @@ typedef enum {
     SWIGLU_OK = 0,
     SWIGLU_ERR_NULL_POINTER = 1,      /* a required pointer is NULL (with M > 0)      */
     SWIGLU_ERR_BAD_SHAPE = 2,         /* M < 0, K <= 0, N <= 0, or sizes overflow     */
-    SWIGLU_ERR_UNSUPPORTED_SHAPE = 3, /* K or N not a multiple of 8                   */
+    SWIGLU_ERR_UNSUPPORTED_SHAPE = 3, /* K or N not a multiple of 8, or K > 2^22      */
     SWIGLU_ERR_MISALIGNED = 4,        /* a pointer is not 16-byte aligned             */
     SWIGLU_ERR_ALIASING = 5,          /* an output overlaps an input or other output  */
     SWIGLU_ERR_WORKSPACE = 6,         /* workspace missing or too small               */

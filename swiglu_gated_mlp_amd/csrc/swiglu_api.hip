@@ -29,6 +29,7 @@ swiglu_status hip_fail(hipError_t e) {
 }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;   // every dimension fits int32 with room
+constexpr int64_t kMaxK = (int64_t)1 << 22;     // 256 rows of activations stay below 2 GiB
 
 bool log_enabled() {
     static int on = -1;
@@ -63,7 +64,24 @@ swiglu_status check_shape(int64_t M, int64_t K, int64_t N) {
     if (M * N > ((int64_t)1 << 40) || K * N > ((int64_t)1 << 40) || M * K > ((int64_t)1 << 40))
         return SWIGLU_ERR_BAD_SHAPE;
     if ((K % 8) != 0 || (N % 8) != 0) return SWIGLU_ERR_UNSUPPORTED_SHAPE;
+    if (K > kMaxK) return SWIGLU_ERR_UNSUPPORTED_SHAPE;
     return SWIGLU_OK;
+}
+
+// The streaming kernel keeps each activation address as a 32-bit byte offset
+// from the stage base (row * K * bytes).  Calls whose activation slice would
+// reach 2 GiB are split into row chunks of at most this many rows (a multiple
+// of 256), each with A and Y advanced to its first row.
+int64_t stream_rows_limit(int64_t K, int elem_bytes) {
+    const int64_t rows = (((int64_t)1 << 31) / (K * elem_bytes)) / 256 * 256;
+    return rows >= 256 ? rows : 256;
+}
+
+// Equal chunks (multiples of 256 rows) of at most `limit` rows covering M.
+int64_t balanced_chunk(int64_t M, int64_t limit) {
+    const int64_t n = (M + limit - 1) / limit;
+    const int64_t per = (M + n - 1) / n;
+    return std::min(limit, (per + 255) / 256 * 256);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -448,6 +466,14 @@ swiglu_status swiglu_fused_packed_interleaved(const swiglu_bf16* A, const swiglu
     const Range y = range_of(Y, M * N * 2);
     if (overlap(y, range_of(A, M * K * 2)) || overlap(y, range_of(Wp, packed_elems(K, N) * 2)))
         return SWIGLU_ERR_ALIASING;
+    if (M > stream_rows_limit(K, 2)) {
+        const int64_t rows = balanced_chunk(M, stream_rows_limit(K, 2));
+        for (int64_t m0 = 0; m0 < M; m0 += rows) {
+            st = swiglu_fused_packed_interleaved(A + m0 * K, Wp, Y + m0 * N, std::min(rows, M - m0), K, N, stream);
+            if (st != SWIGLU_OK) return st;
+        }
+        return SWIGLU_OK;
+    }
     const Plan p = stream_dp_plan(M, K, N, cu_count_now());
     swk::FusedArgs a{};
     a.A = A; a.W1 = Wp; a.W2 = nullptr; a.Y = Y;
@@ -490,6 +516,14 @@ swiglu_status swiglu_fused_packed_fp8(const uint8_t* A, const uint8_t* Wp, swigl
     const Range y = range_of(Y, M * N * 2);
     if (overlap(y, range_of(A, M * K)) || overlap(y, range_of(Wp, packed_bytes_fp8(K, N))))
         return SWIGLU_ERR_ALIASING;
+    if (M > stream_rows_limit(K, 1)) {
+        const int64_t rows = balanced_chunk(M, stream_rows_limit(K, 1));
+        for (int64_t m0 = 0; m0 < M; m0 += rows) {
+            st = swiglu_fused_packed_fp8(A + m0 * K, Wp, Y + m0 * N, std::min(rows, M - m0), K, N, sg, su, stream);
+            if (st != SWIGLU_OK) return st;
+        }
+        return SWIGLU_OK;
+    }
     const Plan p = stream_dp_plan(M, K, N, cu_count_now());
     swk::FusedArgs a{};
     a.A = reinterpret_cast<const uint16_t*>(A);
@@ -566,6 +600,17 @@ swiglu_status swiglu_fused_packed(const swiglu_bf16* A, const swiglu_bf16* Wp, s
     const Range y = range_of(Y, M * N * 2);
     if (overlap(y, range_of(A, M * K * 2)) || overlap(y, range_of(Wp, packed_elems(K, N) * 2)))
         return SWIGLU_ERR_ALIASING;
+    if (M > stream_rows_limit(K, 2)) {
+        // chunks of at least half the limit: always the data-parallel
+        // schedule, which needs no workspace
+        const int64_t rows = balanced_chunk(M, stream_rows_limit(K, 2));
+        for (int64_t m0 = 0; m0 < M; m0 += rows) {
+            st = swiglu_fused_packed(A + m0 * K, Wp, Y + m0 * N, std::min(rows, M - m0), K, N, nullptr, 0,
+                                     SWIGLU_VARIANT_DATA_PARALLEL, stream);
+            if (st != SWIGLU_OK) return st;
+        }
+        return SWIGLU_OK;
+    }
 
     const Plan p = make_plan(M, K, N, variant, cu_count_now());
     const size_t need = split_workspace_bytes(p, M, N);

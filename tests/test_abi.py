@@ -55,7 +55,7 @@ A_, W1_, W2_, Y_, WP_, WS_ = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x5
 
 @pytest.mark.parametrize("M,K,N,want", [
     (-1, 64, 64, SHAPE), (4, 0, 64, SHAPE), (4, 64, 0, SHAPE), (4, -8, 64, SHAPE),
-    (4, 60, 64, UNSUP), (4, 64, 60, UNSUP), (1 << 31, 64, 64, SHAPE),
+    (4, 60, 64, UNSUP), (4, 64, 60, UNSUP), (1 << 31, 64, 64, SHAPE), (4, (1 << 22) + 8, 8, UNSUP),
 ])
 def test_fused_shape_errors(M, K, N, want):
     assert sw.lib().swiglu_fused(A_, W1_, W2_, Y_, M, K, N, None) == want
