@@ -958,8 +958,8 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
 
     // activation: lane l of direct load i fetches row (wave*A_INS+i)*8 + l/8,
     // logical chunk (l%8) ^ swz(row), so LDS holds the tile in lds_off order;
-    // byte offsets from A (the host keeps M*K*2 below 4 GiB) so the uniform
-    // part of the address stays scalar
+    // byte offsets from A (the host splits products whose activations reach
+    // 2 GiB into row chunks) so the uniform part of the address stays scalar
     uint32_t a_off[A_INS];
     // lane l's logical chunk in direct load i is (l%8) ^ swz(row) with
     // row = (wave*A_INS + i)*8 + l/8, i.e. chunk_x ^ ((wave*A_INS + i) & 7)
