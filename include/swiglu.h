@@ -196,8 +196,9 @@ int swiglu_choose_variant(int64_t M, int64_t K, int64_t N);
  *   rb*32 + (lane & 31) (rows 0-127 W1, 128-255 W2 columns of the tile) at
  *   k = 64*step + 32*(lane >> 5) + 0..31; padding is zero.
  * swiglu_pack_weights_fp8: W1_8, W2_8 [K,N] bytes -> that layout.
- * swiglu_fused_packed_fp8: Y[M,N] bf16 from A8 [M,K] and the packed weights
- *   on the data-parallel streaming schedule (no workspace, any M >= 0).
+ * swiglu_fused_packed_fp8: Y[M,N] bf16 from A8 [M,K] and the packed weights:
+ *   a weight-streaming decode kernel for M <= 32, the data-parallel streaming
+ *   schedule above (no workspace, any M >= 0).
  * Shapes: K a multiple of 16 and N a multiple of 8 (else
  * SWIGLU_ERR_UNSUPPORTED_SHAPE); pointers 16-byte aligned; Y must not
  * overlap A8 or the packed weights; validation codes return before any

@@ -1526,6 +1526,119 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// FP8 decode (M <= 32): weight streaming on the FP8 pack.  Each workgroup owns
+// CG groups of 32 output columns (32-row blocks rb of the packed tile for
+// Gate, 4 + rb for Up); its 4 waves take the 128-k blocks round-robin,
+// UNROLL blocks in flight, and each 64-k step is one
+// v_mfma_f32_32x32x64_f8f6f4 per (group, Gate|Up) with the weight fragment
+// as src0 (lane l: packed row l & 31, k 32(l >> 5) + 0..31, read whole from
+// the pack) and the activations as src1 (lane l: token l & 31, the same k,
+// two 16-byte loads).  The four per-wave fp32 sums are added in LDS in wave
+// order 0..3, scaled (p.sg, p.su), and SiLU(Gate) * Up is stored as bf16.
+// ---------------------------------------------------------------------------
+template <int CG, int UNROLL>
+__global__ __launch_bounds__(256) void decode_fp8_kernel(FusedArgs p) {
+    constexpr int WAVES = 4;
+    __shared__ f32x16 red[WAVES][CG][2][64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int M = p.M, K = p.K, N = p.N, KB = p.KB;
+    const int n0 = blockIdx.x * (32 * CG);
+    const int jt = n0 / PACK_BN, rb0 = (n0 % PACK_BN) / 32;
+    const char* wtile = reinterpret_cast<const char*>(p.W1) + (size_t)jt * KB * 32768 + lane * 32;
+    const char* arow = reinterpret_cast<const char*>(p.A) + (size_t)min(lane & 31, M - 1) * K + 32 * (lane >> 5);
+
+    f32x16 acc[CG][2];
+#pragma unroll
+    for (int c = 0; c < CG; ++c)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[c][g][r] = 0.0f;
+
+    for (int kb0 = wave; kb0 < KB; kb0 += WAVES * UNROLL) {
+        i32x4 wv[UNROLL][CG][2][2][2], av[UNROLL][2][2];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int kb = kb0 + u * WAVES;
+            if (kb < KB) {
+                const char* blk = wtile + (size_t)kb * 32768;
+#pragma unroll
+                for (int c = 0; c < CG; ++c)
+#pragma unroll
+                    for (int g = 0; g < 2; ++g)
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                            for (int h = 0; h < 2; ++h)
+                                wv[u][c][g][ks][h] = *reinterpret_cast<const i32x4*>(
+                                    blk + ((4 * g + rb0 + c) * 2 + ks) * 2048 + 16 * h);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int k = kb * 128 + 64 * ks + 32 * (lane >> 5) + 16 * h;
+                        av[u][ks][h] = k < K ? *reinterpret_cast<const i32x4*>(arow + (size_t)kb * 128 + 64 * ks + 16 * h)
+                                             : i32x4{0, 0, 0, 0};
+                    }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int kb = kb0 + u * WAVES;
+            if (kb < KB) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const i32x8 a8 = __builtin_shufflevector(av[u][ks][0], av[u][ks][1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                    for (int c = 0; c < CG; ++c)
+#pragma unroll
+                        for (int g = 0; g < 2; ++g) {
+                            const i32x8 w8 = __builtin_shufflevector(wv[u][c][g][ks][0], wv[u][c][g][ks][1],
+                                                                     0, 1, 2, 3, 4, 5, 6, 7);
+                            acc[c][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w8, a8, acc[c][g], 0, 0,
+                                                                                        0, 0, 0, 0);
+                        }
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int c = 0; c < CG; ++c)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) red[wave][c][g][lane] = acc[c][g];
+    __syncthreads();
+    // epilogue: wave w finishes groups w, w + 4, ...; lane l holds token
+    // m = l & 31 and columns n0 + 32c + 8(r/4) + 4(l >> 5) + r%4
+    for (int c = wave; c < CG; c += WAVES) {
+        f32x16 g = red[0][c][0][lane], u = red[0][c][1][lane];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) {
+            g += red[w][c][0][lane];
+            u += red[w][c][1][lane];
+        }
+        const int m = lane & 31;
+        if (m < M) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + 32 * c + 8 * q + 4 * (lane >> 5);
+                if (n < N) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = silu_f(g[4 * q + e] * p.sg) * (u[4 * q + e] * p.su);
+                    u32x2 out;
+                    out[0] = pack2(v[0], v[1]);
+                    out[1] = pack2(v[2], v[3]);
+                    *reinterpret_cast<u32x2*>(p.Y + (size_t)m * N + n) = out;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Weight pack / unpack (one-time transforms; see the packed layout in swiglu.h
 // and packed_off above).  One thread per 16-byte packed chunk: 8 consecutive
 // k of one packed row, at chunk index q = block * 2048 + ((group * 2 + half)

@@ -313,6 +313,28 @@ Plan stream_dp_plan(int64_t M, int64_t K, int64_t N, int cus) {
     return make_plan(M, K, N, SWIGLU_VARIANT_DATA_PARALLEL, cus);
 }
 
+// FP8 decode (M <= 32): groups of 32 output columns per workgroup (CG) and
+// 128-k blocks in flight per wave (UNROLL).
+constexpr int64_t kDecodeFp8MaxM = 32;
+
+template <int CG, int UNROLL>
+hipError_t launch_decode_fp8_cfg(const swk::FusedArgs& a, hipStream_t s) {
+    swk::FusedArgs args = a;
+    void* kargs[] = {&args};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&swk::decode_fp8_kernel<CG, UNROLL>),
+                           dim3((unsigned)ceil_div(a.N, 32 * CG)), dim3(256), kargs, 0, s);
+}
+
+// Measured (7B width M=1: <1,2> 27.2 us against 28.5-34.9 for the others;
+// 72B width M=32: <4,1> 83.6 us against 86.4-107): four groups per workgroup
+// when that grid still gives about one workgroup per CU, else one group and
+// two blocks in flight (two workgroups per CU).
+hipError_t launch_decode_fp8(const swk::FusedArgs& a, int cus, hipStream_t s) {
+    const int64_t wide = ceil_div(a.N, 128);
+    if (wide <= cus && 4 * wide >= 3 * (int64_t)cus) return launch_decode_fp8_cfg<4, 1>(a, s);
+    return launch_decode_fp8_cfg<1, 2>(a, s);
+}
+
 hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) {
     if (p.variant == SWIGLU_VARIANT_DECODE) {
         swk::DecodeArgs d{};
@@ -524,16 +546,21 @@ swiglu_status swiglu_fused_packed_fp8(const uint8_t* A, const uint8_t* Wp, swigl
         }
         return SWIGLU_OK;
     }
-    const Plan p = stream_dp_plan(M, K, N, cu_count_now());
     swk::FusedArgs a{};
     a.A = reinterpret_cast<const uint16_t*>(A);
     a.W1 = reinterpret_cast<const uint16_t*>(Wp);
     a.W2 = nullptr; a.Y = Y;
     a.M = (int)M; a.K = (int)K; a.N = (int)N;
-    a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n;
     a.KB = (int)ceil_div(K, 128);
     a.splits = 1; a.kb_per_split = a.KB;
     a.sg = sg; a.su = su;
+    const int cus = cu_count_now();
+    if (M <= kDecodeFp8MaxM) {
+        const hipError_t e = launch_decode_fp8(a, cus, (hipStream_t)stream);
+        return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
+    }
+    const Plan p = stream_dp_plan(M, K, N, cus);
+    a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n;
     const hipError_t e = launch_stream_dp<false, true>(a, p, (hipStream_t)stream);
     return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
 }
