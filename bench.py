@@ -8,7 +8,7 @@ timed region, as a model-load step.
 Prints ONE JSON line (metric, value, ..., roofline, cpu_baseline).
 
     python bench.py [--steps K] [--warmup W] [--prewarm SECONDS] [--workload NAME] [--m M]
-                    [--variant auto|data_parallel|split_k] [--no-cpu] [--all]
+                    [--variant auto|data_parallel|split_k|sequential] [--no-cpu] [--all]
 
 The timed region is exactly K steps after W warm-up steps; before those, the
 same calls run untimed for --prewarm seconds so the GPU has left its idle
@@ -335,7 +335,7 @@ def main():
                     help="untimed calls before the warm-up steps, in seconds of wall time (0 under a profiler)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--m", type=int, default=None, help="token count (default: the workload's largest)")
-    ap.add_argument("--variant", default="auto", choices=["auto", "data_parallel", "split_k"])
+    ap.add_argument("--variant", default="auto", choices=["auto", "data_parallel", "split_k", "sequential"])
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp8"],
                     help="operand type: bf16 (default) or FP8 E4M3 with per-tensor scales (the workload's "
                          "tensors quantised; data-parallel streaming schedule)")

@@ -89,12 +89,24 @@ typedef enum {
  *                 DECODE up to 32 rows, and up to 64 rows while the weight
  *                 panels (4 per 128 columns) number fewer than the CUs;
  *                 otherwise DATA_PARALLEL, or SPLIT_K when the data-parallel
- *                 tiles would fill under half the CUs (and K >= 32 M). */
+ *                 tiles would fill under half the CUs (and K >= 32 M).
+ *  SEQUENTIAL:    the Gate-then-Up order ([Summary: Methodology] Kernel-1:
+ *                 SiLU on the finished Gate accumulator while the Up
+ *                 operands are still loading): on the data-parallel 128- or
+ *                 256-row tiles,
+ *                 each tile runs a K loop over the Gate half of the packed
+ *                 weights, then computes SiLU(Gate) while the Up loop's first
+ *                 stages load, then runs a second K loop over the activations
+ *                 and the Up half.  Same result as DATA_PARALLEL, bit for bit;
+ *                 any M; no workspace.  AUTO never picks it (it re-reads the
+ *                 activation tiles and is slower on this chip at every
+ *                 measured shape); it exists for comparison. */
 typedef enum {
     SWIGLU_VARIANT_AUTO = 0,
     SWIGLU_VARIANT_DATA_PARALLEL = 1,
     SWIGLU_VARIANT_SPLIT_K = 2,
-    SWIGLU_VARIANT_DECODE = 3
+    SWIGLU_VARIANT_DECODE = 3,
+    SWIGLU_VARIANT_SEQUENTIAL = 4
 } swiglu_variant;
 
 /* Returns SWIGLU_ABI_VERSION. */

@@ -26,8 +26,9 @@ VARIANT_AUTO = 0
 VARIANT_DATA_PARALLEL = 1
 VARIANT_SPLIT_K = 2
 VARIANT_DECODE = 3
+VARIANT_SEQUENTIAL = 4
 VARIANTS = {"auto": VARIANT_AUTO, "data_parallel": VARIANT_DATA_PARALLEL, "split_k": VARIANT_SPLIT_K,
-            "decode": VARIANT_DECODE}
+            "decode": VARIANT_DECODE, "sequential": VARIANT_SEQUENTIAL}
 
 # Every entry point of include/swiglu.h with its ctypes signature.
 _I64 = ctypes.c_int64

@@ -887,11 +887,20 @@ constexpr int stream_smem_elems() {
 // p.sg, p.su applied to the fp32 sums): a stage is 128 k (the same 128-byte
 // activation rows), each 32-row block takes one v_mfma_f32_32x32x64_f8f6f4
 // per 64 k, and a sub-step covers one 64-k step for half of the row blocks.
-template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false, bool IL = false, bool F8 = false>
+// SEQ: the sequential order (Gate first, then Up): each tile is two K loops
+// over the same activations, the first on the Gate half of every packed
+// block, the second on the Up half, each with one MFMA per 32-row block into
+// the one accumulator set acc[0].  Between the two, the Up loop's first two
+// stages are issued and SiLU(Gate) is computed into acc[1] while they land;
+// the epilogue is then acc[1] * acc[0].  The Gate and Up sums take the same
+// MFMAs in the same order as the dual loop, so the two agree bitwise.
+template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false, bool IL = false, bool F8 = false,
+          bool SEQ = false>
 __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_t* smem, int first, int stride,
                                                      int total) {
     static_assert(!(IL && SPLIT), "the interleaved layout has no split-K schedule");
     static_assert(!(F8 && (IL || SPLIT)), "FP8 operands: per-tile layout, data-parallel only");
+    static_assert(!(SEQ && (SPLIT || PANELS || IL || F8)), "sequential order: bf16 per-tile tiles only");
     constexpr int EB = F8 ? 1 : 2;              // bytes per operand element
     constexpr int KSTAGE = F8 ? 128 : BK;       // k per stage (128-byte activation rows)
     constexpr int CE = 16 / EB;                 // elements per 16-byte chunk
@@ -900,7 +909,8 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
     constexpr int A_INS = BM / 8 / NW;          // 1 KiB direct loads per wave per stage
     constexpr int ASTAGE = BM * BK;             // elements per activation stage
     constexpr int NBUF = 3;                     // ring slots == weight register sets
-    constexpr int LOADS = A_INS + 8;            // vector-memory instructions per wave per stage
+    constexpr int WT = SEQ ? 1 : 2;             // weight halves per stage (Gate and Up, or one)
+    constexpr int LOADS = A_INS + 4 * WT;       // vector-memory instructions per wave per stage
     constexpr int NST = BM / 16;                // Y stores per wave per tile
     constexpr int GROUP_M = 8;
     static_assert(TM >= 1 && A_INS >= 1 && (BM / 8) % NW == 0, "tile");
@@ -916,7 +926,7 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
     // work item w -> output tile (m0, n0), K blocks [kb_first, kb_first + ns)
     // and the number np of waves with weights (32-column panels from n0 on)
     struct Item {
-        int m0, n0, kb_first, ns, split, np;
+        int m0, n0, kb_first, ns, split, np, up;
     };
     auto item_of = [&](int w) {
         if constexpr (PANELS) {
@@ -935,6 +945,7 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
                 it.ns = KB;
                 it.split = 0;
                 it.np = q1 - q0;
+                it.up = 0;
                 return it;
             }
         }
@@ -953,6 +964,7 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
         it.ns = (SPLIT ? min(KB, it.kb_first + p.kb_per_split) : KB) - it.kb_first;   // >= 1
         it.split = split;
         it.np = 4;
+        it.up = 0;
         return it;
     };
 
@@ -1000,7 +1012,8 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
         else
             w_off = (uint32_t)((((wq & 3) * (IL ? 4 : 2) + ((ll >> 4) & 1)) * 1024 + (ll >> 5) * 128 +
                                 (ll & 15) * 8) * 2);
-        w_tile = reinterpret_cast<const char*>(p.W1) + (size_t)(wq >> 2) * KB * (PACK_ROWS * PACK_BK * 2);
+        w_tile = reinterpret_cast<const char*>(p.W1) + (size_t)(wq >> 2) * KB * (PACK_ROWS * PACK_BK * 2) +
+                 (SEQ && it.up ? 16384 : 0);   // SEQ: the Up half of each packed block
         ld_kb_first = it.kb_first;
         ld_ns = valid ? it.ns : 0;
         ld_ns_w = (!PANELS || wave < it.np) ? ld_ns : 0;
@@ -1041,12 +1054,12 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
     zero_acc();
     bf16x8 fa[2][TM];
     i32x8 fa8[2][TM / 2 > 0 ? TM / 2 : 1];
-    bf16x8 wf[NBUF][2][4];
+    bf16x8 wf[NBUF][WT][4];
     // every register set defined on every path into the stage loop
 #pragma unroll
     for (int q = 0; q < NBUF; ++q)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < WT; ++t)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) wf[q][t][kk] = bf16x8{};
 
@@ -1153,7 +1166,9 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             acc[0][i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[WS][0][kk], fa[cur][i], acc[0][i][0], 0, 0, 0);
-            acc[1][i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[WS][1][kk], fa[cur][i], acc[1][i][0], 0, 0, 0);
+            if constexpr (!SEQ)
+                acc[1][i][0] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[WS][WT - 1][kk], fa[cur][i], acc[1][i][0], 0, 0, 0);
             if constexpr (RD) {
 #pragma unroll
                 for (int q = i * RPI; q < (i + 1) * RPI; ++q)
@@ -1250,7 +1265,7 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
 #pragma unroll
         for (int q = 0; q < NBUF; ++q)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < WT; ++t)
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) asm volatile("" ::"v"(wf[q][t][kk]));
         __builtin_amdgcn_s_barrier();
@@ -1258,6 +1273,34 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
         if constexpr (SPLIT) {
             store_partials<TM, 1>(acc, p.part, cur.split, M, N, cur.m0, cur.n0 + wave * 32, lane);
             break;   // one item per workgroup
+        }
+
+        if constexpr (SEQ) {
+            if (!cur.up) {
+                // Gate done: the Up loop's first two stages stream in while
+                // SiLU(Gate) goes to acc[1] and acc[0] is cleared for Up
+                Item upi = cur;
+                upi.up = 1;
+                load_item(upi, true);
+                issue_first_w();
+                issue_first_a();
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        acc[1][i][0][r] = silu_f(acc[0][i][0][r]);
+                        acc[0][i][0][r] = 0.0f;
+                    }
+                __builtin_amdgcn_sched_barrier(0);
+                set_rd_base();
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(A_INS, 0));
+                __builtin_amdgcn_s_barrier();
+#pragma unroll
+                for (int i = 0; i < TM; ++i) read_a(0u, 0, i, 0);
+                cur = upi;
+                continue;
+            }
         }
 
         // the next item's first two stages stream in during this epilogue
@@ -1314,7 +1357,8 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
                             gv *= p.sg;
                             uv *= p.su;
                         }
-                        v[e] = silu_f(gv) * uv;
+                        // SEQ: acc[1] holds SiLU(Gate), acc[0] Up
+                        v[e] = SEQ ? uv * gv : silu_f(gv) * uv;
                     }
                     u32x2 out;
                     out[0] = pack2(v[0], v[1]);
@@ -1332,7 +1376,7 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
         for (int j = A_INS; j < LOADS; ++j) issue_one(j, 1, 1, I1{});
         // the next item's stage 0 (and stage 1's activations) has landed once
         // at most stage 1's weight loads are in flight; the Y tile is in LDS
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(8, 0));
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(LOADS - A_INS, 0));
         __builtin_amdgcn_s_barrier();
         {
             // wave w stores rows w*BM/4 + 4t + l/16, 16 bytes at column 8(l%16)
@@ -1368,33 +1412,34 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < WT; ++t)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) asm volatile("" ::"v"(wf[q][t][kk]));
 }
 
-template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false, bool IL = false, bool F8 = false>
+template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false, bool IL = false, bool F8 = false,
+          bool SEQ = false>
 __global__ __launch_bounds__(256) void stream_prefill_kernel(FusedArgs p, int total) {
     static_assert(!PANELS || (BM == 128 && !SPLIT), "panel schedule: one 128-row tile, data-parallel");
     __shared__ __attribute__((aligned(16))) uint16_t smem[stream_smem_elems<BM>()];
-    stream_prefill_tiles<BM, SPLIT, RAGGED, PANELS, IL, F8>(p, smem, blockIdx.x, gridDim.x, total);
+    stream_prefill_tiles<BM, SPLIT, RAGGED, PANELS, IL, F8, SEQ>(p, smem, blockIdx.x, gridDim.x, total);
 }
 
 // The 256-row tiles and the 128-row tail column tiles in one launch: blocks
 // 0 .. n_pers-1 work through the n_big 256-row tiles of `big` (block b takes
 // tiles b, b + n_pers, ...), the remaining blocks take one 128-row tile of
 // `tail` each and start on CUs as the 256-row work drains.
-template <bool RAGGED, bool IL = false, bool F8 = false>
+template <bool RAGGED, bool IL = false, bool F8 = false, bool SEQ = false>
 __global__ __launch_bounds__(256) void stream_prefill_mixed_kernel(FusedArgs big, FusedArgs tail, int n_pers,
                                                                    int n_big) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[stream_smem_elems<256>()];
     static_assert(stream_smem_elems<256>() >= stream_smem_elems<128>(), "one LDS block serves both tiles");
     const int b = blockIdx.x;
     if (b < n_pers) {
-        stream_prefill_tiles<256, false, RAGGED, false, IL, F8>(big, smem, b, n_pers, n_big);
+        stream_prefill_tiles<256, false, RAGGED, false, IL, F8, SEQ>(big, smem, b, n_pers, n_big);
     } else {
         const int n_tail = gridDim.x - n_pers;
-        stream_prefill_tiles<128, false, RAGGED, false, IL, F8>(tail, smem, b - n_pers, n_tail, n_tail);
+        stream_prefill_tiles<128, false, RAGGED, false, IL, F8, SEQ>(tail, smem, b - n_pers, n_tail, n_tail);
     }
 }
 

@@ -161,7 +161,7 @@ struct Plan {
 };
 
 constexpr int kDecodeMaxM = 64;
-bool variant_known(int v) { return v >= SWIGLU_VARIANT_AUTO && v <= SWIGLU_VARIANT_DECODE; }
+bool variant_known(int v) { return v >= SWIGLU_VARIANT_AUTO && v <= SWIGLU_VARIANT_SEQUENTIAL; }
 
 Plan make_plan(int64_t M, int64_t K, int64_t N, int variant, int cus) {
     Plan p{};
@@ -196,7 +196,9 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int variant, int cus) {
     }
     p.variant = v;
     p.decode_mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    p.t = packed_tile_for(M, v);
+    // the sequential order runs on the data-parallel tiles (no panel schedule)
+    const bool dp_tiles = v == SWIGLU_VARIANT_DATA_PARALLEL || v == SWIGLU_VARIANT_SEQUENTIAL;
+    p.t = packed_tile_for(M, dp_tiles ? SWIGLU_VARIANT_DATA_PARALLEL : v);
     p.tiles_m = (int)ceil_div(M, p.t.BM);
     p.tiles_n = (int)ceil_div(N, p.t.BN);
     p.tiles = p.tiles_m * p.tiles_n;
@@ -204,7 +206,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int variant, int cus) {
     // tiles would leave most CUs idle, the column tiles that make up that round
     // run afterwards as 128 x 128 tiles (twice as many, half the work each).
     p.tail_ntiles = 0;
-    if (v == SWIGLU_VARIANT_DATA_PARALLEL && p.t.BM == 256 && p.tiles > cus) {
+    if (dp_tiles && p.t.BM == 256 && p.tiles > cus) {
         const int rem = p.tiles % cus;
         if (rem > 0 && rem * 10 <= cus * 6) {
             const int nt = (int)ceil_div(rem, p.tiles_m);
@@ -263,23 +265,25 @@ hipError_t launch_prefill(const swk::FusedArgs& a, int grid, hipStream_t s) {
 
 // `total` work items (tiles, or tile x K split) on `grid` <= total workgroups;
 // each workgroup takes items b, b + grid, ...
-template <int BM, bool SPLIT, bool PANELS = false, bool IL = false, bool F8 = false>
+template <int BM, bool SPLIT, bool PANELS = false, bool IL = false, bool F8 = false, bool SEQ = false>
 hipError_t launch_stream(const swk::FusedArgs& a, int total, int grid, hipStream_t s) {
     const bool ragged = (a.K % (F8 ? 128 : swk::BK)) != 0;
-    const void* fn = ragged
-                         ? reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, true, PANELS, IL, F8>)
-                         : reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, false, PANELS, IL, F8>);
+    const void* fn =
+        ragged ? reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, true, PANELS, IL, F8, SEQ>)
+               : reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, false, PANELS, IL, F8, SEQ>);
     swk::FusedArgs args = a;
     void* kargs[] = {&args, &total};
     return hipLaunchKernel(fn, dim3(grid), dim3(256), kargs, 0, s);
 }
 
 // The data-parallel streaming schedules (128- or 256-row tiles, the panel
-// schedule, the mixed 256/128-row launch) on either weight layout.
-template <bool IL, bool F8 = false>
+// schedule, the mixed 256/128-row launch) on either weight layout; SEQ: the
+// sequential Gate-then-Up order (per-tile layout, no panel schedule).
+template <bool IL, bool F8 = false, bool SEQ = false>
 hipError_t launch_stream_dp(const swk::FusedArgs& a, const Plan& p, hipStream_t s) {
     const int grid = p.tiles;
     if (p.t.BM == 128) {
+        if constexpr (SEQ) return launch_stream<128, false, false, false, false, true>(a, grid, grid, s);
         if (p.panels > 0) {
             swk::FusedArgs pa = a;
             pa.panels = p.panels;
@@ -289,7 +293,7 @@ hipError_t launch_stream_dp(const swk::FusedArgs& a, const Plan& p, hipStream_t 
         return launch_stream<128, false, false, IL, F8>(a, grid, grid, s);
     }
     // one workgroup per CU works through the 256-row tiles
-    if (p.tail_ntiles == 0) return launch_stream<256, false, false, IL, F8>(a, grid, std::min(grid, p.cus), s);
+    if (p.tail_ntiles == 0) return launch_stream<256, false, false, IL, F8, SEQ>(a, grid, std::min(grid, p.cus), s);
     // one launch: the 256-row tiles of the first column tiles, then
     // the last tail_ntiles column tiles as 128-row tiles
     swk::FusedArgs big = a, tail = a;
@@ -302,8 +306,8 @@ hipError_t launch_stream_dp(const swk::FusedArgs& a, const Plan& p, hipStream_t 
     const int grid_all = n_pers + tail.tiles_m * tail.tiles_n;
     const bool ragged = (a.K % (F8 ? 128 : swk::BK)) != 0;
     const void* fn = ragged
-                         ? reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<true, IL, F8>)
-                         : reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<false, IL, F8>);
+                         ? reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<true, IL, F8, SEQ>)
+                         : reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<false, IL, F8, SEQ>);
     void* kargs[] = {&big, &tail, &n_pers, &n_big};
     return hipLaunchKernel(fn, dim3(grid_all), dim3(256), kargs, 0, s);
 }
@@ -336,6 +340,7 @@ hipError_t launch_decode_fp8(const swk::FusedArgs& a, int cus, hipStream_t s) {
 }
 
 hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) {
+    if (p.variant == SWIGLU_VARIANT_SEQUENTIAL) return launch_stream_dp<false, false, true>(a, p, s);
     if (p.variant == SWIGLU_VARIANT_DECODE) {
         swk::DecodeArgs d{};
         d.A = a.A; d.Wp = a.W1; d.Y = a.Y;
@@ -633,7 +638,9 @@ swiglu_status swiglu_fused_packed(const swiglu_bf16* A, const swiglu_bf16* Wp, s
         const int64_t rows = balanced_chunk(M, stream_rows_limit(K, 2));
         for (int64_t m0 = 0; m0 < M; m0 += rows) {
             st = swiglu_fused_packed(A + m0 * K, Wp, Y + m0 * N, std::min(rows, M - m0), K, N, nullptr, 0,
-                                     SWIGLU_VARIANT_DATA_PARALLEL, stream);
+                                     variant == SWIGLU_VARIANT_SEQUENTIAL ? SWIGLU_VARIANT_SEQUENTIAL
+                                                                          : SWIGLU_VARIANT_DATA_PARALLEL,
+                                     stream);
             if (st != SWIGLU_OK) return st;
         }
         return SWIGLU_OK;

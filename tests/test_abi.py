@@ -82,6 +82,11 @@ def test_packed_errors():
     # the decode schedule serves M <= 64 only
     assert L.swiglu_fused_packed(A_, WP_, Y_, 65, 64, 64, None, 0, 3, None) == VARIANT
     assert L.swiglu_workspace_bytes(16, 3584, 18944, 3) == 0
+    # the sequential order: any M, no workspace; codes past it are unknown
+    assert L.swiglu_workspace_bytes(16, 3584, 18944, 4) == 0
+    assert L.swiglu_workspace_bytes(8192, 3584, 18944, 4) == 0
+    assert L.swiglu_fused_packed(A_, WP_, Y_, 4, 64, 64, None, 0, 5, None) == VARIANT
+    assert L.swiglu_fused_packed(A_, None, Y_, 4, 64, 64, None, 0, 4, None) == NULLP
     assert L.swiglu_fused_packed(A_, WP_, Y_, 4, 64, 64, None, 0, -1, None) == VARIANT
     assert L.swiglu_fused_packed(A_, None, Y_, 4, 64, 64, None, 0, 0, None) == NULLP
     assert L.swiglu_fused_packed(A_, WP_, WP_ + 16, 4, 64, 64, None, 0, 1, None) == ALIAS

@@ -1,7 +1,8 @@
 """Products whose activations pass 2 GiB: the library runs them as row chunks
 (the streaming kernel addresses an activation tile with 32-bit offsets).
 Rows on both sides of every chunk boundary and the last row are checked
-against the oracle, for the bf16, interleaved-layout and FP8 entry points.
+against the oracle, for the bf16 (both orders), interleaved-layout and FP8
+entry points.
 The activations are drawn on the GPU (seeded); only the sampled rows go to
 the oracle."""
 import numpy as np
@@ -48,13 +49,16 @@ def test_bf16_over_2gib(dev):
     _, W1, W2 = inputs.gaussian_case(1, K, N, seed=12)
     W1d, W2d = W1.to(dev), W2.to(dev)
     say("[large] bf16 M=%d K=%d N=%d (%.2f GiB of activations)" % (M, K, N, M * K * 2 / 2 ** 30))
-    Y = gpu_bits(sw.swiglu_fused_packed(Ad, sw.swiglu_pack_weights(W1d, W2d), N))
+    Wp = sw.swiglu_pack_weights(W1d, W2d)
+    Y = gpu_bits(sw.swiglu_fused_packed(Ad, Wp, N))
+    Ys = gpu_bits(sw.swiglu_fused_packed(Ad, Wp, N, variant=sw.VARIANT_SEQUENTIAL))
     Yi = gpu_bits(sw.swiglu_fused_packed_interleaved(Ad, sw.swiglu_pack_weights_interleaved(W1d, W2d), N))
     rows = _rows(M, 65536)
     A_rows = inputs.as_bits(Ad[rows].cpu())
     ref = oracle.swiglu(A_rows, W1, W2)
     check_close(Y[rows], ref, "bf16 chunked rows %s" % rows)
     assert np.array_equal(Yi, Y), "interleaved layout != per-tile layout bitwise"
+    assert np.array_equal(Ys, Y), "sequential order != data-parallel bitwise"
 
 
 def test_fp8_over_2gib(dev):

@@ -18,8 +18,8 @@ from _util import (check_close, f32, gpu_bits, mismatch_rates, oracle_cols, orac
 
 pytestmark = pytest.mark.gpu
 
-DP, SPLIT, AUTO, DECODE = (sw.VARIANT_DATA_PARALLEL, sw.VARIANT_SPLIT_K, sw.VARIANT_AUTO,
-                           sw.VARIANT_DECODE)
+DP, SPLIT, AUTO, DECODE, SEQ = (sw.VARIANT_DATA_PARALLEL, sw.VARIANT_SPLIT_K, sw.VARIANT_AUTO,
+                                sw.VARIANT_DECODE, sw.VARIANT_SEQUENTIAL)
 
 
 @pytest.fixture(scope="module")
@@ -39,14 +39,18 @@ def run_all_variants(dev, A, W1, W2, label):
     out = {}
     say("[%s] M=%d K=%d N=%d fused" % (label, M, K, N))
     out["fused"] = sw.swiglu_fused(Ad, W1d, W2d)
-    variants = [("dp", DP), ("split", SPLIT), ("auto", AUTO)]
+    variants = [("dp", DP), ("split", SPLIT), ("auto", AUTO), ("seq", SEQ)]
     if M <= 64:
         variants.append(("decode", DECODE))
     for name, v in variants:
         say("[%s] M=%d K=%d N=%d packed/%s" % (label, M, K, N, name))
         out[name] = sw.swiglu_fused_packed(Ad, Wp, N, variant=v)
     torch.cuda.synchronize()
-    return {k: gpu_bits(v) for k, v in out.items()}
+    bits = {k: gpu_bits(v) for k, v in out.items()}
+    # the sequential order sums the same MFMAs in the same order as the dual
+    # loop of the data-parallel schedule
+    assert np.array_equal(bits["seq"], bits["dp"]), "sequential != data-parallel bitwise"
+    return bits
 
 
 SMALL_SHAPES = [
