@@ -8,11 +8,18 @@ timed region, as a model-load step.
 Prints ONE JSON line (metric, value, ..., roofline, cpu_baseline).
 
     python bench.py [--steps K] [--warmup W] [--prewarm SECONDS] [--workload NAME] [--m M]
-                    [--variant auto|data_parallel|split_k|sequential] [--no-cpu] [--all]
+                    [--variant auto|data_parallel|split_k|sequential] [--dtype bf16|fp8]
+                    [--layout per-tile|interleaved] [--no-cpu] [--all [--repeats R] [--mlp]]
 
 The timed region is exactly K steps after W warm-up steps; before those, the
 same calls run untimed for --prewarm seconds so the GPU has left its idle
 clock (a 75 us step would otherwise be timed partly at the idle clock).
+
+--all also reports every workload point on stderr (POINT lines): the median of
+R timed repeats with its min/max, the unfused pipeline's time, and for the
+decode-sized points (M <= 64) the per-call time of a graph-captured loop,
+which leaves out the host's launch cost; a CONTEXT line first records the
+device, its CUs, the HIP version and rocm-smi's clocks and power limit.
 """
 from __future__ import annotations
 
@@ -101,6 +108,51 @@ def time_gpu(fn_list, steps, warmup, stream, prewarm_s=0.0):
     return start.elapsed_time(stop) / 1e3
 
 
+def time_gpu_graph(fn_list, calls, replays, stream):
+    """Per-call seconds of `calls` calls captured in one HIP graph and replayed
+    `replays` times (after one untimed replay), timed with HIP events on the
+    stream; what is left of a call's time is its device time plus the gap the
+    device leaves between two graph nodes, with no host launch cost."""
+    import torch
+    R = len(fn_list)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            fn_list[i % R]()
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(replays):
+        g.replay()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return start.elapsed_time(stop) / 1e3 / (calls * replays)
+
+
+def run_context():
+    """Device facts for the --all report: name, CUs, HIP and torch versions,
+    and what rocm-smi says of clocks and power (when it runs)."""
+    import subprocess
+    import torch
+    prop = torch.cuda.get_device_properties(0)
+    ctx = {"device": prop.name, "gcn_arch": getattr(prop, "gcnArchName", None),
+           "cus": prop.multi_processor_count, "hbm_gib": round(prop.total_memory / 2 ** 30, 1),
+           "hip": torch.version.hip, "torch": torch.__version__,
+           "host_cpus": len(os.sched_getaffinity(0))}
+    try:
+        r = subprocess.run(["rocm-smi", "--showmaxpower", "--showclocks", "--showdriverversion", "--json"],
+                           capture_output=True, text=True, timeout=30)
+        if r.returncode == 0:
+            ctx["rocm_smi"] = json.loads(r.stdout)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        pass
+    return ctx
+
+
 def kernel_source_sha256():
     import hashlib
     h = hashlib.sha256()
@@ -187,7 +239,8 @@ def bench_point_fp8(w, M, steps, warmup, stream, prewarm_s=0.0):
             "tflops": flops(M, K, N) / per / 1e12, "gbs": fused_bytes_fp8(M, K, N) / per / 1e9}
 
 
-def bench_point(w, M, steps, warmup, variant, stream, prewarm_s=0.0, layout="per-tile"):
+def bench_point(w, M, steps, warmup, variant, stream, prewarm_s=0.0, layout="per-tile", repeats=1,
+                graph=False):
     import torch
     import swiglu_gated_mlp_amd as sw
     from swiglu_gated_mlp_amd import inputs
@@ -214,12 +267,24 @@ def bench_point(w, M, steps, warmup, variant, stream, prewarm_s=0.0, layout="per
                for s in sets]
     sec = time_gpu(fns, steps, warmup, stream, prewarm_s)
     per = sec / steps
-    return {
+    out = {
         "M": M, "K": K, "N": N, "rotation": R, "seconds": sec, "per_launch_s": per,
         "tflops": flops(M, K, N) / per / 1e12,
         "gbs": fused_bytes(M, K, N) / per / 1e9,
         "variant": variant, "resolved_variant": sw.swiglu_choose_variant(M, K, N) if v == 0 else v,
     }
+    if repeats > 1:
+        # further timed repeats of the same steps (no new warm-up needed);
+        # the median is reported with the spread
+        pers = [per] + [time_gpu(fns, steps, 0, stream) / steps for _ in range(repeats - 1)]
+        pers.sort()
+        out.update(per_launch_s=pers[len(pers) // 2], per_min_s=pers[0], per_max_s=pers[-1], repeats=repeats)
+        per = out["per_launch_s"]
+        out["tflops"] = flops(M, K, N) / per / 1e12
+        out["gbs"] = fused_bytes(M, K, N) / per / 1e9
+    if graph:
+        out["graph_per_launch_s"] = time_gpu_graph(fns, max(R, 32), max(3, steps // 32), stream)
+    return out
 
 
 def bench_unfused(w, M, steps, warmup, stream, prewarm_s=0.0):
@@ -343,6 +408,8 @@ def main():
                     help="packed weight layout: per-128-column-tile [W1|W2] (default) or column-granular "
                          "interleave (the data-parallel streaming schedule only)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="--all: timed repeats per point (median and min/max reported)")
     ap.add_argument("--mlp", action="store_true",
                     help="also time the whole gated MLP block (with the down projection), fused and "
                          "unfused, at the workload point (with --all: at every point) (stderr)")
@@ -392,10 +459,11 @@ def main():
 
     extra = {}
     if args.all:
+        log("CONTEXT " + json.dumps(run_context()))
         for ww in inputs.WORKLOADS:
             for mm in ww.ms:
                 r = bench_point(ww, mm, max(10, args.steps // 2), 5, args.variant, stream, args.prewarm,
-                                args.layout)
+                                args.layout, repeats=args.repeats, graph=mm <= 64)
                 tu = bench_unfused(ww, mm, max(5, args.steps // 4), 3, stream, args.prewarm)
                 b = bound_of(mm, ww.K, ww.N)
                 frac = r["tflops"] / MFMA_BF16_PEAK_TFLOPS if b == "mfma" else r["gbs"] / HBM_PEAK_GBS
@@ -405,6 +473,11 @@ def main():
                         "unfused_us": round(tu * 1e6, 2),
                         "speedup_vs_unfused": round(tu / r["per_launch_s"], 3),
                         "resolved_variant": r["resolved_variant"]}
+                if "repeats" in r:
+                    line.update(repeats=r["repeats"], us_min=round(r["per_min_s"] * 1e6, 2),
+                                us_max=round(r["per_max_s"] * 1e6, 2))
+                if "graph_per_launch_s" in r:
+                    line["graph_us"] = round(r["graph_per_launch_s"] * 1e6, 2)
                 log("POINT " + json.dumps(line))
                 extra.setdefault("points", []).append(line)
                 if args.mlp:
