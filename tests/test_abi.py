@@ -215,3 +215,51 @@ def test_binding_argument_errors():
         sw._dev_bf16(a, "A")
     with pytest.raises(ValueError, match="GPU tensor"):
         sw._dev_bf16(a.float(), "A")
+
+
+def test_auto_dispatch_at_workload_shapes():
+    """AUTO's choice is host logic (no device work): decode up to 32 rows and,
+    up to 64 rows, while the 32-column weight panels number fewer than the CUs;
+    the data-parallel streaming schedule otherwise.  Without a device the
+    library plans for 256 CUs, the MI355X count, so these are the choices the
+    GPU runs make."""
+    L = sw.lib()
+    DP, DEC = 1, 3
+    cases = [
+        (64, 896, 4864, DEC),        # tiny: 152 panels < 256 CUs
+        (4096, 896, 4864, DP),       # 0.5B prefill
+        (1, 3584, 18944, DEC), (16, 3584, 18944, DEC), (32, 3584, 18944, DEC),
+        (64, 3584, 18944, DP),       # 592 panels >= 256 CUs: panel schedule
+        (128, 3584, 18944, DP), (8192, 3584, 18944, DP),
+        (32, 8192, 29568, DEC), (4096, 8192, 29568, DP),
+        (48, 6144, 12288, DP),       # 384 panels >= 256 CUs
+        (33, 64, 128, DEC),          # 4 panels
+    ]
+    for M, K, N, want in cases:
+        assert L.swiglu_choose_variant(M, K, N) == want, (M, K, N)
+    # no AUTO choice needs a workspace at these shapes
+    for M, K, N, _ in cases:
+        assert L.swiglu_workspace_bytes(M, K, N, 0) == 0, (M, K, N)
+
+
+def test_auto_split_k_choice_and_workspace():
+    """Split-K only while the data-parallel tiles fill under half the CUs, with
+    at most K / (16 M) splits; its workspace is S fp32 partial sums of Gate and
+    Up, S * M * 2N * 4 bytes."""
+    L = sw.lib()
+    cases = [
+        # M, K, N, splits: 8 tiles of 128x128 -> cap K/(16M) = 4
+        (128, 8192, 1024, 4),
+        # 16 tiles -> cap 2
+        (256, 8192, 1024, 2),
+        # 4 tiles -> cap 4096 // 1600 = 2
+        (100, 4096, 512, 2),
+    ]
+    for M, K, N, S in cases:
+        assert L.swiglu_choose_variant(M, K, N) == 2, (M, K, N)
+        assert L.swiglu_workspace_bytes(M, K, N, 0) == S * M * 2 * N * 4, (M, K, N)
+    # K too short for two splits of at least 16 M: data-parallel, no workspace
+    assert L.swiglu_choose_variant(128, 1024, 1024) == 1
+    assert L.swiglu_workspace_bytes(128, 1024, 1024, 0) == 0
+    # enough data-parallel tiles to fill half the CUs: data-parallel
+    assert L.swiglu_choose_variant(2048, 8192, 256) == 1
