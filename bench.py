@@ -417,6 +417,9 @@ def main():
                     help="also time every workload point and the unfused pipeline (stderr)")
     ap.add_argument("--ceilings", action="store_true",
                     help="also measure the MFMA / HBM / vendor-GEMM ceilings (stderr)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="only time the unfused pipeline (two GEMM launches, then the SiLU*Up kernel) at "
+                         "the workload point, print an UNFUSED line (stderr) and exit (for counter runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (byte-counter calibration) and exit")
     args = ap.parse_args()
@@ -444,6 +447,12 @@ def main():
         ceilings(stream)
     w = inputs.BY_NAME[args.workload]
     M = args.m or w.m_max
+    if args.unfused:
+        tu = bench_unfused(w, M, args.steps, args.warmup, stream, args.prewarm)
+        log("UNFUSED " + json.dumps({"workload": w.name, "M": M, "K": w.K, "N": w.N,
+                                     "us": round(tu * 1e6, 2),
+                                     "model_bytes": fused_bytes(M, w.K, w.N) + unfused_extra_bytes(M, w.K, w.N)}))
+        return
 
     if args.dtype == "fp8":
         res = bench_point_fp8(w, M, args.steps, args.warmup, stream, args.prewarm)

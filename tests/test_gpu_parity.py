@@ -64,6 +64,9 @@ SMALL_SHAPES = [
     # 352 tiles of 256x128: the last 6 column tiles run as 128-row tiles in the
     # same launch; partial last column tile, M tail, ragged K
     (4000, 200, 2696),
+    # persistent 128-row tiles with the epilogue overlapped: more tiles than
+    # CUs (each workgroup switches tiles mid-ring), M and N tails, ragged K
+    (1500, 328, 3000), (2048, 896, 4864),
 ]
 
 
