@@ -378,6 +378,22 @@ def ceilings(stream):
     return out
 
 
+def mfma_probe(blocks=2048, iters=1000, calls=3):
+    """The MFMA-only loop (no memory traffic) a few times: what the matrix-core
+    counters read when the matrix cores are the only busy unit."""
+    import torch
+    import swiglu_gated_mlp_amd as sw
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        sw.swiglu_probe_mfma(sink, blocks, iters)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / calls
+    log("mfma probe: %d calls of %d workgroups x %d iterations, %.1f TFLOP/s (host clock)"
+        % (calls, blocks, iters, blocks * 4 * iters * 8 * 32768 / dt / 1e12))
+
+
 def copy_probe(mib):
     """A plain device copy of a known size (the byte-counter calibration run)."""
     import torch
@@ -420,6 +436,8 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="only time the unfused pipeline (two GEMM launches, then the SiLU*Up kernel) at "
                          "the workload point, print an UNFUSED line (stderr) and exit (for counter runs)")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only run the MFMA-only loop a few times and exit (matrix-core counter calibration)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (byte-counter calibration) and exit")
     args = ap.parse_args()
@@ -441,6 +459,9 @@ def main():
     sw.lib()
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.mfma_probe:
+        mfma_probe()
         return
     stream = torch.cuda.current_stream()
     if args.ceilings:
