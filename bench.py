@@ -443,7 +443,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build runs the fused SwiGLU product on a "
+        print("bench.py measures one GPU only: the fused SwiGLU product runs on a "
               "single MI355X (no multi-GPU path); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

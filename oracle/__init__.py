@@ -21,7 +21,8 @@ Inference" as summarised on gist.science ("Summary"):
 * ``bf16_rne``    -- rounding of the fp32 result to the bf16 output type.
 * ``swiglu_fp8``  -- the product from FP8 E4M3 operands with per-tensor
   scales (the pages' remark that quantised GEMMs raise SwiGLU's relative cost,
-  Summary, "Problem Statement"; the scale convention is this build's reading).
+  Summary, "Problem Statement"; the pages fix no scale convention, so per-tensor
+  scales are a reading of them).
 * ``mlp``         -- the gated MLP block the pages' "share of MLP time" refers
   to: the bf16 SwiGLU product Y, then the down projection Z = bf16(Y x W3) with
   fp32 accumulation (Summary, "Problem Statement"; the pages do not spell the
