@@ -67,6 +67,9 @@ SMALL_SHAPES = [
     # persistent 128-row tiles with the epilogue overlapped: more tiles than
     # CUs (each workgroup switches tiles mid-ring), M and N tails, ragged K
     (1500, 328, 3000), (2048, 896, 4864),
+    # the smallest legal K and N (one 16-byte chunk of k; one 8-column piece of
+    # a 128-column tile) on the decode, 128-row and 256-row schedules
+    (3, 8, 8), (70, 8, 24), (300, 24, 8), (2100, 8, 8),
 ]
 
 
