@@ -118,6 +118,30 @@ def _dev_bf16(t: torch.Tensor, name: str) -> int:
     raise ValueError("%s must be contiguous" % name)
 
 
+def _shape(t, shape, name: str) -> None:
+    """A tensor the library reads or writes must hold exactly this shape (the C
+    ABI takes bare pointers and trusts the sizes)."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must be %s (got %s)" % (name, list(shape), list(t.shape)))
+
+
+_packed_need: dict = {}
+
+
+def _packed_at_least(Wp, K: int, N: int, name: str = "Wp", fp8: bool = False) -> None:
+    """Wp must hold at least the packed weights of a [K,N] pair."""
+    key = (K, N, fp8)
+    need = _packed_need.get(key)
+    if need is None:
+        need = int(lib().swiglu_packed_bytes_fp8(K, N) if fp8 else lib().swiglu_packed_bytes(K, N))
+        _packed_need[key] = need
+    if need == 0:
+        raise ValueError("invalid weight shape [%d,%d]" % (K, N))
+    if Wp.numel() * Wp.element_size() < need:
+        raise ValueError("%s holds %d bytes; packed [%d,%d] weights need %d"
+                         % (name, Wp.numel() * Wp.element_size(), K, N, need))
+
+
 def _stream(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -149,6 +173,7 @@ def swiglu_fused(A: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor, Y: torch.T
     N = W1.shape[1]
     if W1.shape != (K, N) or W2.shape != (K, N):
         raise ValueError("W1, W2 must be [K,N] = [%d,%d]" % (K, N))
+    _shape(Y, (M, N), "Y")
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     st = lib().swiglu_fused(_dev_bf16(A, "A"), _dev_bf16(W1, "W1"), _dev_bf16(W2, "W2"),
@@ -180,6 +205,7 @@ def swiglu_pack_weights(W1: torch.Tensor, W2: torch.Tensor, Wp: torch.Tensor | N
 
 def swiglu_unpack_weights(Wp: torch.Tensor, K: int, N: int, stream=None):
     """Inverse of swiglu_pack_weights; returns (W1, W2)."""
+    _packed_at_least(Wp, K, N)
     W1 = torch.empty((K, N), dtype=torch.bfloat16, device=Wp.device)
     W2 = torch.empty((K, N), dtype=torch.bfloat16, device=Wp.device)
     st = lib().swiglu_unpack_weights(_dev_bf16(Wp, "Wp"), _dev_bf16(W1, "W1"), _dev_bf16(W2, "W2"),
@@ -217,6 +243,8 @@ def swiglu_fused_packed_fp8(A8: torch.Tensor, Wp: torch.Tensor, N: int, sg: floa
                             Y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Y = bf16(SiLU(sg * A8 W1_8) * (su * A8 W2_8)) from FP8 E4M3 bytes."""
     M, K = A8.shape
+    _packed_at_least(Wp, K, N, fp8=True)
+    _shape(Y, (M, N), "Y")
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=A8.device) if Y is None else Y
     st = lib().swiglu_fused_packed_fp8(_dev_u8(A8, "A8"), _dev_u8(Wp, "Wp"), _dev_bf16(Y, "Y"), M, K, N,
                                        float(sg), float(su), _stream(stream))
@@ -255,6 +283,8 @@ def swiglu_fused_packed_interleaved(A: torch.Tensor, Wp: torch.Tensor, N: int, Y
                                     stream=None) -> torch.Tensor:
     """Y = SiLU(A W1) * (A W2) from column-interleaved packed weights."""
     M, K = A.shape
+    _packed_at_least(Wp, K, N)
+    _shape(Y, (M, N), "Y")
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=A.device) if Y is None else Y
     st = lib().swiglu_fused_packed_interleaved(_dev_bf16(A, "A"), _dev_bf16(Wp, "Wp"), _dev_bf16(Y, "Y"),
                                                M, K, N, _stream(stream))
@@ -319,6 +349,8 @@ def swiglu_fused_packed(A: torch.Tensor, Wp: torch.Tensor, N: int, Y: torch.Tens
     ``workspace`` may be a uint8 tensor of at least swiglu_workspace_bytes()
     bytes, a Workspace, or None (a cached per-stream Workspace is used)."""
     M, K = A.shape
+    _packed_at_least(Wp, K, N)
+    _shape(Y, (M, N), "Y")
     if isinstance(variant, str):
         variant = VARIANTS[variant]
     s = _stream(stream)
@@ -347,6 +379,8 @@ def swiglu_gemm_bf16(A: torch.Tensor, W: torch.Tensor, C: torch.Tensor | None = 
     """C = bf16(A @ W) with fp32 accumulation (one GEMM of the unfused pipeline)."""
     M, K = A.shape
     N = W.shape[1]
+    _shape(W, (K, N), "W")
+    _shape(C, (M, N), "C")
     if C is None:
         C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     st = lib().swiglu_gemm_bf16(_dev_bf16(A, "A"), _dev_bf16(W, "W"), _dev_bf16(C, "C"), M, K, N,
@@ -360,6 +394,7 @@ def swiglu_silu_mul(G: torch.Tensor, U: torch.Tensor, Y: torch.Tensor | None = N
     """Y = bf16(SiLU(G) * U), element-wise (the unfused pipeline's activation)."""
     if G.shape != U.shape:
         raise ValueError("G and U shapes differ")
+    _shape(Y, G.shape, "Y")
     if Y is None:
         Y = torch.empty_like(G)
     st = lib().swiglu_silu_mul(_dev_bf16(G, "G"), _dev_bf16(U, "U"), _dev_bf16(Y, "Y"), G.numel(),
@@ -374,6 +409,9 @@ def swiglu_unfused(A: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor, G: torch
     Returns (G, U, Y)."""
     M, K = A.shape
     N = W1.shape[1]
+    for t, shape, name in ((W1, (K, N), "W1"), (W2, (K, N), "W2"), (G, (M, N), "G"), (U, (M, N), "U"),
+                           (Y, (M, N), "Y")):
+        _shape(t, shape, name)
     mk = lambda: torch.empty((M, N), dtype=torch.bfloat16, device=A.device)  # noqa: E731
     G = mk() if G is None else G
     U = mk() if U is None else U
@@ -392,6 +430,9 @@ def swiglu_mlp_packed(A: torch.Tensor, Wp: torch.Tensor, W3: torch.Tensor, N: in
     """The gated MLP block on packed weights: Y = SiLU(A W1) * (A W2), then
     Z = Y @ W3 (W3 [N,K] row-major, the down projection).  Returns (Y, Z)."""
     M, K = A.shape
+    _packed_at_least(Wp, K, N)
+    for t, shape, name in ((W3, (N, K), "W3"), (Y, (M, N), "Y"), (Z, (M, K), "Z")):
+        _shape(t, shape, name)
     if isinstance(variant, str):
         variant = VARIANTS[variant]
     s = _stream(stream)
@@ -417,6 +458,8 @@ def swiglu_mlp_down(Y: torch.Tensor, W3: torch.Tensor, Z: torch.Tensor | None = 
     """The MLP block's down projection alone: Z[M,K] = Y[M,N] @ W3[N,K]."""
     M, N = Y.shape
     K = W3.shape[1]
+    _shape(W3, (N, K), "W3")
+    _shape(Z, (M, K), "Z")
     Z = torch.empty((M, K), dtype=torch.bfloat16, device=Y.device) if Z is None else Z
     st = lib().swiglu_mlp_down(_dev_bf16(Y, "Y"), _dev_bf16(W3, "W3"), _dev_bf16(Z, "Z"), M, K, N,
                                _stream(stream))
@@ -431,6 +474,9 @@ def swiglu_mlp_unfused(A: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor, W3: 
     Z = Y @ W3.  Returns (Y, Z)."""
     M, K = A.shape
     N = W1.shape[1]
+    for t, shape, name in ((W1, (K, N), "W1"), (W2, (K, N), "W2"), (W3, (N, K), "W3"), (G, (M, N), "G"),
+                           (U, (M, N), "U"), (Y, (M, N), "Y"), (Z, (M, K), "Z")):
+        _shape(t, shape, name)
     mk = lambda r, c: torch.empty((r, c), dtype=torch.bfloat16, device=A.device)  # noqa: E731
     G = mk(M, N) if G is None else G
     U = mk(M, N) if U is None else U

@@ -217,6 +217,47 @@ def test_binding_argument_errors():
         sw._dev_bf16(a.float(), "A")
 
 
+def test_binding_rejects_wrong_sizes():
+    """Buffers the library would read or write past their end are rejected by
+    the binding before the call (the C ABI trusts the sizes it is given)."""
+    import torch
+    bf = torch.bfloat16
+    M, K, N = 4, 64, 128
+    A = torch.zeros(M, K, dtype=bf)
+    W = torch.zeros(K, N, dtype=bf)
+    need = sw.swiglu_packed_bytes(K, N)
+    small_wp = torch.zeros(need // 2 - 8, dtype=bf)
+    with pytest.raises(ValueError, match="Wp holds"):
+        sw.swiglu_fused_packed(A, small_wp, N)
+    with pytest.raises(ValueError, match="Wp holds"):
+        sw.swiglu_fused_packed_interleaved(A, small_wp, N)
+    with pytest.raises(ValueError, match="Wp holds"):
+        sw.swiglu_unpack_weights(small_wp, K, N)
+    wp = torch.zeros(need // 2, dtype=bf)
+    with pytest.raises(ValueError, match="Y must be"):
+        sw.swiglu_fused_packed(A, wp, N, Y=torch.zeros(M, N - 8, dtype=bf))
+    with pytest.raises(ValueError, match="Y must be"):
+        sw.swiglu_fused(A, W, W, Y=torch.zeros(M + 1, N, dtype=bf))
+    with pytest.raises(ValueError, match="W must be"):
+        sw.swiglu_gemm_bf16(A, torch.zeros(K + 8, N, dtype=bf))
+    with pytest.raises(ValueError, match="C must be"):
+        sw.swiglu_gemm_bf16(A, W, C=torch.zeros(M, N + 8, dtype=bf))
+    with pytest.raises(ValueError, match="U must be"):
+        sw.swiglu_unfused(A, W, W, U=torch.zeros(M, 8, dtype=bf))
+    with pytest.raises(ValueError, match="Y must be"):
+        sw.swiglu_silu_mul(torch.zeros(M, N, dtype=bf), torch.zeros(M, N, dtype=bf), Y=torch.zeros(M, 8, dtype=bf))
+    with pytest.raises(ValueError, match="W3 must be"):
+        sw.swiglu_mlp_packed(A, wp, torch.zeros(K, N, dtype=bf), N)
+    with pytest.raises(ValueError, match="Z must be"):
+        sw.swiglu_mlp_down(torch.zeros(M, N, dtype=bf), torch.zeros(N, K, dtype=bf), Z=torch.zeros(M, 8, dtype=bf))
+    with pytest.raises(ValueError, match="W3 must be"):
+        sw.swiglu_mlp_unfused(A, W, W, torch.zeros(K, K, dtype=bf))
+    need8 = int(sw.lib().swiglu_packed_bytes_fp8(K, N))
+    with pytest.raises(ValueError, match="Wp holds"):
+        sw.swiglu_fused_packed_fp8(torch.zeros(M, K, dtype=torch.uint8), torch.zeros(need8 - 16, dtype=torch.uint8),
+                                   N, 1.0, 1.0)
+
+
 def test_auto_dispatch_at_workload_shapes():
     """AUTO's choice is host logic (no device work): decode up to 32 rows and,
     up to 64 rows, while the 32-column weight panels number fewer than the CUs;
