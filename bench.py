@@ -502,6 +502,10 @@ def main():
                         "gbs": round(r["gbs"], 1), "frac": round(frac, 4),
                         "unfused_us": round(tu * 1e6, 2),
                         "speedup_vs_unfused": round(tu / r["per_launch_s"], 3),
+                        # time saved against the time the removed traffic (Gate and
+                        # Up written and read, A read again) takes at peak HBM
+                        "fusion_efficiency": round((tu - r["per_launch_s"]) /
+                                                   (unfused_extra_bytes(mm, ww.K, ww.N) / (HBM_PEAK_GBS * 1e9)), 3),
                         "resolved_variant": r["resolved_variant"]}
                 if "repeats" in r:
                     line.update(repeats=r["repeats"], us_min=round(r["per_min_s"] * 1e6, 2),
