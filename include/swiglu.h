@@ -24,6 +24,10 @@
  *    CUDA tensors) of the current HIP device, 16-byte aligned.
  *  - Ownership: the caller owns every buffer.  The library allocates no memory
  *    on any path and keeps no pointer after a call returns.
+ *  - Sizes: each buffer holds at least the elements its shape implies (A M*K,
+ *    W1/W2 K*N, Y M*N, a packed weight buffer swiglu_packed_bytes(K, N)
+ *    bytes).  The library receives bare pointers and cannot check this; a
+ *    smaller buffer is read or written past its end.
  *  - Streams: `stream` is a hipStream_t (NULL = the default stream).  Work is
  *    enqueued and the call returns without synchronising; device-side faults
  *    surface at the caller's next synchronisation.
