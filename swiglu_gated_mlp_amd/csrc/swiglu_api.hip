@@ -699,11 +699,11 @@ swiglu_status swiglu_gemm_bf16(const swiglu_bf16* A, const swiglu_bf16* W, swigl
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (M <= 32) {
-        a.tiles_m = (int)ceil_div(M, 32); a.tiles_n = (int)ceil_div(N, 256);
-        e = launch_tile<32, 256, 1, 4, false, false, false>(a, a.tiles_m * a.tiles_n, s);
+        a.tiles_m = (int)ceil_div(M, 32); a.tiles_n = (int)ceil_div(N, 128);
+        e = launch_tile<32, 128, 1, 2, false, false, false>(a, a.tiles_m * a.tiles_n, s);
     } else if (M <= 64) {
-        a.tiles_m = 1; a.tiles_n = (int)ceil_div(N, 256);
-        e = launch_tile<64, 256, 2, 2, false, false, false>(a, a.tiles_m * a.tiles_n, s);
+        a.tiles_m = 1; a.tiles_n = (int)ceil_div(N, 128);
+        e = launch_tile<64, 128, 2, 1, false, false, false>(a, a.tiles_m * a.tiles_n, s);
     } else if (M <= 2048) {
         a.tiles_m = (int)ceil_div(M, 128); a.tiles_n = (int)ceil_div(N, 256);
         e = launch_prefill<128, 256, 2, 2, false, swk::W_ROW_SINGLE>(a, a.tiles_m * a.tiles_n, s);
