@@ -38,7 +38,9 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 (256 CU x 4096 flop/clk 
 MFMA_FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 (published)
 HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
 MALL_BYTES = 256 << 20
-DEFAULT_WORKLOAD = "qwen2.5-0.5B-prefill"
+# the largest single-GPU workload point: 72B MLP width, 4096 tokens
+DEFAULT_WORKLOAD = "qwen2.5-72B"
+DEFAULT_M = 4096
 
 
 def log(msg):
@@ -177,6 +179,26 @@ def measured_traffic(workload_label):
     return t.get("traffic_bytes_per_dispatch")
 
 
+def cpu_model():
+    """The host CPU's model name (lscpu's "Model name", else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        r = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10)
+        for line in r.stdout.splitlines():
+            if line.strip().lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, M, target_s=12.0):
     """Time the CPU oracle (as it stands) on the first rows of the same workload:
     a few rows first to estimate the rate, then enough rows for ~target_s (the
@@ -206,6 +228,7 @@ def cpu_baseline(w, M, target_s=12.0):
         "value": round(reps * flops(m, w.K, w.N) / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(oracle.max_threads()),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": "first %d of %d rows of A, all %d columns (K=%d), %d run(s); %.1f s"
                   % (m, M, w.N, w.K, reps, dt),
@@ -467,7 +490,7 @@ def main():
     if args.ceilings:
         ceilings(stream)
     w = inputs.BY_NAME[args.workload]
-    M = args.m or w.m_max
+    M = args.m or (DEFAULT_M if w.name == DEFAULT_WORKLOAD else w.m_max)
     if args.unfused:
         tu = bench_unfused(w, M, args.steps, args.warmup, stream, args.prewarm)
         log("UNFUSED " + json.dumps({"workload": w.name, "M": M, "K": w.K, "N": w.N,

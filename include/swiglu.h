@@ -294,9 +294,9 @@ swiglu_status swiglu_unfused(const swiglu_bf16 *A, const swiglu_bf16 *W1,
  * speedup falling with model size in [Summary: Results]); these two entry
  * points are that MLP, fused and unfused, so the share can be measured.
  *
- * The down projection is a plain GEMM outside the fused product and runs on
- * rocBLAS (bf16 in and out, fp32 compute; one handle per device, created on
- * first use and kept for the process), in both entry points.
+ * The down projection is a plain GEMM outside the fused product; it runs on
+ * this library's own GEMM (swiglu_gemm_bf16 with Y as the activations and
+ * W3 as the row-major weights), in both entry points.
  *
  * swiglu_mlp_packed:  Y = swiglu_fused_packed(A, Wp, ...), then Z = gemm(Y,
  *   W3).  Y is a caller-owned [M,N] bf16 device buffer and holds the SwiGLU
@@ -310,7 +310,7 @@ swiglu_status swiglu_unfused(const swiglu_bf16 *A, const swiglu_bf16 *W1,
  *   both entry points above end with); Z must not overlap Y or W3.
  * Both: K and N multiples of 8, pointers 16-byte aligned; M == 0 returns
  * SWIGLU_OK without a launch; the validation codes return before any launch;
- * a rocBLAS failure returns SWIGLU_ERR_HIP; work is enqueued on `stream`
+ * a launch failure returns SWIGLU_ERR_HIP; work is enqueued on `stream`
  * with no synchronisation.
  * ---------------------------------------------------------------------- */
 swiglu_status swiglu_mlp_packed(const swiglu_bf16 *A, const swiglu_bf16 *Wp,

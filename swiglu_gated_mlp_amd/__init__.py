@@ -190,6 +190,7 @@ def swiglu_pack_weights(W1: torch.Tensor, W2: torch.Tensor, Wp: torch.Tensor | N
                         stream=None) -> torch.Tensor:
     """Pack W1, W2 [K,N] into the per-128-column-tile interleaved layout."""
     K, N = W1.shape
+    _shape(W2, (K, N), "W2")
     nbytes = swiglu_packed_bytes(K, N)
     if nbytes == 0:
         raise ValueError("invalid weight shape [%d,%d]" % (K, N))
@@ -229,6 +230,9 @@ def _dev_u8(t: torch.Tensor, name: str) -> int:
 def swiglu_pack_weights_fp8(W1: torch.Tensor, W2: torch.Tensor, stream=None) -> torch.Tensor:
     """Pack FP8 E4M3 weight bytes W1, W2 [K,N] (uint8) for swiglu_fused_packed_fp8."""
     K, N = W1.shape
+    _shape(W2, (K, N), "W2")
+    _dev_u8(W1, "W1")
+    _dev_u8(W2, "W2")
     nbytes = int(lib().swiglu_packed_bytes_fp8(K, N))
     if nbytes == 0:
         raise ValueError("invalid FP8 weight shape [%d,%d] (K must be a multiple of 16)" % (K, N))
@@ -256,6 +260,7 @@ def swiglu_pack_weights_interleaved(W1: torch.Tensor, W2: torch.Tensor, Wp: torc
                                     stream=None) -> torch.Tensor:
     """Pack W1, W2 [K,N] column-granular interleaved (Gate even, Up odd rows)."""
     K, N = W1.shape
+    _shape(W2, (K, N), "W2")
     nbytes = swiglu_packed_bytes(K, N)
     if nbytes == 0:
         raise ValueError("invalid weight shape [%d,%d]" % (K, N))
@@ -271,6 +276,7 @@ def swiglu_pack_weights_interleaved(W1: torch.Tensor, W2: torch.Tensor, Wp: torc
 
 def swiglu_unpack_weights_interleaved(Wp: torch.Tensor, K: int, N: int, stream=None):
     """Inverse of swiglu_pack_weights_interleaved; returns (W1, W2)."""
+    _packed_at_least(Wp, K, N)
     W1 = torch.empty((K, N), dtype=torch.bfloat16, device=Wp.device)
     W2 = torch.empty((K, N), dtype=torch.bfloat16, device=Wp.device)
     st = lib().swiglu_unpack_weights_interleaved(_dev_bf16(Wp, "Wp"), _dev_bf16(W1, "W1"),

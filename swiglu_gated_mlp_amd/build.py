@@ -39,9 +39,9 @@ def compile_flags():
 
 
 def link_flags():
-    # rocBLAS serves the MLP block's down projection (a plain GEMM)
-    lib = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
-    return ["-L", lib, "-Wl,-rpath," + lib, "-lrocblas"]
+    # the HIP runtime only: every kernel, the MLP block's down projection
+    # included, is this library's own
+    return []
 
 
 def build(verbose: bool = False) -> str:

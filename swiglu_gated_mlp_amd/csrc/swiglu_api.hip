@@ -7,7 +7,6 @@
 #include "swiglu_probe.h"
 
 #include <hip/hip_runtime.h>
-#include <rocblas/rocblas.h>
 
 #include <algorithm>
 #include <atomic>
@@ -755,33 +754,12 @@ swiglu_status swiglu_unfused(const swiglu_bf16* A, const swiglu_bf16* W1, const 
 
 // ---------------------------------------------------------------------------
 // Down projection of the MLP block, Z[M,K] = bf16(Y[M,N] x W3[N,K]): a plain
-// GEMM outside the fused product, so it goes to rocBLAS (bf16 in and out,
-// fp32 compute).  Row-major Z = Y W3 is, column-major, Z^T[K,M] = W3^T[K,N]
-// Y^T[N,M] with no transposes.  One handle per device for the process; the
-// stream is set per call under the lock, so calls on different streams do
-// not race on the handle.
+// GEMM on this library's own kernel, with Y as the activations (N deep) and
+// the row-major W3 as the weights (K output columns).
 // ---------------------------------------------------------------------------
 swiglu_status down_projection(const swiglu_bf16* Y, const swiglu_bf16* W3, swiglu_bf16* Z, int64_t M,
                               int64_t N, int64_t K, void* stream) {
-    static std::mutex mu;
-    static rocblas_handle handles[64] = {};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e);
-    if (dev < 0 || dev >= 64) return hip_fail(hipErrorInvalidDevice);
-    std::lock_guard<std::mutex> lock(mu);
-    if (!handles[dev] && rocblas_create_handle(&handles[dev]) != rocblas_status_success) {
-        handles[dev] = nullptr;
-        return hip_fail(hipErrorNotInitialized);
-    }
-    rocblas_handle h = handles[dev];
-    if (rocblas_set_stream(h, (hipStream_t)stream) != rocblas_status_success) return hip_fail(hipErrorInvalidHandle);
-    const float alpha = 1.0f, beta = 0.0f;
-    const rocblas_status rs = rocblas_gemm_ex_64(
-        h, rocblas_operation_none, rocblas_operation_none, K, M, N, &alpha, W3, rocblas_datatype_bf16_r, K, Y,
-        rocblas_datatype_bf16_r, N, &beta, Z, rocblas_datatype_bf16_r, K, Z, rocblas_datatype_bf16_r, K,
-        rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-    return rs == rocblas_status_success ? SWIGLU_OK : hip_fail(hipErrorLaunchFailure);
+    return swiglu_gemm_bf16(Y, W3, Z, M, N, K, stream);
 }
 
 swiglu_status swiglu_mlp_down(const swiglu_bf16* Y, const swiglu_bf16* W3, swiglu_bf16* Z, int64_t M, int64_t K,

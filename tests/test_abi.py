@@ -252,6 +252,16 @@ def test_binding_rejects_wrong_sizes():
         sw.swiglu_mlp_down(torch.zeros(M, N, dtype=bf), torch.zeros(N, K, dtype=bf), Z=torch.zeros(M, 8, dtype=bf))
     with pytest.raises(ValueError, match="W3 must be"):
         sw.swiglu_mlp_unfused(A, W, W, torch.zeros(K, K, dtype=bf))
+    # the pack entry points read W2 at W1's shape; the interleaved unpack
+    # reads a whole packed buffer
+    with pytest.raises(ValueError, match="W2 must be"):
+        sw.swiglu_pack_weights(W, torch.zeros(K - 8, N, dtype=bf))
+    with pytest.raises(ValueError, match="W2 must be"):
+        sw.swiglu_pack_weights_interleaved(W, torch.zeros(K, N - 8, dtype=bf))
+    with pytest.raises(ValueError, match="W2 must be"):
+        sw.swiglu_pack_weights_fp8(torch.zeros(K, N, dtype=torch.uint8), torch.zeros(K, 8, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="Wp holds"):
+        sw.swiglu_unpack_weights_interleaved(small_wp, K, N)
     need8 = int(sw.lib().swiglu_packed_bytes_fp8(K, N))
     with pytest.raises(ValueError, match="Wp holds"):
         sw.swiglu_fused_packed_fp8(torch.zeros(M, K, dtype=torch.uint8), torch.zeros(need8 - 16, dtype=torch.uint8),
