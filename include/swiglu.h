@@ -196,6 +196,34 @@ swiglu_status swiglu_fused_packed(const swiglu_bf16 *A, const swiglu_bf16 *Wp,
 int swiglu_choose_variant(int64_t M, int64_t K, int64_t N);
 
 /* ------------------------------------------------------------------------
+ * swiglu_fused_packed_noalloc -- swiglu_fused_packed for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The caller passes the inputs and the
+ * output only; the split-K schedule's fp32 partial sums go to a scratch
+ * array the library keeps in device memory, SWIGLU_NOALLOC_SCRATCH_BYTES
+ * bytes per device, held from the library's load until the process ends.
+ * The call allocates nothing on any path (no hipMalloc, no hipFree, no
+ * allocating library routine).
+ *   A, Wp, Y, M, K, N, variant, stream: as swiglu_fused_packed; the schedule
+ *     is the one swiglu_fused_packed runs for the same arguments, so the two
+ *     give the same Y.
+ *   Returns SWIGLU_ERR_WORKSPACE, before any HIP call, when that schedule's
+ *     partial sums (swiglu_workspace_bytes(M, K, N, variant)) exceed
+ *     SWIGLU_NOALLOC_SCRATCH_BYTES; AUTO, DATA_PARALLEL, DECODE and
+ *     SEQUENTIAL need none at the Qwen-2.5 shapes.  Other validation codes as
+ *     swiglu_fused_packed.
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents (nothing in it needs clearing: each split writes all of
+ * its partial sums before the reduction reads them).  Calls that overlap in
+ * time on one device race on it: issue them on one stream, or order them.
+ * ---------------------------------------------------------------------- */
+#define SWIGLU_NOALLOC_SCRATCH_BYTES (32u << 20)
+swiglu_status swiglu_fused_packed_noalloc(const swiglu_bf16 *A,
+                                          const swiglu_bf16 *Wp, swiglu_bf16 *Y,
+                                          int64_t M, int64_t K, int64_t N,
+                                          int variant, void *stream);
+
+/* ------------------------------------------------------------------------
  * FP8 operands.  The pages note that quantised GEMMs (FP8, INT4) raise the
  * relative cost of SwiGLU's memory traffic ([Summary: Problem Statement]) but
  * give no scale convention; this library takes per-tensor scales:

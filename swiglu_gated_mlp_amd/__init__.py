@@ -46,6 +46,7 @@ SIGNATURES = {
     "swiglu_fused_packed": ([_P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, ctypes.c_int, _P],
                             ctypes.c_int),
     "swiglu_choose_variant": ([_I64, _I64, _I64], ctypes.c_int),
+    "swiglu_fused_packed_noalloc": ([_P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P], ctypes.c_int),
     "swiglu_packed_bytes_fp8": ([_I64, _I64], ctypes.c_size_t),
     "swiglu_pack_weights_fp8": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
     "swiglu_fused_packed_fp8": ([_P, _P, _P, _I64, _I64, _I64, ctypes.c_float, ctypes.c_float, _P], ctypes.c_int),
@@ -377,6 +378,27 @@ def swiglu_fused_packed(A: torch.Tensor, Wp: torch.Tensor, N: int, Y: torch.Tens
     st = lib().swiglu_fused_packed(_dev_bf16(A, "A"), _dev_bf16(Wp, "Wp"), _dev_bf16(Y, "Y"), M, K, N,
                                    _ptr(ws), ws_bytes, int(variant), s)
     _check("swiglu_fused_packed", st)
+    return Y
+
+
+#: bytes of the library's per-device scratch array (swiglu_fused_packed_noalloc)
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def swiglu_fused_packed_noalloc(A: torch.Tensor, Wp: torch.Tensor, Y: torch.Tensor, variant: int = VARIANT_AUTO,
+                                stream=None) -> torch.Tensor:
+    """swiglu_fused_packed into the caller's Y with no allocation: split-K
+    partial sums go to the library's own device scratch array (the binding
+    allocates nothing either; Y [M,N] is required)."""
+    M, K = A.shape
+    N = Y.shape[1]
+    _packed_at_least(Wp, K, N)
+    _shape(Y, (M, N), "Y")
+    if isinstance(variant, str):
+        variant = VARIANTS[variant]
+    st = lib().swiglu_fused_packed_noalloc(_dev_bf16(A, "A"), _dev_bf16(Wp, "Wp"), _dev_bf16(Y, "Y"), M, K, N,
+                                           int(variant), _stream(stream))
+    _check("swiglu_fused_packed_noalloc", st)
     return Y
 
 

@@ -18,6 +18,13 @@
 #include "fused_kernels.hpp"
 #include "probe_kernels.hpp"
 
+// Device scratch of swiglu_fused_packed_noalloc: the split-K partial sums of
+// callers that cannot allocate.  One copy per device, held from the
+// library's load until the process ends; every no-allocation call on a
+// device shares it.  Host code never uses this name as an address: the
+// device address comes from hipGetSymbolAddress (scratch_device_ptr below).
+static __device__ __align__(256) unsigned char scratch[SWIGLU_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -114,6 +121,28 @@ int cu_count_now() {
         cache[dev] = n;
     }
     return cache[dev];
+}
+
+// Device address of `scratch` on the current device: looked up once per
+// device (with that device current) and kept; each device holds its own copy
+// of the array at its own address.
+hipError_t scratch_device_ptr(void** out) {
+    static std::mutex mu;
+    static void* ptrs[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        ptrs[dev] = p;
+    }
+    *out = ptrs[dev];
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------
@@ -679,6 +708,32 @@ swiglu_status swiglu_fused_packed(const swiglu_bf16* A, const swiglu_bf16* Wp, s
                             args, 0, (hipStream_t)stream);
     }
     return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
+}
+
+// swiglu_fused_packed with the split-K partial sums in the library's own
+// device scratch array instead of a caller's workspace: no allocation on any
+// path.  The schedule is the one swiglu_fused_packed would run; a schedule
+// whose partial sums exceed the array is rejected before any HIP call.
+swiglu_status swiglu_fused_packed_noalloc(const swiglu_bf16* A, const swiglu_bf16* Wp, swiglu_bf16* Y,
+                                          int64_t M, int64_t K, int64_t N, int variant, void* stream) {
+    swiglu_status st = check_shape(M, K, N);
+    if (st != SWIGLU_OK) return st;
+    if (!variant_known(variant)) return SWIGLU_ERR_BAD_VARIANT;
+    if (variant == SWIGLU_VARIANT_DECODE && M > kDecodeMaxM) return SWIGLU_ERR_BAD_VARIANT;
+    if (M == 0) return SWIGLU_OK;
+    if (!A || !Wp || !Y) return SWIGLU_ERR_NULL_POINTER;
+    // products chunked by rows run on the data-parallel schedule, which
+    // needs no partial sums; otherwise the plan swiglu_fused_packed makes
+    size_t need = 0;
+    if (M <= stream_rows_limit(K, 2)) need = split_workspace_bytes(make_plan(M, K, N, variant, cu_count_now()), M, N);
+    if (need > (size_t)SWIGLU_NOALLOC_SCRATCH_BYTES) return SWIGLU_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need > 0) {
+        const hipError_t e = scratch_device_ptr(&ws);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return swiglu_fused_packed(A, Wp, Y, M, K, N, ws, need > 0 ? (size_t)SWIGLU_NOALLOC_SCRATCH_BYTES : 0, variant,
+                               stream);
 }
 
 swiglu_status swiglu_gemm_bf16(const swiglu_bf16* A, const swiglu_bf16* W, swiglu_bf16* C,

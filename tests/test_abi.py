@@ -185,6 +185,22 @@ def test_fp8_errors():
     assert P(W1_, W2_, W1_ + 16, 64, 64, None) == ALIAS
 
 
+def test_noalloc_host_checks():
+    """The no-allocation entry point validates like swiglu_fused_packed and
+    rejects, before any HIP call, a schedule whose split-K partial sums do not
+    fit the library's scratch array."""
+    L = sw.lib()
+    F = L.swiglu_fused_packed_noalloc
+    assert F(None, None, None, 0, 64, 64, 0, None) == OK
+    assert F(A_, WP_, Y_, 4, 60, 64, 0, None) == UNSUP
+    assert F(A_, WP_, Y_, 4, 64, 64, 9, None) == VARIANT
+    assert F(A_, WP_, Y_, 65, 64, 64, 3, None) == VARIANT
+    assert F(A_, None, Y_, 4, 64, 64, 0, None) == NULLP
+    big = L.swiglu_workspace_bytes(128, 3584, 18944, 2)
+    assert big > sw.NOALLOC_SCRATCH_BYTES
+    assert F(A_, WP_, Y_, 128, 3584, 18944, 2, None) == WS
+
+
 def test_workspace_holds_fp32_partials():
     L = sw.lib()
     # split-K workspace = splits x M x 2N fp32 partial sums; zero for the
