@@ -311,19 +311,52 @@ def bench_point(w, M, steps, warmup, variant, stream, prewarm_s=0.0, layout="per
 
 
 def bench_unfused(w, M, steps, warmup, stream, prewarm_s=0.0):
+    """The unfused pipeline on the library's fastest GEMM: W1 and W2 in the
+    single-weight pack (packed once, like the fused weights), two GEMM calls
+    writing bf16 Gate and Up, then the SiLU * Up kernel reading them back;
+    rotated sets like the fused call."""
     import torch
     import swiglu_gated_mlp_amd as sw
     from swiglu_gated_mlp_amd import inputs
     dev = torch.device("cuda:0")
     K, N = w.K, w.N
     A, W1, W2 = inputs.workload_tensors(w, M)
-    Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
-    G = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    U = torch.empty_like(G)
-    Y = torch.empty_like(G)
-    fn = lambda: sw.swiglu_unfused(Ad, W1d, W2d, G, U, Y)  # noqa: E731
-    sec = time_gpu([fn], steps, warmup, stream, prewarm_s)
+    R = max(1, math.ceil(2 * MALL_BYTES / (fused_bytes(M, K, N) + unfused_extra_bytes(M, K, N))))
+    sets = []
+    for _ in range(R):
+        W1d, W2d = W1.to(dev), W2.to(dev)
+        sets.append((A.to(dev), sw.swiglu_gemm_pack_weight(W1d), sw.swiglu_gemm_pack_weight(W2d),
+                     torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                     torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                     torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+        del W1d, W2d
+    torch.cuda.synchronize()
+    fns = [(lambda t=t: sw.swiglu_unfused_packed(t[0], t[1], t[2], N, t[3], t[4], t[5])) for t in sets]
+    sec = time_gpu(fns, steps, warmup, stream, prewarm_s)
     return sec / steps
+
+
+def bench_gemm(w, M, steps, warmup, stream, prewarm_s=0.0):
+    """One GEMM of the unfused pipeline alone, C = A @ W1 on the single-weight
+    pack, over rotated sets: per-call seconds, TFLOP/s (2 M K N) and GB/s
+    (A, W and C once each)."""
+    import torch
+    import swiglu_gated_mlp_amd as sw
+    from swiglu_gated_mlp_amd import inputs
+    dev = torch.device("cuda:0")
+    K, N = w.K, w.N
+    A, W1, _ = inputs.workload_tensors(w, M)
+    nbytes = 2.0 * (M * K + K * N + M * N)
+    R = max(1, math.ceil(2 * MALL_BYTES / nbytes))
+    W1d = W1.to(dev)
+    sets = [(A.to(dev), sw.swiglu_gemm_pack_weight(W1d), torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+            for _ in range(R)]
+    del W1d
+    torch.cuda.synchronize()
+    fns = [(lambda t=t: sw.swiglu_gemm_packed(t[0], t[1], N, t[2])) for t in sets]
+    per = time_gpu(fns, steps, warmup, stream, prewarm_s) / steps
+    return {"gemm_us": round(per * 1e6, 2), "gemm_tflops": round(2.0 * M * K * N / per / 1e12, 2),
+            "gemm_gbs": round(nbytes / per / 1e9, 1)}
 
 
 def bench_mlp(w, M, steps, warmup, stream, prewarm_s=0.0):
@@ -342,14 +375,16 @@ def bench_mlp(w, M, steps, warmup, stream, prewarm_s=0.0):
     sets = []
     for _ in range(R):
         W1d, W2d = W1.to(dev), W2.to(dev)
-        sets.append(dict(A=A.to(dev), W1=W1d, W2=W2d, Wp=sw.swiglu_pack_weights(W1d, W2d), W3=W3.to(dev),
+        sets.append(dict(A=A.to(dev), W1g=sw.swiglu_gemm_pack_weight(W1d), W2g=sw.swiglu_gemm_pack_weight(W2d),
+                         Wp=sw.swiglu_pack_weights(W1d, W2d), W3g=sw.swiglu_gemm_pack_weight(W3.to(dev)),
                          G=mk(M, N), U=mk(M, N), Y=mk(M, N), Z=mk(M, K), ws=sw.Workspace(dev)))
+        del W1d, W2d
     torch.cuda.synchronize()
-    fused = [(lambda d=d: sw.swiglu_mlp_packed(d["A"], d["Wp"], d["W3"], N, Y=d["Y"], Z=d["Z"],
+    fused = [(lambda d=d: sw.swiglu_mlp_packed(d["A"], d["Wp"], d["W3g"], N, Y=d["Y"], Z=d["Z"],
                                                workspace=d["ws"])) for d in sets]
-    unfused = [(lambda d=d: sw.swiglu_mlp_unfused(d["A"], d["W1"], d["W2"], d["W3"], d["G"], d["U"],
+    unfused = [(lambda d=d: sw.swiglu_mlp_unfused(d["A"], d["W1g"], d["W2g"], d["W3g"], N, d["G"], d["U"],
                                                   d["Y"], d["Z"])) for d in sets]
-    down = [(lambda d=d: sw.swiglu_mlp_down(d["Y"], d["W3"], d["Z"])) for d in sets]
+    down = [(lambda d=d: sw.swiglu_mlp_down(d["Y"], d["W3g"], K, d["Z"])) for d in sets]
     tf = time_gpu(fused, steps, warmup, stream, prewarm_s) / steps
     tu = time_gpu(unfused, steps, warmup, stream, prewarm_s) / steps
     td = time_gpu(down, steps, warmup, stream, prewarm_s) / steps
@@ -535,6 +570,7 @@ def main():
                                 us_max=round(r["per_max_s"] * 1e6, 2))
                 if "graph_per_launch_s" in r:
                     line["graph_us"] = round(r["graph_per_launch_s"] * 1e6, 2)
+                line.update(bench_gemm(ww, mm, max(10, args.steps // 2), 5, stream, args.prewarm))
                 log("POINT " + json.dumps(line))
                 extra.setdefault("points", []).append(line)
                 if args.mlp:

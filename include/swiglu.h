@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SWIGLU_ABI_VERSION 1
+#define SWIGLU_ABI_VERSION 2
 
 typedef uint16_t swiglu_bf16;
 
@@ -315,42 +315,84 @@ swiglu_status swiglu_unfused(const swiglu_bf16 *A, const swiglu_bf16 *W1,
                              int64_t K, int64_t N, void *stream);
 
 /* ------------------------------------------------------------------------
+ * The same unfused pipeline on this library's fastest GEMM: one weight
+ * packed once (model-load time) into the fused pack's block layout, so the
+ * plain GEMM runs on the fused product's own schedules (the weight-streaming
+ * decode kernel for small M, the streaming MFMA grid otherwise) and the
+ * fused-vs-unfused comparison measures the materialised Gate and Up, not a
+ * slower GEMM ([Summary: Problem Statement]: two GEMMs, then the activation
+ * reading them back; [Summary: Results]: the eager baseline).
+ *
+ * Single-weight pack of W [K,N]: tile jt (of ceil(N/256)) holds W's columns
+ * jt*256 + 0..255 as its 256 packed rows, in the block layout of
+ * swiglu_pack_weights (packed row p = g*16 + l%16 of 16-row group g):
+ *   Wg = for jt, kb (64-deep block), g in 0..15, h in 0..1, l in 0..63,
+ *        e in 0..7:  W[k][n], k = kb*64 + h*32 + (l/16)*8 + e,
+ *                             n = jt*256 + g*16 + l%16;  zero past K or N.
+ *
+ * swiglu_gemm_packed_bytes: size of Wg in bytes (0 for an invalid shape).
+ * swiglu_gemm_pack_weight:  W [K,N] -> Wg; Wg must not overlap W.
+ * swiglu_gemm_packed:       C[M,N] = bf16_RNE(A[M,K] x W), fp32 accumulation
+ *   in the fused product's MFMA order; C must not overlap A or Wg.  No
+ *   workspace (split-K is never used); products whose activations reach
+ *   2 GiB run as row chunks.
+ * swiglu_unfused_packed:    G = gemm_packed(A, W1g); U = gemm_packed(A, W2g);
+ *   Y = silu_mul(G, U); G_scratch, U_scratch, Y as in swiglu_unfused.
+ * All: K and N multiples of 8, pointers 16-byte aligned, M == 0 returns
+ * SWIGLU_OK without a launch, validation before any launch, work enqueued
+ * on `stream` with no synchronisation.
+ * ---------------------------------------------------------------------- */
+size_t swiglu_gemm_packed_bytes(int64_t K, int64_t N);
+swiglu_status swiglu_gemm_pack_weight(const swiglu_bf16 *W, swiglu_bf16 *Wg,
+                                      int64_t K, int64_t N, void *stream);
+swiglu_status swiglu_gemm_packed(const swiglu_bf16 *A, const swiglu_bf16 *Wg,
+                                 swiglu_bf16 *C, int64_t M, int64_t K, int64_t N,
+                                 void *stream);
+swiglu_status swiglu_unfused_packed(const swiglu_bf16 *A, const swiglu_bf16 *W1g,
+                                    const swiglu_bf16 *W2g,
+                                    swiglu_bf16 *G_scratch,
+                                    swiglu_bf16 *U_scratch, swiglu_bf16 *Y,
+                                    int64_t M, int64_t K, int64_t N,
+                                    void *stream);
+
+/* ------------------------------------------------------------------------
  * The whole gated MLP block: the SwiGLU product followed by the down
  * projection back to the model width, Z[M,K] = bf16_RNE(Y[M,N] x W3[N,K])
- * with fp32 accumulation, W3 row-major.  The pages give SwiGLU's cost as a
- * share of MLP execution time ([Summary: Problem Statement], 9-37 %; the
- * speedup falling with model size in [Summary: Results]); these two entry
- * points are that MLP, fused and unfused, so the share can be measured.
+ * with fp32 accumulation.  The pages give SwiGLU's cost as a share of MLP
+ * execution time ([Summary: Problem Statement], 9-37 %; the speedup falling
+ * with model size in [Summary: Results]); these entry points are that MLP,
+ * fused and unfused, so the share can be measured.
  *
- * The down projection is a plain GEMM outside the fused product; it runs on
- * this library's own GEMM (swiglu_gemm_bf16 with Y as the activations and
- * W3 as the row-major weights), in both entry points.
+ * The down projection is a plain GEMM outside the fused product: W3 [N,K]
+ * is passed in the single-weight pack (W3g = swiglu_gemm_pack_weight of the
+ * [N,K] matrix, swiglu_gemm_packed_bytes(N, K) bytes) and Z =
+ * swiglu_gemm_packed(Y, W3g) with N as the depth.
  *
- * swiglu_mlp_packed:  Y = swiglu_fused_packed(A, Wp, ...), then Z = gemm(Y,
- *   W3).  Y is a caller-owned [M,N] bf16 device buffer and holds the SwiGLU
+ * swiglu_mlp_packed:  Y = swiglu_fused_packed(A, Wp, ...), then Z = Y x W3.
+ *   Y is a caller-owned [M,N] bf16 device buffer and holds the SwiGLU
  *   product on return; workspace, workspace_bytes and variant are those of
- *   swiglu_fused_packed.  Z must not overlap A, Wp, W3, Y or the workspace;
- *   Y must not overlap W3 (nor the inputs, as in swiglu_fused_packed).
- * swiglu_mlp_unfused: Y = swiglu_unfused(A, W1, W2, G, U, ...), then
- *   Z = gemm(Y, W3); Z must not overlap any other buffer, and no scratch may
- *   overlap W3.
- * swiglu_mlp_down:    the down projection alone, Z = gemm(Y, W3) (the step
- *   both entry points above end with); Z must not overlap Y or W3.
- * Both: K and N multiples of 8, pointers 16-byte aligned; M == 0 returns
+ *   swiglu_fused_packed.  Z must not overlap A, Wp, W3g, Y or the workspace;
+ *   Y must not overlap W3g (nor the inputs, as in swiglu_fused_packed).
+ * swiglu_mlp_unfused: Y = swiglu_unfused_packed(A, W1g, W2g, G, U, ...), then
+ *   Z = Y x W3 (W1g, W2g single-weight packs of W1, W2 [K,N]); Z must not
+ *   overlap any other buffer, and no scratch may overlap W3g.
+ * swiglu_mlp_down:    the down projection alone, Z = Y x W3 (the step both
+ *   entry points above end with); Z must not overlap Y or W3g.
+ * All: K and N multiples of 8, pointers 16-byte aligned; M == 0 returns
  * SWIGLU_OK without a launch; the validation codes return before any launch;
  * a launch failure returns SWIGLU_ERR_HIP; work is enqueued on `stream`
  * with no synchronisation.
  * ---------------------------------------------------------------------- */
 swiglu_status swiglu_mlp_packed(const swiglu_bf16 *A, const swiglu_bf16 *Wp,
-                                const swiglu_bf16 *W3, swiglu_bf16 *Y,
+                                const swiglu_bf16 *W3g, swiglu_bf16 *Y,
                                 swiglu_bf16 *Z, int64_t M, int64_t K, int64_t N,
                                 void *workspace, size_t workspace_bytes,
                                 int variant, void *stream);
-swiglu_status swiglu_mlp_down(const swiglu_bf16 *Y, const swiglu_bf16 *W3,
+swiglu_status swiglu_mlp_down(const swiglu_bf16 *Y, const swiglu_bf16 *W3g,
                              swiglu_bf16 *Z, int64_t M, int64_t K, int64_t N,
                              void *stream);
-swiglu_status swiglu_mlp_unfused(const swiglu_bf16 *A, const swiglu_bf16 *W1,
-                                 const swiglu_bf16 *W2, const swiglu_bf16 *W3,
+swiglu_status swiglu_mlp_unfused(const swiglu_bf16 *A, const swiglu_bf16 *W1g,
+                                 const swiglu_bf16 *W2g, const swiglu_bf16 *W3g,
                                  swiglu_bf16 *G_scratch, swiglu_bf16 *U_scratch,
                                  swiglu_bf16 *Y, swiglu_bf16 *Z, int64_t M,
                                  int64_t K, int64_t N, void *stream);

@@ -54,6 +54,10 @@ SIGNATURES = {
     "swiglu_unpack_weights_interleaved": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
     "swiglu_fused_packed_interleaved": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "swiglu_gemm_bf16": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "swiglu_gemm_packed_bytes": ([_I64, _I64], ctypes.c_size_t),
+    "swiglu_gemm_pack_weight": ([_P, _P, _I64, _I64, _P], ctypes.c_int),
+    "swiglu_gemm_packed": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "swiglu_unfused_packed": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "swiglu_silu_mul": ([_P, _P, _P, _I64, _P], ctypes.c_int),
     "swiglu_unfused": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "swiglu_mlp_packed": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, ctypes.c_int, _P],
@@ -141,6 +145,21 @@ def _packed_at_least(Wp, K: int, N: int, name: str = "Wp", fp8: bool = False) ->
     if Wp.numel() * Wp.element_size() < need:
         raise ValueError("%s holds %d bytes; packed [%d,%d] weights need %d"
                          % (name, Wp.numel() * Wp.element_size(), K, N, need))
+
+
+_gemm_need: dict = {}
+
+
+def _gemm_packed_at_least(Wg, K: int, N: int, name: str = "Wg") -> None:
+    """Wg must hold at least the single-weight pack of a [K,N] weight."""
+    need = _gemm_need.get((K, N))
+    if need is None:
+        need = _gemm_need[(K, N)] = int(lib().swiglu_gemm_packed_bytes(K, N))
+    if need == 0:
+        raise ValueError("invalid weight shape [%d,%d]" % (K, N))
+    if Wg.numel() * Wg.element_size() < need:
+        raise ValueError("%s holds %d bytes; a packed [%d,%d] weight needs %d"
+                         % (name, Wg.numel() * Wg.element_size(), K, N, need))
 
 
 def _stream(stream) -> int:
@@ -417,6 +436,60 @@ def swiglu_gemm_bf16(A: torch.Tensor, W: torch.Tensor, C: torch.Tensor | None = 
     return C
 
 
+def swiglu_gemm_packed_bytes(K: int, N: int) -> int:
+    return int(lib().swiglu_gemm_packed_bytes(K, N))
+
+
+def swiglu_gemm_pack_weight(W: torch.Tensor, Wg: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Pack one weight W [K,N] for swiglu_gemm_packed (256 columns per packed
+    tile, the fused pack's block layout)."""
+    K, N = W.shape
+    nbytes = swiglu_gemm_packed_bytes(K, N)
+    if nbytes == 0:
+        raise ValueError("invalid weight shape [%d,%d]" % (K, N))
+    if Wg is None:
+        Wg = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=W.device)
+    else:
+        _gemm_packed_at_least(Wg, K, N)
+    st = lib().swiglu_gemm_pack_weight(_dev_bf16(W, "W"), _dev_bf16(Wg, "Wg"), K, N, _stream(stream))
+    _check("swiglu_gemm_pack_weight", st)
+    return Wg
+
+
+def swiglu_gemm_packed(A: torch.Tensor, Wg: torch.Tensor, N: int, C: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """C = bf16(A @ W) with fp32 accumulation from a single-weight pack."""
+    M, K = A.shape
+    _gemm_packed_at_least(Wg, K, N)
+    _shape(C, (M, N), "C")
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device) if C is None else C
+    st = lib().swiglu_gemm_packed(_dev_bf16(A, "A"), _dev_bf16(Wg, "Wg"), _dev_bf16(C, "C"), M, K, N,
+                                  _stream(stream))
+    _check("swiglu_gemm_packed", st)
+    return C
+
+
+def swiglu_unfused_packed(A: torch.Tensor, W1g: torch.Tensor, W2g: torch.Tensor, N: int,
+                          G: torch.Tensor | None = None, U: torch.Tensor | None = None,
+                          Y: torch.Tensor | None = None, stream=None):
+    """The unfused pipeline on single-weight packs: G = A@W1, U = A@W2 (bf16,
+    in memory), Y = SiLU(G)*U.  Returns (G, U, Y)."""
+    M, K = A.shape
+    _gemm_packed_at_least(W1g, K, N, "W1g")
+    _gemm_packed_at_least(W2g, K, N, "W2g")
+    for t, name in ((G, "G"), (U, "U"), (Y, "Y")):
+        _shape(t, (M, N), name)
+    mk = lambda: torch.empty((M, N), dtype=torch.bfloat16, device=A.device)  # noqa: E731
+    G = mk() if G is None else G
+    U = mk() if U is None else U
+    Y = mk() if Y is None else Y
+    st = lib().swiglu_unfused_packed(_dev_bf16(A, "A"), _dev_bf16(W1g, "W1g"), _dev_bf16(W2g, "W2g"),
+                                     _dev_bf16(G, "G"), _dev_bf16(U, "U"), _dev_bf16(Y, "Y"), M, K, N,
+                                     _stream(stream))
+    _check("swiglu_unfused_packed", st)
+    return G, U, Y
+
+
 def swiglu_silu_mul(G: torch.Tensor, U: torch.Tensor, Y: torch.Tensor | None = None,
                     stream=None) -> torch.Tensor:
     """Y = bf16(SiLU(G) * U), element-wise (the unfused pipeline's activation)."""
@@ -451,15 +524,17 @@ def swiglu_unfused(A: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor, G: torch
     return G, U, Y
 
 
-def swiglu_mlp_packed(A: torch.Tensor, Wp: torch.Tensor, W3: torch.Tensor, N: int,
+def swiglu_mlp_packed(A: torch.Tensor, Wp: torch.Tensor, W3g: torch.Tensor, N: int,
                       Y: torch.Tensor | None = None, Z: torch.Tensor | None = None,
                       workspace: torch.Tensor | Workspace | None = None, variant: int = VARIANT_AUTO,
                       stream=None):
     """The gated MLP block on packed weights: Y = SiLU(A W1) * (A W2), then
-    Z = Y @ W3 (W3 [N,K] row-major, the down projection).  Returns (Y, Z)."""
+    Z = Y @ W3 (W3 [N,K] in the single-weight pack of swiglu_gemm_pack_weight,
+    the down projection).  Returns (Y, Z)."""
     M, K = A.shape
     _packed_at_least(Wp, K, N)
-    for t, shape, name in ((W3, (N, K), "W3"), (Y, (M, N), "Y"), (Z, (M, K), "Z")):
+    _gemm_packed_at_least(W3g, N, K, "W3g")
+    for t, shape, name in ((Y, (M, N), "Y"), (Z, (M, K), "Z")):
         _shape(t, shape, name)
     if isinstance(variant, str):
         variant = VARIANTS[variant]
@@ -474,44 +549,45 @@ def swiglu_mlp_packed(A: torch.Tensor, Wp: torch.Tensor, W3: torch.Tensor, N: in
     else:
         ws = workspace
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    st = lib().swiglu_mlp_packed(_dev_bf16(A, "A"), _dev_bf16(Wp, "Wp"), _dev_bf16(W3, "W3"),
+    st = lib().swiglu_mlp_packed(_dev_bf16(A, "A"), _dev_bf16(Wp, "Wp"), _dev_bf16(W3g, "W3g"),
                                  _dev_bf16(Y, "Y"), _dev_bf16(Z, "Z"), M, K, N, _ptr(ws), ws_bytes,
                                  int(variant), s)
     _check("swiglu_mlp_packed", st)
     return Y, Z
 
 
-def swiglu_mlp_down(Y: torch.Tensor, W3: torch.Tensor, Z: torch.Tensor | None = None,
+def swiglu_mlp_down(Y: torch.Tensor, W3g: torch.Tensor, K: int, Z: torch.Tensor | None = None,
                     stream=None) -> torch.Tensor:
-    """The MLP block's down projection alone: Z[M,K] = Y[M,N] @ W3[N,K]."""
+    """The MLP block's down projection alone: Z[M,K] = Y[M,N] @ W3[N,K], W3 in
+    the single-weight pack."""
     M, N = Y.shape
-    K = W3.shape[1]
-    _shape(W3, (N, K), "W3")
+    _gemm_packed_at_least(W3g, N, K, "W3g")
     _shape(Z, (M, K), "Z")
     Z = torch.empty((M, K), dtype=torch.bfloat16, device=Y.device) if Z is None else Z
-    st = lib().swiglu_mlp_down(_dev_bf16(Y, "Y"), _dev_bf16(W3, "W3"), _dev_bf16(Z, "Z"), M, K, N,
+    st = lib().swiglu_mlp_down(_dev_bf16(Y, "Y"), _dev_bf16(W3g, "W3g"), _dev_bf16(Z, "Z"), M, K, N,
                                _stream(stream))
     _check("swiglu_mlp_down", st)
     return Z
 
 
-def swiglu_mlp_unfused(A: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor, W3: torch.Tensor,
+def swiglu_mlp_unfused(A: torch.Tensor, W1g: torch.Tensor, W2g: torch.Tensor, W3g: torch.Tensor, N: int,
                        G: torch.Tensor | None = None, U: torch.Tensor | None = None,
                        Y: torch.Tensor | None = None, Z: torch.Tensor | None = None, stream=None):
-    """The gated MLP block, unfused: G, U through memory, Y = SiLU(G)*U, then
-    Z = Y @ W3.  Returns (Y, Z)."""
+    """The gated MLP block, unfused, on single-weight packs: G, U through
+    memory, Y = SiLU(G)*U, then Z = Y @ W3.  Returns (Y, Z)."""
     M, K = A.shape
-    N = W1.shape[1]
-    for t, shape, name in ((W1, (K, N), "W1"), (W2, (K, N), "W2"), (W3, (N, K), "W3"), (G, (M, N), "G"),
-                           (U, (M, N), "U"), (Y, (M, N), "Y"), (Z, (M, K), "Z")):
+    _gemm_packed_at_least(W1g, K, N, "W1g")
+    _gemm_packed_at_least(W2g, K, N, "W2g")
+    _gemm_packed_at_least(W3g, N, K, "W3g")
+    for t, shape, name in ((G, (M, N), "G"), (U, (M, N), "U"), (Y, (M, N), "Y"), (Z, (M, K), "Z")):
         _shape(t, shape, name)
     mk = lambda r, c: torch.empty((r, c), dtype=torch.bfloat16, device=A.device)  # noqa: E731
     G = mk(M, N) if G is None else G
     U = mk(M, N) if U is None else U
     Y = mk(M, N) if Y is None else Y
     Z = mk(M, K) if Z is None else Z
-    st = lib().swiglu_mlp_unfused(_dev_bf16(A, "A"), _dev_bf16(W1, "W1"), _dev_bf16(W2, "W2"),
-                                  _dev_bf16(W3, "W3"), _dev_bf16(G, "G"), _dev_bf16(U, "U"),
+    st = lib().swiglu_mlp_unfused(_dev_bf16(A, "A"), _dev_bf16(W1g, "W1g"), _dev_bf16(W2g, "W2g"),
+                                  _dev_bf16(W3g, "W3g"), _dev_bf16(G, "G"), _dev_bf16(U, "U"),
                                   _dev_bf16(Y, "Y"), _dev_bf16(Z, "Z"), M, K, N, _stream(stream))
     _check("swiglu_mlp_unfused", st)
     return Y, Z

@@ -212,9 +212,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 //   for Gate and for Up when DUAL.
 //   PACKED: weights come from the packed layout (K-contiguous rows), else from
 //   row-major [K,N] W1/W2 and are transposed in registers on the way to LDS.
-//   SPLIT: the workgroup covers kb_per_split K blocks; partial Gate/Up go to
-//   `part`, and the last workgroup of a tile to arrive sums the partials in
-//   split order 0..S-1 (before SiLU) and runs the epilogue.
+//   SPLIT: the workgroup covers kb_per_split K blocks and writes its fp32
+//   partial Gate/Up sums to `part`; splitk_reduce_kernel, launched after it,
+//   adds the partials in split order 0..S-1 (before SiLU) and runs the
+//   epilogue.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int WM, int WN, bool DUAL, bool PACKED, bool SPLIT>
 __global__ __launch_bounds__(64 * WM * WN) void fused_tile_kernel(FusedArgs p) {
@@ -894,10 +895,16 @@ constexpr int stream_smem_elems() {
 // stages are issued and SiLU(Gate) is computed into acc[1] while they land;
 // the epilogue is then acc[1] * acc[0].  The Gate and Up sums take the same
 // MFMAs in the same order as the dual loop, so the two agree bitwise.
+// GEMM: a plain product C = bf16(A x W) on a single-weight pack (packed tile
+// jt holds W's columns jt*256 + 0..255): the "Gate" accumulators are output
+// columns jt*256 + c, the "Up" ones jt*256 + 128 + c; p.N is C's width.  The
+// Y tile in LDS holds 128 columns, so the epilogue runs in two passes (Gate
+// half, then Up half), each staged, synchronised and stored.
 template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false, bool IL = false, bool F8 = false,
-          bool SEQ = false>
+          bool SEQ = false, bool GEMM = false>
 __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_t* smem, int first, int stride,
                                                      int total) {
+    static_assert(!(GEMM && (SPLIT || IL || F8 || SEQ)), "plain GEMM: bf16 single-weight pack, data-parallel");
     static_assert(!(IL && SPLIT), "the interleaved layout has no split-K schedule");
     static_assert(!(F8 && (IL || SPLIT)), "FP8 operands: per-tile layout, data-parallel only");
     static_assert(!(SEQ && (SPLIT || PANELS || IL || F8)), "sequential order: bf16 per-tile tiles only");
@@ -1327,8 +1334,26 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
         int el = lane;
         asm volatile("" : "+v"(el));
         __builtin_amdgcn_sched_barrier(0);
+        // GEMM pass gh: bf16 of accumulator set gh (no SiLU) into the Y tile
+        auto fill_gemm = [&](int gh) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+            for (int i = 0; i < TM; ++i) {
+                const int r = i * 32 + (el & 31);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    u32x2 out;
+                    out[0] = pack2(acc[gh][i][0][4 * q], acc[gh][i][0][4 * q + 1]);
+                    out[1] = pack2(acc[gh][i][0][4 * q + 2], acc[gh][i][0][4 * q + 3]);
+                    const int chunk = wave * 4 + q;
+                    *reinterpret_cast<u32x2*>(sY + r * PACK_BN + 8 * (chunk ^ (r & 15)) +
+                                              4 * ((el >> 5) ^ ((r >> 4) & 1))) = out;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        if constexpr (GEMM) fill_gemm(0);
+#pragma unroll
+        for (int i = 0; i < (GEMM ? 0 : TM); ++i) {
             const int r = i * 32 + (el & 31);
             if constexpr (IL) {
                 // accumulator register 4q + 2e + g of set t is packed row
@@ -1378,12 +1403,16 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
         // at most stage 1's weight loads are in flight; the Y tile is in LDS
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(LOADS - A_INS, 0));
         __builtin_amdgcn_s_barrier();
-        {
-            // wave w stores rows w*BM/4 + 4t + l/16, 16 bytes at column 8(l%16)
+        // wave w stores rows w*BM/4 + 4t + l/16, 16 bytes at tile column
+        // 8(l%16); GEMM pass gh: output column (f / 128) * 256 + 128 gh +
+        // f % 128 of tile column f
+        auto store_tile = [&](int gh) {
             const int r0 = wave * (BM / 4) + (el >> 4);
             const int c = el & 15;
-            const int n = cur.n0 + 8 * c;
-            const int n_lim = PANELS ? min(N, cur.n0 + 32 * cur.np) : N;
+            const int f = cur.n0 + 8 * c;
+            const int n = GEMM ? (f >> 7) * PACK_ROWS + PACK_BN * gh + (f & (PACK_BN - 1)) : f;
+            const bool col_ok = GEMM ? (n < N && (!PANELS || f < cur.n0 + 32 * cur.np))
+                                     : (n < (PANELS ? min(N, cur.n0 + 32 * cur.np) : N));
             const int rows_left = M - cur.m0 - r0;   // rows r0 + 4t < M - m0
             uint16_t* yp = p.Y + (size_t)(cur.m0 + r0) * N + n;
 #pragma unroll
@@ -1391,8 +1420,21 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
                 const int r = r0 + t * 4;
                 u32x4 v = *reinterpret_cast<const u32x4*>(sY + r * PACK_BN + 8 * (c ^ (r & 15)));
                 if ((r >> 4) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-                if (4 * t < rows_left && n < n_lim) store16_untracked(yp + (size_t)t * 4 * N, v);
+                if (4 * t < rows_left && col_ok) store16_untracked(yp + (size_t)t * 4 * N, v);
             }
+        };
+        store_tile(0);
+        if constexpr (GEMM) {
+            // every wave has read the Gate half out of the Y tile (its reads
+            // fed the stores above); then the Up half goes through it
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            fill_gemm(1);
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            store_tile(1);
         }
         if (!more) break;
 
@@ -1418,28 +1460,28 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
 }
 
 template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false, bool IL = false, bool F8 = false,
-          bool SEQ = false>
+          bool SEQ = false, bool GEMM = false>
 __global__ __launch_bounds__(256) void stream_prefill_kernel(FusedArgs p, int total) {
     static_assert(!PANELS || (BM == 128 && !SPLIT), "panel schedule: one 128-row tile, data-parallel");
     __shared__ __attribute__((aligned(16))) uint16_t smem[stream_smem_elems<BM>()];
-    stream_prefill_tiles<BM, SPLIT, RAGGED, PANELS, IL, F8, SEQ>(p, smem, blockIdx.x, gridDim.x, total);
+    stream_prefill_tiles<BM, SPLIT, RAGGED, PANELS, IL, F8, SEQ, GEMM>(p, smem, blockIdx.x, gridDim.x, total);
 }
 
 // The 256-row tiles and the 128-row tail column tiles in one launch: blocks
 // 0 .. n_pers-1 work through the n_big 256-row tiles of `big` (block b takes
 // tiles b, b + n_pers, ...), the remaining blocks take one 128-row tile of
 // `tail` each and start on CUs as the 256-row work drains.
-template <bool RAGGED, bool IL = false, bool F8 = false, bool SEQ = false>
+template <bool RAGGED, bool IL = false, bool F8 = false, bool SEQ = false, bool GEMM = false>
 __global__ __launch_bounds__(256) void stream_prefill_mixed_kernel(FusedArgs big, FusedArgs tail, int n_pers,
                                                                    int n_big) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[stream_smem_elems<256>()];
     static_assert(stream_smem_elems<256>() >= stream_smem_elems<128>(), "one LDS block serves both tiles");
     const int b = blockIdx.x;
     if (b < n_pers) {
-        stream_prefill_tiles<256, false, RAGGED, false, IL, F8, SEQ>(big, smem, b, n_pers, n_big);
+        stream_prefill_tiles<256, false, RAGGED, false, IL, F8, SEQ, GEMM>(big, smem, b, n_pers, n_big);
     } else {
         const int n_tail = gridDim.x - n_pers;
-        stream_prefill_tiles<128, false, RAGGED, false, IL, F8, SEQ>(tail, smem, b - n_pers, n_tail, n_tail);
+        stream_prefill_tiles<128, false, RAGGED, false, IL, F8, SEQ, GEMM>(tail, smem, b - n_pers, n_tail, n_tail);
     }
 }
 
@@ -1466,7 +1508,11 @@ struct DecodeArgs {
     int KB;               // ceil(K / 64)
 };
 
-template <int MT, int CG, int UNROLL>
+// GEMM: a plain product C = bf16(A x W) on a single-weight pack (packed tile
+// jt holds W's columns jt*256 + 0..255); the "Gate" sums of tile column c are
+// output column jt*256 + c, the "Up" sums jt*256 + 128 + c; p.N is C's width
+// (the grid covers the packed tiles' 128 columns each).
+template <int MT, int CG, int UNROLL, bool GEMM = false>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
     constexpr int WAVES = 4;
     __shared__ f32x4 red[WAVES][MT][CG][2][64];
@@ -1561,7 +1607,21 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
         }
         const int m = t * 16 + r16;
         const int n = n0 + 16 * c + 4 * kq;
-        if (m < M && n < N) {
+        if constexpr (GEMM) {
+            const int col = (n / PACK_BN) * PACK_ROWS + n % PACK_BN;
+            if (m < M && col < N) {
+                u32x2 out;
+                out[0] = pack2(g[0], g[1]);
+                out[1] = pack2(g[2], g[3]);
+                *reinterpret_cast<u32x2*>(p.Y + (size_t)m * N + col) = out;
+            }
+            if (m < M && col + PACK_BN < N) {
+                u32x2 out;
+                out[0] = pack2(u[0], u[1]);
+                out[1] = pack2(u[2], u[3]);
+                *reinterpret_cast<u32x2*>(p.Y + (size_t)m * N + col + PACK_BN) = out;
+            }
+        } else if (m < M && n < N) {
             u32x2 out;
             out[0] = pack2(silu_f(g[0]) * u[0], silu_f(g[1]) * u[1]);
             out[1] = pack2(silu_f(g[2]) * u[2], silu_f(g[3]) * u[3]);
@@ -1698,8 +1758,12 @@ struct PackChunk {
 
 // IL = false: per-tile [W1 | W2] (packed rows 0-127 the tile's W1 columns,
 // 128-255 its W2 columns).  IL = true: column-granular interleave (packed row
-// 2c the tile's W1 column c, row 2c + 1 its W2 column c).
-template <bool IL>
+// 2c the tile's W1 column c, row 2c + 1 its W2 column c).  SINGLE: one
+// weight W (passed as W1) for a plain GEMM, 256 of its columns per packed
+// tile: packed row p of tile jt is column jt*256 + p, so the dual kernels'
+// "Gate" half of a tile holds columns jt*256 + 0..127 and the "Up" half
+// jt*256 + 128..255.
+template <bool IL, bool SINGLE = false>
 __device__ __forceinline__ PackChunk pack_chunk(long long q, int KB) {
     const long long blk = q >> 11;                  // jt * KB + kb
     const int within = (int)(q & 2047);
@@ -1710,7 +1774,10 @@ __device__ __forceinline__ PackChunk pack_chunk(long long q, int KB) {
     const int kb = (int)(blk % KB);
     const int jt = (int)(blk / KB);
     PackChunk c;
-    if constexpr (IL) {
+    if constexpr (SINGLE) {
+        c.up = false;
+        c.n = jt * PACK_ROWS + prow;
+    } else if constexpr (IL) {
         c.up = (prow & 1) != 0;
         c.n = jt * PACK_BN + (prow >> 1);
     } else {
@@ -1721,14 +1788,14 @@ __device__ __forceinline__ PackChunk pack_chunk(long long q, int KB) {
     return c;
 }
 
-template <bool IL>
+template <bool IL, bool SINGLE = false>
 __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ W1,
                                                    const uint16_t* __restrict__ W2,
                                                    uint16_t* __restrict__ Wp, int K, int N,
                                                    int KB, long long nchunks) {
     const long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= nchunks) return;
-    const PackChunk c = pack_chunk<IL>(q, KB);
+    const PackChunk c = pack_chunk<IL, SINGLE>(q, KB);
     const uint16_t* W = c.up ? W2 : W1;
     unsigned short v[8];
 #pragma unroll

@@ -106,6 +106,14 @@ int64_t packed_elems(int64_t K, int64_t N) {
     return ceil_div(N, swk::PACK_BN) * ceil_div(K, swk::PACK_BK) * swk::PACK_ROWS * swk::PACK_BK;
 }
 
+// Single-weight pack of W [K,N] for the plain GEMM: 256 columns per packed
+// tile (the dual kernels' Gate and Up halves), so ceil(N/256) tiles whose
+// 128-column "output" width n_tiled the dual schedules are planned on.
+int64_t gemm_packed_elems(int64_t K, int64_t N) {
+    return ceil_div(N, swk::PACK_ROWS) * ceil_div(K, swk::PACK_BK) * swk::PACK_ROWS * swk::PACK_BK;
+}
+int64_t gemm_tiled_cols(int64_t N) { return ceil_div(N, swk::PACK_ROWS) * swk::PACK_BN; }
+
 // ---------------------------------------------------------------------------
 // device facts
 // ---------------------------------------------------------------------------
@@ -275,12 +283,14 @@ hipError_t launch_tile(const swk::FusedArgs& a, int grid, hipStream_t s) {
     return hipLaunchKernel(fn, dim3(grid), dim3(64 * WM * WN), kargs, 0, s);
 }
 
-template <int MT, int CG, int UNROLL>
-hipError_t launch_decode(const swk::DecodeArgs& a, hipStream_t s) {
-    const void* fn = reinterpret_cast<const void*>(&swk::decode_kernel<MT, CG, UNROLL>);
+// n_tiled: the packed weights' output columns (N for the fused product; 128
+// per packed tile for the single-weight GEMM)
+template <int MT, int CG, int UNROLL, bool GEMM = false>
+hipError_t launch_decode(const swk::DecodeArgs& a, int64_t n_tiled, hipStream_t s) {
+    const void* fn = reinterpret_cast<const void*>(&swk::decode_kernel<MT, CG, UNROLL, GEMM>);
     swk::DecodeArgs args = a;
     void* kargs[] = {&args};
-    return hipLaunchKernel(fn, dim3((unsigned)ceil_div(a.N, 16 * CG)), dim3(256), kargs, 0, s);
+    return hipLaunchKernel(fn, dim3((unsigned)ceil_div(n_tiled, 16 * CG)), dim3(256), kargs, 0, s);
 }
 
 template <int BM, int BN, int WM, int WN, bool SPLIT, int WSRC = swk::W_PACKED>
@@ -293,12 +303,13 @@ hipError_t launch_prefill(const swk::FusedArgs& a, int grid, hipStream_t s) {
 
 // `total` work items (tiles, or tile x K split) on `grid` <= total workgroups;
 // each workgroup takes items b, b + grid, ...
-template <int BM, bool SPLIT, bool PANELS = false, bool IL = false, bool F8 = false, bool SEQ = false>
+template <int BM, bool SPLIT, bool PANELS = false, bool IL = false, bool F8 = false, bool SEQ = false,
+          bool GEMM = false>
 hipError_t launch_stream(const swk::FusedArgs& a, int total, int grid, hipStream_t s) {
     const bool ragged = (a.K % (F8 ? 128 : swk::BK)) != 0;
     const void* fn =
-        ragged ? reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, true, PANELS, IL, F8, SEQ>)
-               : reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, false, PANELS, IL, F8, SEQ>);
+        ragged ? reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, true, PANELS, IL, F8, SEQ, GEMM>)
+               : reinterpret_cast<const void*>(&swk::stream_prefill_kernel<BM, SPLIT, false, PANELS, IL, F8, SEQ, GEMM>);
     swk::FusedArgs args = a;
     void* kargs[] = {&args, &total};
     return hipLaunchKernel(fn, dim3(grid), dim3(256), kargs, 0, s);
@@ -307,7 +318,7 @@ hipError_t launch_stream(const swk::FusedArgs& a, int total, int grid, hipStream
 // The data-parallel streaming schedules (128- or 256-row tiles, the panel
 // schedule, the mixed 256/128-row launch) on either weight layout; SEQ: the
 // sequential Gate-then-Up order (per-tile layout, no panel schedule).
-template <bool IL, bool F8 = false, bool SEQ = false>
+template <bool IL, bool F8 = false, bool SEQ = false, bool GEMM = false>
 hipError_t launch_stream_dp(const swk::FusedArgs& a, const Plan& p, hipStream_t s) {
     const int grid = p.tiles;
     if (p.t.BM == 128) {
@@ -316,12 +327,13 @@ hipError_t launch_stream_dp(const swk::FusedArgs& a, const Plan& p, hipStream_t 
             swk::FusedArgs pa = a;
             pa.panels = p.panels;
             const int g = std::min(p.panels, p.cus);
-            return launch_stream<128, false, true, IL, F8>(pa, g, g, s);
+            return launch_stream<128, false, true, IL, F8, false, GEMM>(pa, g, g, s);
         }
-        return launch_stream<128, false, false, IL, F8>(a, grid, grid, s);
+        return launch_stream<128, false, false, IL, F8, false, GEMM>(a, grid, grid, s);
     }
     // one workgroup per CU works through the 256-row tiles
-    if (p.tail_ntiles == 0) return launch_stream<256, false, false, IL, F8, SEQ>(a, grid, std::min(grid, p.cus), s);
+    if (p.tail_ntiles == 0)
+        return launch_stream<256, false, false, IL, F8, SEQ, GEMM>(a, grid, std::min(grid, p.cus), s);
     // one launch: the 256-row tiles of the first column tiles, then
     // the last tail_ntiles column tiles as 128-row tiles
     swk::FusedArgs big = a, tail = a;
@@ -334,8 +346,8 @@ hipError_t launch_stream_dp(const swk::FusedArgs& a, const Plan& p, hipStream_t 
     const int grid_all = n_pers + tail.tiles_m * tail.tiles_n;
     const bool ragged = (a.K % (F8 ? 128 : swk::BK)) != 0;
     const void* fn = ragged
-                         ? reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<true, IL, F8, SEQ>)
-                         : reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<false, IL, F8, SEQ>);
+                         ? reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<true, IL, F8, SEQ, GEMM>)
+                         : reinterpret_cast<const void*>(&swk::stream_prefill_mixed_kernel<false, IL, F8, SEQ, GEMM>);
     void* kargs[] = {&big, &tail, &n_pers, &n_big};
     return hipLaunchKernel(fn, dim3(grid_all), dim3(256), kargs, 0, s);
 }
@@ -367,30 +379,37 @@ hipError_t launch_decode_fp8(const swk::FusedArgs& a, int cus, hipStream_t s) {
     return launch_decode_fp8_cfg<1, 2>(a, s);
 }
 
+// The decode kernel's configuration for a plan: column groups per workgroup
+// (CG) and K blocks in flight per wave (UNROLL), measured on this chip: wider
+// groups read each activation fragment for more weight bytes and stream
+// longer contiguous runs of the packed blocks; they pay off for long K (>= 96
+// blocks) as long as the grid still gives about one workgroup per CU.
+// n_tiled: the packed weights' output columns.
+template <bool GEMM>
+hipError_t launch_decode_cfg(const swk::DecodeArgs& d, int64_t n_tiled, const Plan& p, hipStream_t s) {
+    const bool long_k = p.KB >= 96;
+    const int64_t wg64 = ceil_div(n_tiled, 64), wg128 = ceil_div(n_tiled, 128);
+    switch (p.decode_mt) {
+        case 1:
+            return (long_k && 4 * wg128 >= 3 * p.cus) ? launch_decode<1, 8, 2, GEMM>(d, n_tiled, s)
+                                                     : launch_decode<1, 1, 8, GEMM>(d, n_tiled, s);
+        case 2:
+            if (long_k && 4 * wg64 >= 3 * p.cus) return launch_decode<2, 4, 1, GEMM>(d, n_tiled, s);
+            return 2 * wg128 >= p.cus ? launch_decode<2, 8, 1, GEMM>(d, n_tiled, s)
+                                      : launch_decode<2, 2, 2, GEMM>(d, n_tiled, s);
+        default:
+            return (long_k && 4 * wg64 >= 3 * p.cus) ? launch_decode<4, 4, 1, GEMM>(d, n_tiled, s)
+                                                    : launch_decode<4, 2, 1, GEMM>(d, n_tiled, s);
+    }
+}
+
 hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) {
     if (p.variant == SWIGLU_VARIANT_SEQUENTIAL) return launch_stream_dp<false, false, true>(a, p, s);
     if (p.variant == SWIGLU_VARIANT_DECODE) {
         swk::DecodeArgs d{};
         d.A = a.A; d.Wp = a.W1; d.Y = a.Y;
         d.M = a.M; d.K = a.K; d.N = a.N; d.KB = a.KB;
-        // Column groups per workgroup (CG) and K blocks in flight per wave
-        // (UNROLL), measured on this chip: wider groups read each activation
-        // fragment for more weight bytes and stream longer contiguous runs of
-        // the packed blocks; they pay off for long K (>= 96 blocks) as long
-        // as the grid still gives about one workgroup per CU.
-        const bool long_k = p.KB >= 96;
-        const int64_t wg64 = ceil_div(a.N, 64), wg128 = ceil_div(a.N, 128);
-        switch (p.decode_mt) {
-            case 1:
-                return (long_k && 4 * wg128 >= 3 * p.cus) ? launch_decode<1, 8, 2>(d, s)
-                                                         : launch_decode<1, 1, 8>(d, s);
-            case 2:
-                if (long_k && 4 * wg64 >= 3 * p.cus) return launch_decode<2, 4, 1>(d, s);
-                return 2 * wg128 >= p.cus ? launch_decode<2, 8, 1>(d, s) : launch_decode<2, 2, 2>(d, s);
-            default:
-                return (long_k && 4 * wg64 >= 3 * p.cus) ? launch_decode<4, 4, 1>(d, s)
-                                                        : launch_decode<4, 2, 1>(d, s);
-        }
+        return launch_decode_cfg<false>(d, a.N, p, s);
     }
     const int grid = p.tiles * p.splits;
     const bool split = p.splits > 1;
@@ -768,6 +787,90 @@ swiglu_status swiglu_gemm_bf16(const swiglu_bf16* A, const swiglu_bf16* W, swigl
     return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
 }
 
+size_t swiglu_gemm_packed_bytes(int64_t K, int64_t N) {
+    if (check_shape(0, K, N) != SWIGLU_OK) return 0;
+    return (size_t)gemm_packed_elems(K, N) * sizeof(swiglu_bf16);
+}
+
+swiglu_status swiglu_gemm_pack_weight(const swiglu_bf16* W, swiglu_bf16* Wg, int64_t K, int64_t N, void* stream) {
+    swiglu_status st = check_shape(0, K, N);
+    if (st != SWIGLU_OK) return st;
+    if (!W || !Wg) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(W) || !aligned16(Wg)) return SWIGLU_ERR_MISALIGNED;
+    if (overlap(range_of(Wg, gemm_packed_elems(K, N) * 2), range_of(W, K * N * 2))) return SWIGLU_ERR_ALIASING;
+    const long long nchunks = (long long)gemm_packed_elems(K, N) / 8;
+    const int KB = (int)ceil_div(K, swk::PACK_BK);
+    int Ki = (int)K, Ni = (int)N;
+    void* args[] = {(void*)&W, (void*)&W, (void*)&Wg, &Ki, &Ni, (void*)&KB, (void*)&nchunks};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&swk::pack_kernel<false, true>),
+                                   dim3((unsigned)ceil_div(nchunks, 256)), dim3(256), args, 0, (hipStream_t)stream);
+    return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
+}
+
+swiglu_status swiglu_gemm_packed(const swiglu_bf16* A, const swiglu_bf16* Wg, swiglu_bf16* C, int64_t M, int64_t K,
+                                 int64_t N, void* stream) {
+    swiglu_status st = check_shape(M, K, N);
+    if (st != SWIGLU_OK) return st;
+    if (M == 0) return SWIGLU_OK;
+    if (!A || !Wg || !C) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(A) || !aligned16(Wg) || !aligned16(C)) return SWIGLU_ERR_MISALIGNED;
+    const Range c = range_of(C, M * N * 2);
+    if (overlap(c, range_of(A, M * K * 2)) || overlap(c, range_of(Wg, gemm_packed_elems(K, N) * 2)))
+        return SWIGLU_ERR_ALIASING;
+    if (M > stream_rows_limit(K, 2)) {
+        const int64_t rows = balanced_chunk(M, stream_rows_limit(K, 2));
+        for (int64_t m0 = 0; m0 < M; m0 += rows) {
+            st = swiglu_gemm_packed(A + m0 * K, Wg, C + m0 * N, std::min(rows, M - m0), K, N, stream);
+            if (st != SWIGLU_OK) return st;
+        }
+        return SWIGLU_OK;
+    }
+    // the fused product's schedules on the packed tiles' width, without
+    // split-K (no workspace): decode for small M, else the streaming grid
+    const int cus = cu_count_now();
+    const int64_t nt = gemm_tiled_cols(N);
+    Plan p = make_plan(M, K, nt, SWIGLU_VARIANT_AUTO, cus);
+    if (p.variant == SWIGLU_VARIANT_SPLIT_K) p = make_plan(M, K, nt, SWIGLU_VARIANT_DATA_PARALLEL, cus);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (p.variant == SWIGLU_VARIANT_DECODE) {
+        swk::DecodeArgs d{};
+        d.A = A; d.Wp = Wg; d.Y = C;
+        d.M = (int)M; d.K = (int)K; d.N = (int)N; d.KB = p.KB;
+        e = launch_decode_cfg<true>(d, nt, p, s);
+    } else {
+        swk::FusedArgs a{};
+        a.A = A; a.W1 = Wg; a.W2 = nullptr; a.Y = C;
+        a.M = (int)M; a.K = (int)K; a.N = (int)N;
+        a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n;
+        a.splits = 1; a.kb_per_split = p.KB; a.KB = p.KB;
+        e = launch_stream_dp<false, false, false, true>(a, p, s);
+    }
+    return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
+}
+
+swiglu_status swiglu_unfused_packed(const swiglu_bf16* A, const swiglu_bf16* W1g, const swiglu_bf16* W2g,
+                                    swiglu_bf16* G_scratch, swiglu_bf16* U_scratch, swiglu_bf16* Y, int64_t M,
+                                    int64_t K, int64_t N, void* stream) {
+    swiglu_status st = check_shape(M, K, N);
+    if (st != SWIGLU_OK) return st;
+    if (M == 0) return SWIGLU_OK;
+    if (!A || !W1g || !W2g || !G_scratch || !U_scratch || !Y) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(G_scratch) || !aligned16(U_scratch) || !aligned16(Y)) return SWIGLU_ERR_MISALIGNED;
+    const Range g = range_of(G_scratch, M * N * 2), u = range_of(U_scratch, M * N * 2),
+                y = range_of(Y, M * N * 2);
+    const int64_t wb = gemm_packed_elems(K, N) * 2;
+    const Range ins[3] = {range_of(A, M * K * 2), range_of(W1g, wb), range_of(W2g, wb)};
+    for (const Range& r : ins)
+        if (overlap(g, r) || overlap(u, r) || overlap(y, r)) return SWIGLU_ERR_ALIASING;
+    if (overlap(g, u) || overlap(g, y) || overlap(u, y)) return SWIGLU_ERR_ALIASING;
+    st = swiglu_gemm_packed(A, W1g, G_scratch, M, K, N, stream);
+    if (st != SWIGLU_OK) return st;
+    st = swiglu_gemm_packed(A, W2g, U_scratch, M, K, N, stream);
+    if (st != SWIGLU_OK) return st;
+    return swiglu_silu_mul(G_scratch, U_scratch, Y, M * N, stream);
+}
+
 swiglu_status swiglu_silu_mul(const swiglu_bf16* G, const swiglu_bf16* U, swiglu_bf16* Y,
                               int64_t count, void* stream) {
     if (count < 0) return SWIGLU_ERR_BAD_SHAPE;
@@ -809,36 +912,33 @@ swiglu_status swiglu_unfused(const swiglu_bf16* A, const swiglu_bf16* W1, const 
 
 // ---------------------------------------------------------------------------
 // Down projection of the MLP block, Z[M,K] = bf16(Y[M,N] x W3[N,K]): a plain
-// GEMM on this library's own kernel, with Y as the activations (N deep) and
-// the row-major W3 as the weights (K output columns).
+// GEMM on this library's own kernels, Y as the activations (N deep) and W3 in
+// the single-weight pack (swiglu_gemm_pack_weight of the [N,K] W3).
 // ---------------------------------------------------------------------------
-swiglu_status down_projection(const swiglu_bf16* Y, const swiglu_bf16* W3, swiglu_bf16* Z, int64_t M,
-                              int64_t N, int64_t K, void* stream) {
-    return swiglu_gemm_bf16(Y, W3, Z, M, N, K, stream);
-}
-
-swiglu_status swiglu_mlp_down(const swiglu_bf16* Y, const swiglu_bf16* W3, swiglu_bf16* Z, int64_t M, int64_t K,
-                             int64_t N, void* stream) {
+swiglu_status swiglu_mlp_down(const swiglu_bf16* Y, const swiglu_bf16* W3g, swiglu_bf16* Z, int64_t M, int64_t K,
+                              int64_t N, void* stream) {
     swiglu_status st = check_shape(M, K, N);
     if (st != SWIGLU_OK) return st;
     if (M == 0) return SWIGLU_OK;
-    if (!Y || !W3 || !Z) return SWIGLU_ERR_NULL_POINTER;
-    if (!aligned16(Y) || !aligned16(W3) || !aligned16(Z)) return SWIGLU_ERR_MISALIGNED;
+    if (!Y || !W3g || !Z) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(Y) || !aligned16(W3g) || !aligned16(Z)) return SWIGLU_ERR_MISALIGNED;
     const Range z = range_of(Z, M * K * 2);
-    if (overlap(z, range_of(Y, M * N * 2)) || overlap(z, range_of(W3, N * K * 2))) return SWIGLU_ERR_ALIASING;
-    return down_projection(Y, W3, Z, M, N, K, stream);
+    if (overlap(z, range_of(Y, M * N * 2)) || overlap(z, range_of(W3g, gemm_packed_elems(N, K) * 2)))
+        return SWIGLU_ERR_ALIASING;
+    return swiglu_gemm_packed(Y, W3g, Z, M, N, K, stream);
 }
 
-swiglu_status swiglu_mlp_packed(const swiglu_bf16* A, const swiglu_bf16* Wp, const swiglu_bf16* W3,
+swiglu_status swiglu_mlp_packed(const swiglu_bf16* A, const swiglu_bf16* Wp, const swiglu_bf16* W3g,
                                 swiglu_bf16* Y, swiglu_bf16* Z, int64_t M, int64_t K, int64_t N,
                                 void* workspace, size_t workspace_bytes, int variant, void* stream) {
     swiglu_status st = check_shape(M, K, N);
     if (st != SWIGLU_OK) return st;
     if (!variant_known(variant)) return SWIGLU_ERR_BAD_VARIANT;
     if (M == 0) return SWIGLU_OK;
-    if (!A || !Wp || !W3 || !Y || !Z) return SWIGLU_ERR_NULL_POINTER;
-    if (!aligned16(W3) || !aligned16(Z)) return SWIGLU_ERR_MISALIGNED;
-    const Range z = range_of(Z, M * K * 2), w3 = range_of(W3, N * K * 2), y = range_of(Y, M * N * 2);
+    if (!A || !Wp || !W3g || !Y || !Z) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(W3g) || !aligned16(Z)) return SWIGLU_ERR_MISALIGNED;
+    const Range z = range_of(Z, M * K * 2), w3 = range_of(W3g, gemm_packed_elems(N, K) * 2),
+                y = range_of(Y, M * N * 2);
     if (overlap(z, range_of(A, M * K * 2)) || overlap(z, range_of(Wp, packed_elems(K, N) * 2)) ||
         overlap(z, w3) || overlap(z, y) || overlap(y, w3))
         return SWIGLU_ERR_ALIASING;
@@ -846,29 +946,30 @@ swiglu_status swiglu_mlp_packed(const swiglu_bf16* A, const swiglu_bf16* Wp, con
         return SWIGLU_ERR_ALIASING;
     st = swiglu_fused_packed(A, Wp, Y, M, K, N, workspace, workspace_bytes, variant, stream);
     if (st != SWIGLU_OK) return st;
-    return down_projection(Y, W3, Z, M, N, K, stream);
+    return swiglu_gemm_packed(Y, W3g, Z, M, N, K, stream);
 }
 
-swiglu_status swiglu_mlp_unfused(const swiglu_bf16* A, const swiglu_bf16* W1, const swiglu_bf16* W2,
-                                 const swiglu_bf16* W3, swiglu_bf16* G_scratch, swiglu_bf16* U_scratch,
+swiglu_status swiglu_mlp_unfused(const swiglu_bf16* A, const swiglu_bf16* W1g, const swiglu_bf16* W2g,
+                                 const swiglu_bf16* W3g, swiglu_bf16* G_scratch, swiglu_bf16* U_scratch,
                                  swiglu_bf16* Y, swiglu_bf16* Z, int64_t M, int64_t K, int64_t N,
                                  void* stream) {
     swiglu_status st = check_shape(M, K, N);
     if (st != SWIGLU_OK) return st;
     if (M == 0) return SWIGLU_OK;
-    if (!A || !W1 || !W2 || !W3 || !G_scratch || !U_scratch || !Y || !Z) return SWIGLU_ERR_NULL_POINTER;
-    if (!aligned16(W3) || !aligned16(Z)) return SWIGLU_ERR_MISALIGNED;
-    const Range z = range_of(Z, M * K * 2), w3 = range_of(W3, N * K * 2);
-    const Range others[7] = {range_of(A, M * K * 2), range_of(W1, K * N * 2), range_of(W2, K * N * 2), w3,
+    if (!A || !W1g || !W2g || !W3g || !G_scratch || !U_scratch || !Y || !Z) return SWIGLU_ERR_NULL_POINTER;
+    if (!aligned16(W3g) || !aligned16(Z)) return SWIGLU_ERR_MISALIGNED;
+    const int64_t wb = gemm_packed_elems(K, N) * 2;
+    const Range z = range_of(Z, M * K * 2), w3 = range_of(W3g, gemm_packed_elems(N, K) * 2);
+    const Range others[7] = {range_of(A, M * K * 2), range_of(W1g, wb), range_of(W2g, wb), w3,
                              range_of(G_scratch, M * N * 2), range_of(U_scratch, M * N * 2),
                              range_of(Y, M * N * 2)};
     for (const Range& r : others)
         if (overlap(z, r)) return SWIGLU_ERR_ALIASING;
     for (int i = 4; i < 7; ++i)
         if (overlap(others[i], w3)) return SWIGLU_ERR_ALIASING;
-    st = swiglu_unfused(A, W1, W2, G_scratch, U_scratch, Y, M, K, N, stream);
+    st = swiglu_unfused_packed(A, W1g, W2g, G_scratch, U_scratch, Y, M, K, N, stream);
     if (st != SWIGLU_OK) return st;
-    return down_projection(Y, W3, Z, M, N, K, stream);
+    return swiglu_gemm_packed(Y, W3g, Z, M, N, K, stream);
 }
 
 swiglu_status swiglu_probe_mfma(float* sink, int blocks, int iters, void* stream) {

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert sw.swiglu_abi_version() == 1
+    assert sw.swiglu_abi_version() == 2
     for s in range(9):
         assert sw.status_str(s) and sw.status_str(s) != "unknown status"
     assert sw.status_str(99) == "unknown status"
@@ -151,6 +151,32 @@ def test_mlp_errors():
     assert U(A_, W1_, W2_, W3_, G_, W3_ + 128, Y_, Z_, 4, 64, 64, None) == ALIAS
 
 
+def test_gemm_packed_sizes_and_errors():
+    """The single-weight pack: ceil(N/256) tiles of 256 packed rows, the fused
+    pack's 32 KiB blocks per 64 k; the packed GEMM's validation codes."""
+    L = sw.lib()
+    assert L.swiglu_gemm_packed_bytes(896, 4864) == 19 * 14 * 256 * 64 * 2 == 896 * 4864 * 2
+    assert L.swiglu_gemm_packed_bytes(8192, 29568) == 116 * 128 * 32768    # 115.5 tiles -> 116
+    assert L.swiglu_gemm_packed_bytes(72, 136) == 1 * 2 * 32768
+    assert L.swiglu_gemm_packed_bytes(12, 8) == 0 and L.swiglu_gemm_packed_bytes(8, 0) == 0
+    G = L.swiglu_gemm_packed
+    assert G(None, None, None, 0, 64, 64, None) == OK
+    assert G(A_, WP_, Y_, 4, 60, 64, None) == UNSUP
+    assert G(A_, None, Y_, 4, 64, 64, None) == NULLP
+    assert G(A_, WP_, Y_ + 2, 4, 64, 64, None) == MISAL
+    assert G(A_, WP_, WP_ + 1024, 4, 64, 64, None) == ALIAS
+    assert G(A_, WP_, A_ + 16, 4, 64, 64, None) == ALIAS
+    P = L.swiglu_gemm_pack_weight
+    assert P(W1_, W1_ + 16, 64, 64, None) == ALIAS
+    assert P(W1_, WP_, 64, 63, None) == UNSUP
+    assert P(None, WP_, 64, 64, None) == NULLP
+    U = L.swiglu_unfused_packed
+    assert U(None, None, None, None, None, None, 0, 64, 64, None) == OK
+    assert U(A_, W1_, W2_, Y_, Y_, WS_, 4, 64, 64, None) == ALIAS
+    assert U(A_, W1_, W2_, W1_ + 64, WP_, WS_, 4, 64, 64, None) == ALIAS
+    assert U(A_, W1_, W2_, None, WP_, WS_, 4, 64, 64, None) == NULLP
+
+
 def test_interleaved_errors():
     L = sw.lib()
     assert L.swiglu_pack_weights_interleaved(W1_, W2_, W1_ + 16, 64, 64, None) == ALIAS
@@ -262,12 +288,26 @@ def test_binding_rejects_wrong_sizes():
         sw.swiglu_unfused(A, W, W, U=torch.zeros(M, 8, dtype=bf))
     with pytest.raises(ValueError, match="Y must be"):
         sw.swiglu_silu_mul(torch.zeros(M, N, dtype=bf), torch.zeros(M, N, dtype=bf), Y=torch.zeros(M, 8, dtype=bf))
-    with pytest.raises(ValueError, match="W3 must be"):
+    wg = torch.zeros(sw.swiglu_gemm_packed_bytes(K, N) // 2, dtype=bf)
+    w3g = torch.zeros(sw.swiglu_gemm_packed_bytes(N, K) // 2, dtype=bf)
+    with pytest.raises(ValueError, match="W3g holds"):
         sw.swiglu_mlp_packed(A, wp, torch.zeros(K, N, dtype=bf), N)
     with pytest.raises(ValueError, match="Z must be"):
-        sw.swiglu_mlp_down(torch.zeros(M, N, dtype=bf), torch.zeros(N, K, dtype=bf), Z=torch.zeros(M, 8, dtype=bf))
-    with pytest.raises(ValueError, match="W3 must be"):
-        sw.swiglu_mlp_unfused(A, W, W, torch.zeros(K, K, dtype=bf))
+        sw.swiglu_mlp_down(torch.zeros(M, N, dtype=bf), w3g, K, Z=torch.zeros(M, 8, dtype=bf))
+    with pytest.raises(ValueError, match="W3g holds"):
+        sw.swiglu_mlp_down(torch.zeros(M, N, dtype=bf), w3g[:-8], K)
+    with pytest.raises(ValueError, match="W3g holds"):
+        sw.swiglu_mlp_unfused(A, wg, wg, torch.zeros(K, K, dtype=bf), N)
+    with pytest.raises(ValueError, match="W2g holds"):
+        sw.swiglu_mlp_unfused(A, wg, wg[:-8], w3g, N)
+    with pytest.raises(ValueError, match="Wg holds"):
+        sw.swiglu_gemm_packed(A, wg[:-8], N)
+    with pytest.raises(ValueError, match="C must be"):
+        sw.swiglu_gemm_packed(A, wg, N, C=torch.zeros(M, N - 8, dtype=bf))
+    with pytest.raises(ValueError, match="W1g holds"):
+        sw.swiglu_unfused_packed(A, wg[:-8], wg, N)
+    with pytest.raises(ValueError, match="Wg holds"):
+        sw.swiglu_gemm_pack_weight(W, Wg=wg[:-8])
     # the pack entry points read W2 at W1's shape; the interleaved unpack
     # reads a whole packed buffer
     with pytest.raises(ValueError, match="W2 must be"):

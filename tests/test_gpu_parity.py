@@ -352,17 +352,19 @@ def test_mlp_block(dev, M, K, N):
     step on the GPU's own bf16 Gate and Up (their one-ulp rounding
     differences from summation order are checked by test_unfused_pipeline),
     Z against the oracle's GEMM of the GPU's own Y (isolating the down
-    projection), and the fused block's Y bitwise equal to a plain
-    swiglu_fused_packed call."""
+    projection, on the single-weight pack of W3), and the fused block's Y
+    bitwise equal to a plain swiglu_fused_packed call."""
     A, W1, W2 = inputs.gaussian_case(M, K, N, seed=7 * M + K + N)
     W3 = inputs.weight(N, K, seed=M + K)
     Ad, W1d, W2d, W3d = A.to(dev), W1.to(dev), W2.to(dev), W3.to(dev)
     Wp = sw.swiglu_pack_weights(W1d, W2d)
     say("[mlp] M=%d K=%d N=%d" % (M, K, N))
-    Yf, Zf = sw.swiglu_mlp_packed(Ad, Wp, W3d, N)
+    W3g = sw.swiglu_gemm_pack_weight(W3d)
+    W1g, W2g = sw.swiglu_gemm_pack_weight(W1d), sw.swiglu_gemm_pack_weight(W2d)
+    Yf, Zf = sw.swiglu_mlp_packed(Ad, Wp, W3g, N)
     G = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     U = torch.empty_like(G)
-    Yu, Zu = sw.swiglu_mlp_unfused(Ad, W1d, W2d, W3d, G=G, U=U)
+    Yu, Zu = sw.swiglu_mlp_unfused(Ad, W1g, W2g, W3g, N, G=G, U=U)
     Y0 = sw.swiglu_fused_packed(Ad, Wp, N)
     torch.cuda.synchronize()
     yf, zf, yu, zu = gpu_bits(Yf), gpu_bits(Zf), gpu_bits(Yu), gpu_bits(Zu)
@@ -373,11 +375,11 @@ def test_mlp_block(dev, M, K, N):
     check_gemm_ulp(gpu_bits(G), oracle.gemm_bf16(A, W1), "mlp unfused G")
     check_gemm_ulp(gpu_bits(U), oracle.gemm_bf16(A, W2), "mlp unfused U")
     W3b = inputs.as_bits(W3)
-    check_close(zf, oracle.gemm_bf16(yf, W3b), "mlp fused Z")
-    check_close(zu, oracle.gemm_bf16(yu, W3b), "mlp unfused Z")
-    Zd = sw.swiglu_mlp_down(Yf, W3d)
+    check_gemm_ulp(zf, oracle.gemm_bf16(yf, W3b), "mlp fused Z")
+    check_gemm_ulp(zu, oracle.gemm_bf16(yu, W3b), "mlp unfused Z")
+    Zd = sw.swiglu_mlp_down(Yf, W3g, K)
     torch.cuda.synchronize()
-    check_close(gpu_bits(Zd), oracle.gemm_bf16(yf, W3b), "mlp down projection alone")
+    check_gemm_ulp(gpu_bits(Zd), oracle.gemm_bf16(yf, W3b), "mlp down projection alone")
 
 
 def test_interleaved_pack_roundtrip_and_layout(dev):
@@ -475,3 +477,71 @@ def check_gemm_ulp(got_bits, ref_bits, what):
     bad = np.argwhere(np.abs(got - ref) > 2.0 ** -7 * np.abs(ref) + 1e-3)
     assert bad.size == 0, "%s: %d elements beyond 1 ulp, e.g. %s got %r want %r" % (
         what, len(bad), bad[0].tolist(), got[tuple(bad[0])], ref[tuple(bad[0])])
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (1, 200, 264), (16, 3584, 1032), (17, 136, 520), (32, 896, 4864),   # decode GEMM
+    (48, 200, 1032), (64, 72, 136),                                        # decode, few panels
+    (64, 3584, 18944),                                                     # panel schedule
+    (128, 4864, 896),                                                      # down-projection shape: 3.5 tiles
+    (300, 200, 520), (2100, 136, 264),                                     # 128-row tiles
+    (2304, 128, 7680),                                                     # 256-row tiles + 128-row tail
+    (4096, 136, 16384),                                                    # four 256-row tiles per workgroup
+])
+def test_gemm_packed_against_oracle(dev, M, K, N):
+    """The plain GEMM on the single-weight pack, through every schedule of the
+    fused product (decode, panels, 128-row tiles, persistent 256-row tiles
+    with the mixed tail): every element within one bf16 rounding flip of the
+    oracle's GEMM; partial last tiles in both halves (N not a multiple of 256
+    or of 128), ragged K."""
+    A, W, _ = inputs.gaussian_case(M, K, N, seed=3 * M + K + 7 * N)
+    say("[gemm_packed] M=%d K=%d N=%d" % (M, K, N))
+    Wg = sw.swiglu_gemm_pack_weight(W.to(dev))
+    C = sw.swiglu_gemm_packed(A.to(dev), Wg, N)
+    torch.cuda.synchronize()
+    check_gemm_ulp(gpu_bits(C), oracle.gemm_bf16(A, W), "gemm_packed %s" % ((M, K, N),))
+
+
+def test_gemm_pack_layout(dev):
+    """Single-weight pack as documented in swiglu.h: tile jt holds columns
+    jt*256 + g*16 + l%16 in 16-row group g; padding (columns past N, k past
+    K) is zero."""
+    for K, N in [(64, 256), (72, 264), (200, 1032)]:
+        _, W, _ = inputs.gaussian_case(1, K, N, seed=5 * K + N)
+        P = inputs.as_bits(sw.swiglu_gemm_pack_weight(W.to(dev)).cpu())
+        assert P.size * 2 == sw.swiglu_gemm_packed_bytes(K, N)
+        w = inputs.as_bits(W)
+        KB, JT = (K + 63) // 64, (N + 255) // 256
+
+        def pos(jt, kb, g, h, l, e):
+            return ((((jt * KB + kb) * 16 + g) * 2 + h) * 64 + l) * 8 + e
+
+        for n in range(0, N, 3):
+            for k in range(0, K, 7):
+                jt, r, kb, kk = n // 256, n % 256, k // 64, k % 64
+                g, h, l, e = r // 16, kk // 32, ((kk % 32) // 8) * 16 + r % 16, kk % 8
+                assert P[pos(jt, kb, g, h, l, e)] == w[k, n]
+        for r in range(N % 256 or 256, 256):
+            assert P[pos(JT - 1, 0, r // 16, 0, r % 16, 0)] == 0
+        if K % 64:
+            for n in range(0, N, 13):
+                r, kk = n % 256, K % 64
+                assert P[pos(n // 256, KB - 1, r // 16, kk // 32, ((kk % 32) // 8) * 16 + r % 16, kk % 8)] == 0
+
+
+@pytest.mark.parametrize("M,K,N", [(16, 3584, 18944), (64, 896, 4864), (4096, 896, 4864)])
+def test_unfused_packed_pipeline(dev, M, K, N):
+    """The unfused pipeline on the packed GEMM: G and U within one bf16 flip
+    of the oracle's GEMMs, Y within tolerance of the oracle's element-wise
+    step on the GPU's own G and U."""
+    A, W1, W2 = inputs.gaussian_case(M, K, N, seed=M + 2 * K + N)
+    Ad = A.to(dev)
+    W1g, W2g = sw.swiglu_gemm_pack_weight(W1.to(dev)), sw.swiglu_gemm_pack_weight(W2.to(dev))
+    say("[unfused_packed] M=%d K=%d N=%d" % (M, K, N))
+    G, U, Y = sw.swiglu_unfused_packed(Ad, W1g, W2g, N)
+    torch.cuda.synchronize()
+    Gb, Ub, Yb = gpu_bits(G), gpu_bits(U), gpu_bits(Y)
+    rows = list(range(M)) if M <= 64 else sample_rows(M, 16)
+    check_gemm_ulp(Gb[rows], oracle.gemm_bf16(A[rows].contiguous(), W1), "G")
+    check_gemm_ulp(Ub[rows], oracle.gemm_bf16(A[rows].contiguous(), W2), "U")
+    check_close(Yb, oracle.silu_mul(Gb, Ub), "silu_mul of the GPU's own G, U")
