@@ -104,7 +104,11 @@ typedef enum {
  *                 and the Up half.  Same result as DATA_PARALLEL, bit for bit;
  *                 any M; no workspace.  AUTO never picks it (it re-reads the
  *                 activation tiles and is slower on this chip at every
- *                 measured shape); it exists for comparison. */
+ *                 measured shape); it exists for comparison.
+ * There is no stream-K schedule: the even share of work per CU it would give
+ * comes from the column-split schedules (DECODE, the panel form of
+ * DATA_PARALLEL) at small M and from the 128-row tail tiles of the last round
+ * at large M, with no partial sums through memory. */
 typedef enum {
     SWIGLU_VARIANT_AUTO = 0,
     SWIGLU_VARIANT_DATA_PARALLEL = 1,
