@@ -1512,17 +1512,25 @@ struct DecodeArgs {
 // jt holds W's columns jt*256 + 0..255); the "Gate" sums of tile column c are
 // output column jt*256 + c, the "Up" sums jt*256 + 128 + c; p.N is C's width
 // (the grid covers the packed tiles' 128 columns each).
-template <int MT, int CG, int UNROLL, bool GEMM = false>
+// HALF (GEMM only): each workgroup takes one of the two halves of its column
+// groups (blockIdx.x & 1: the "Gate" rows, i.e. output columns jt*256 + c, or
+// the "Up" rows, jt*256 + 128 + c), so a single-weight product has as many
+// workgroups, each streaming half the bytes, as the fused product on weights
+// of the same width -- finer work units for the CUs to balance.
+template <int MT, int CG, int UNROLL, bool GEMM = false, bool HALF = false>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
+    static_assert(GEMM || !HALF, "HALF splits the single-weight product only");
     constexpr int WAVES = 4;
-    __shared__ f32x4 red[WAVES][MT][CG][2][64];
+    constexpr int NH = HALF ? 1 : 2;    // weight halves per workgroup
+    __shared__ f32x4 red[WAVES][MT][CG][NH][64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int r16 = lane & 15;          // weight row within a group / token within a tile
     const int kq = lane >> 4;           // which 8-wide K slice of a 32-deep step
-    const int n0 = blockIdx.x * (16 * CG);
+    const int half = HALF ? (int)(blockIdx.x & 1) : 0;
+    const int n0 = (HALF ? (int)(blockIdx.x >> 1) : (int)blockIdx.x) * (16 * CG);
     const int jt = n0 / PACK_BN, ro = n0 % PACK_BN;
     const int M = p.M, K = p.K, N = p.N, KB = p.KB;
 
@@ -1556,8 +1564,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
                 for (int h = 0; h < 2; ++h) {
 #pragma unroll
                     for (int c = 0; c < CG; ++c) {
-                        wg[u][h][c] = ld16(wtile + boff + (((grp0 + c) * 2 + h) * 64 + lane) * 8);
-                        wu[u][h][c] = ld16(wtile + boff + (((grp0 + c + 8) * 2 + h) * 64 + lane) * 8);
+                        wg[u][h][c] = ld16(wtile + boff + (((grp0 + c + 8 * half) * 2 + h) * 64 + lane) * 8);
+                        if constexpr (!HALF)
+                            wu[u][h][c] = ld16(wtile + boff + (((grp0 + c + 8) * 2 + h) * 64 + lane) * 8);
                     }
                     const int k = kb * PACK_BK + 32 * h + 8 * kq;
 #pragma unroll
@@ -1580,8 +1589,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
                         for (int c = 0; c < CG; ++c) {
                             accg[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                                 __builtin_bit_cast(bf16x8, wg[u][h][c]), a8, accg[t][c], 0, 0, 0);
-                            accu[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf16x8, wu[u][h][c]), a8, accu[t][c], 0, 0, 0);
+                            if constexpr (!HALF)
+                                accu[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    __builtin_bit_cast(bf16x8, wu[u][h][c]), a8, accu[t][c], 0, 0, 0);
                         }
                     }
             }
@@ -1593,21 +1603,29 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
 #pragma unroll
         for (int c = 0; c < CG; ++c) {
             red[wave][t][c][0][lane] = accg[t][c];
-            red[wave][t][c][1][lane] = accu[t][c];
+            if constexpr (!HALF) red[wave][t][c][NH - 1][lane] = accu[t][c];
         }
     __syncthreads();
     // epilogue: wave w finishes (token tile, column group) pairs w, w+4, ...
     for (int tc = wave; tc < MT * CG; tc += WAVES) {
         const int t = tc / CG, c = tc % CG;
-        f32x4 g = red[0][t][c][0][lane], u = red[0][t][c][1][lane];
+        f32x4 g = red[0][t][c][0][lane], u = red[0][t][c][NH - 1][lane];
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) {
             g += red[w][t][c][0][lane];
-            u += red[w][t][c][1][lane];
+            if constexpr (!HALF) u += red[w][t][c][NH - 1][lane];
         }
         const int m = t * 16 + r16;
         const int n = n0 + 16 * c + 4 * kq;
-        if constexpr (GEMM) {
+        if constexpr (HALF) {
+            const int col = (n / PACK_BN) * PACK_ROWS + n % PACK_BN + PACK_BN * half;
+            if (m < M && col < N) {
+                u32x2 out;
+                out[0] = pack2(g[0], g[1]);
+                out[1] = pack2(g[2], g[3]);
+                *reinterpret_cast<u32x2*>(p.Y + (size_t)m * N + col) = out;
+            }
+        } else if constexpr (GEMM) {
             const int col = (n / PACK_BN) * PACK_ROWS + n % PACK_BN;
             if (m < M && col < N) {
                 u32x2 out;

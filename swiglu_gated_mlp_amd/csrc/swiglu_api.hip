@@ -284,13 +284,15 @@ hipError_t launch_tile(const swk::FusedArgs& a, int grid, hipStream_t s) {
 }
 
 // n_tiled: the packed weights' output columns (N for the fused product; 128
-// per packed tile for the single-weight GEMM)
-template <int MT, int CG, int UNROLL, bool GEMM = false>
+// per packed tile for the single-weight GEMM).  HALF: one workgroup per
+// (column groups, weight half), twice the grid.
+template <int MT, int CG, int UNROLL, bool GEMM = false, bool HALF = false>
 hipError_t launch_decode(const swk::DecodeArgs& a, int64_t n_tiled, hipStream_t s) {
-    const void* fn = reinterpret_cast<const void*>(&swk::decode_kernel<MT, CG, UNROLL, GEMM>);
+    const void* fn = reinterpret_cast<const void*>(&swk::decode_kernel<MT, CG, UNROLL, GEMM, HALF>);
     swk::DecodeArgs args = a;
     void* kargs[] = {&args};
-    return hipLaunchKernel(fn, dim3((unsigned)ceil_div(n_tiled, 16 * CG)), dim3(256), kargs, 0, s);
+    return hipLaunchKernel(fn, dim3((unsigned)(ceil_div(n_tiled, 16 * CG) * (HALF ? 2 : 1))), dim3(256), kargs, 0,
+                           s);
 }
 
 template <int BM, int BN, int WM, int WN, bool SPLIT, int WSRC = swk::W_PACKED>
@@ -385,21 +387,57 @@ hipError_t launch_decode_fp8(const swk::FusedArgs& a, int cus, hipStream_t s) {
 // longer contiguous runs of the packed blocks; they pay off for long K (>= 96
 // blocks) as long as the grid still gives about one workgroup per CU.
 // n_tiled: the packed weights' output columns.
-template <bool GEMM>
 hipError_t launch_decode_cfg(const swk::DecodeArgs& d, int64_t n_tiled, const Plan& p, hipStream_t s) {
     const bool long_k = p.KB >= 96;
     const int64_t wg64 = ceil_div(n_tiled, 64), wg128 = ceil_div(n_tiled, 128);
     switch (p.decode_mt) {
         case 1:
-            return (long_k && 4 * wg128 >= 3 * p.cus) ? launch_decode<1, 8, 2, GEMM>(d, n_tiled, s)
-                                                     : launch_decode<1, 1, 8, GEMM>(d, n_tiled, s);
+            return (long_k && 4 * wg128 >= 3 * p.cus) ? launch_decode<1, 8, 2>(d, n_tiled, s)
+                                                     : launch_decode<1, 1, 8>(d, n_tiled, s);
         case 2:
-            if (long_k && 4 * wg64 >= 3 * p.cus) return launch_decode<2, 4, 1, GEMM>(d, n_tiled, s);
-            return 2 * wg128 >= p.cus ? launch_decode<2, 8, 1, GEMM>(d, n_tiled, s)
-                                      : launch_decode<2, 2, 2, GEMM>(d, n_tiled, s);
+            if (long_k && 4 * wg64 >= 3 * p.cus) return launch_decode<2, 4, 1>(d, n_tiled, s);
+            return 2 * wg128 >= p.cus ? launch_decode<2, 8, 1>(d, n_tiled, s)
+                                      : launch_decode<2, 2, 2>(d, n_tiled, s);
         default:
-            return (long_k && 4 * wg64 >= 3 * p.cus) ? launch_decode<4, 4, 1, GEMM>(d, n_tiled, s)
-                                                    : launch_decode<4, 2, 1, GEMM>(d, n_tiled, s);
+            return (long_k && 4 * wg64 >= 3 * p.cus) ? launch_decode<4, 4, 1>(d, n_tiled, s)
+                                                    : launch_decode<4, 2, 1>(d, n_tiled, s);
+    }
+}
+
+// The same for the single-weight GEMM (n_tiled = 128 per 256-column packed
+// tile), where a workgroup may take one weight half (HALF): half the bytes per
+// workgroup and twice the grid.  Measured on this chip (us, one call, inputs
+// rotated past the last-level cache):
+//   K=3584 N=18944 M=1: <1,1,14,H> 23.8, <1,1,8,H> 24.5, <1,1,8> 25.7
+//   K=3584 N=18944 M=16: <1,1,8> 28.7, <1,1,8,H> 31.4
+//   K=8192 N=29568 M=1 / 16: <1,4,4,H> 85.5 / 86.6, <1,1,8> 102.2 / 109.5
+//   K=18944 N=3584 M=1 / 16: <1,1,14,H> 24.3 / 32.4, <1,1,8,H> 24.7 / 31.8, <1,1,8> 31.3 / 43.3
+//   K=8192 N=29568 M=32: <2,4,1> 86.6, <2,8,1,H> 86.4, <2,2,2,H> 123.4
+//   K=29568 N=8192 M=32: <2,2,2,H> 96.1, <2,2,2> 132.1, <2,4,1,H> 125.9
+//   K=896 N=4864 M=64: <4,2,1,H> 7.9, <4,2,1> 9.4
+//   K=4864 N=896 M=64: <4,1,1,H> 22.1, <4,2,1,H> 24.3, <4,2,1> 32.0
+// i.e. halves whenever the whole-pair grid leaves CUs short of work, and the
+// deepest per-wave prefetch the registers allow at one or two tokens' rows.
+hipError_t launch_decode_gemm(const swk::DecodeArgs& d, int64_t n_tiled, const Plan& p, hipStream_t s) {
+    const bool long_k = p.KB >= 96;
+    const int64_t wg16 = ceil_div(n_tiled, 16), wg64 = ceil_div(n_tiled, 64);
+    switch (p.decode_mt) {
+        case 1:
+            if (long_k && 2 * wg64 >= p.cus) return launch_decode<1, 4, 4, true, true>(d, n_tiled, s);
+            if (d.M <= 8) return launch_decode<1, 1, 14, true, true>(d, n_tiled, s);
+            return wg16 < 2 * p.cus ? launch_decode<1, 1, 8, true, true>(d, n_tiled, s)
+                                    : launch_decode<1, 1, 8, true>(d, n_tiled, s);
+        case 2:
+            if (long_k) {
+                return 4 * wg64 >= 3 * p.cus ? launch_decode<2, 4, 1, true>(d, n_tiled, s)
+                                             : launch_decode<2, 2, 2, true, true>(d, n_tiled, s);
+            }
+            return 2 * ceil_div(n_tiled, 128) >= p.cus ? launch_decode<2, 8, 1, true>(d, n_tiled, s)
+                                                       : launch_decode<2, 2, 2, true>(d, n_tiled, s);
+        default:
+            if (long_k && 4 * wg64 >= 3 * p.cus) return launch_decode<4, 4, 1, true>(d, n_tiled, s);
+            return p.KB >= 32 ? launch_decode<4, 1, 1, true, true>(d, n_tiled, s)
+                              : launch_decode<4, 2, 1, true, true>(d, n_tiled, s);
     }
 }
 
@@ -409,7 +447,7 @@ hipError_t launch_packed(const swk::FusedArgs& a, const Plan& p, hipStream_t s) 
         swk::DecodeArgs d{};
         d.A = a.A; d.Wp = a.W1; d.Y = a.Y;
         d.M = a.M; d.K = a.K; d.N = a.N; d.KB = a.KB;
-        return launch_decode_cfg<false>(d, a.N, p, s);
+        return launch_decode_cfg(d, a.N, p, s);
     }
     const int grid = p.tiles * p.splits;
     const bool split = p.splits > 1;
@@ -837,7 +875,7 @@ swiglu_status swiglu_gemm_packed(const swiglu_bf16* A, const swiglu_bf16* Wg, sw
         swk::DecodeArgs d{};
         d.A = A; d.Wp = Wg; d.Y = C;
         d.M = (int)M; d.K = (int)K; d.N = (int)N; d.KB = p.KB;
-        e = launch_decode_cfg<true>(d, nt, p, s);
+        e = launch_decode_gemm(d, nt, p, s);
     } else {
         swk::FusedArgs a{};
         a.A = A; a.W1 = Wg; a.W2 = nullptr; a.Y = C;

@@ -480,8 +480,16 @@ def check_gemm_ulp(got_bits, ref_bits, what):
 
 
 @pytest.mark.parametrize("M,K,N", [
-    (1, 200, 264), (16, 3584, 1032), (17, 136, 520), (32, 896, 4864),   # decode GEMM
-    (48, 200, 1032), (64, 72, 136),                                        # decode, few panels
+    # decode GEMM, each of its configurations on a 256-CU chip:
+    (1, 200, 264),                  # <1,1,14> on weight halves (M <= 8)
+    (16, 3584, 1032),               # <1,1,8> on halves (few column groups)
+    (12, 200, 16400),               # <1,1,8> on both halves (wide)
+    (3, 6200, 16400),               # <1,4,4> on halves (long K, wide)
+    (17, 136, 520), (32, 896, 4864),  # <2,2,2>
+    (24, 6200, 24600),              # <2,4,1> (long K, wide)
+    (20, 6200, 1000),               # <2,2,2> on halves (long K, narrow)
+    (48, 200, 1032), (64, 72, 136),   # <4,2,1> on halves (short K, few panels)
+    (40, 2104, 520),                # <4,1,1> on halves (few panels)
     (64, 3584, 18944),                                                     # panel schedule
     (128, 4864, 896),                                                      # down-projection shape: 3.5 tiles
     (300, 200, 520), (2100, 136, 264),                                     # 128-row tiles
