@@ -385,7 +385,13 @@ hipError_t launch_decode_fp8(const swk::FusedArgs& a, int cus, hipStream_t s) {
 // (CG) and K blocks in flight per wave (UNROLL), measured on this chip: wider
 // groups read each activation fragment for more weight bytes and stream
 // longer contiguous runs of the packed blocks; they pay off for long K (>= 96
-// blocks) as long as the grid still gives about one workgroup per CU.
+// blocks), or from 17 tokens on, as long as the grid still gives about one
+// workgroup per CU.  Measured (us, one call, inputs rotated past the
+// last-level cache):
+//   K=3584 N=18944 M=1 / 16: <1,1,8> 42.9 / 45.8, <1,1,4> 43.0 / 46.3, <1,2,4> 46.1 / 47.5
+//   K=8192 N=29568 M=32: <2,8,1> 140.2, <2,4,1> 147.3, <2,2,2> 170.4
+//   K=3584 N=18944 M=32: <2,8,1> 52.2, <2,2,2> 54.7, <2,4,1> 61.8
+//   K=896 N=4864 M=64: <4,2,1> 9.9, <4,2,2> 10.5, <4,1,1> 11.8
 // n_tiled: the packed weights' output columns.
 hipError_t launch_decode_cfg(const swk::DecodeArgs& d, int64_t n_tiled, const Plan& p, hipStream_t s) {
     const bool long_k = p.KB >= 96;
@@ -395,9 +401,9 @@ hipError_t launch_decode_cfg(const swk::DecodeArgs& d, int64_t n_tiled, const Pl
             return (long_k && 4 * wg128 >= 3 * p.cus) ? launch_decode<1, 8, 2>(d, n_tiled, s)
                                                      : launch_decode<1, 1, 8>(d, n_tiled, s);
         case 2:
-            if (long_k && 4 * wg64 >= 3 * p.cus) return launch_decode<2, 4, 1>(d, n_tiled, s);
-            return 2 * wg128 >= p.cus ? launch_decode<2, 8, 1>(d, n_tiled, s)
-                                      : launch_decode<2, 2, 2>(d, n_tiled, s);
+            if (2 * wg128 >= p.cus) return launch_decode<2, 8, 1>(d, n_tiled, s);
+            return (long_k && 4 * wg64 >= 3 * p.cus) ? launch_decode<2, 4, 1>(d, n_tiled, s)
+                                                    : launch_decode<2, 2, 2>(d, n_tiled, s);
         default:
             return (long_k && 4 * wg64 >= 3 * p.cus) ? launch_decode<4, 4, 1>(d, n_tiled, s)
                                                     : launch_decode<4, 2, 1>(d, n_tiled, s);
@@ -408,14 +414,14 @@ hipError_t launch_decode_cfg(const swk::DecodeArgs& d, int64_t n_tiled, const Pl
 // tile), where a workgroup may take one weight half (HALF): half the bytes per
 // workgroup and twice the grid.  Measured on this chip (us, one call, inputs
 // rotated past the last-level cache):
-//   K=3584 N=18944 M=1: <1,1,14,H> 23.8, <1,1,8,H> 24.5, <1,1,8> 25.7
-//   K=3584 N=18944 M=16: <1,1,8> 28.7, <1,1,8,H> 31.4
-//   K=8192 N=29568 M=1 / 16: <1,4,4,H> 85.5 / 86.6, <1,1,8> 102.2 / 109.5
-//   K=18944 N=3584 M=1 / 16: <1,1,14,H> 24.3 / 32.4, <1,1,8,H> 24.7 / 31.8, <1,1,8> 31.3 / 43.3
-//   K=8192 N=29568 M=32: <2,4,1> 86.6, <2,8,1,H> 86.4, <2,2,2,H> 123.4
-//   K=29568 N=8192 M=32: <2,2,2,H> 96.1, <2,2,2> 132.1, <2,4,1,H> 125.9
-//   K=896 N=4864 M=64: <4,2,1,H> 7.9, <4,2,1> 9.4
-//   K=4864 N=896 M=64: <4,1,1,H> 22.1, <4,2,1,H> 24.3, <4,2,1> 32.0
+//   K=3584 N=18944 M=1: <1,1,14,H> 22.6, <1,1,8,H> 23.2, <1,1,8> 23.9
+//   K=3584 N=18944 M=16: <1,1,8> 26.7, <1,1,8,H> 29.7
+//   K=8192 N=29568 M=1 / 16: <1,4,4,H> 79.5 / 78.6, <1,1,8> 93.7 / 99.0
+//   K=18944 N=3584 M=1 / 16: <1,1,14,H> 23.3 / 31.3, <1,1,8,H> 23.6 / 30.8, <1,1,8> 30.6 / 42.6
+//   K=8192 N=29568 M=32: <2,8,1,H> 73.3, <2,4,1> 76.1, <2,2,2,H> 113.4
+//   K=29568 N=8192 M=32: <2,2,2,H> 92.8, <2,2,2> 129.3, <2,4,1,H> 123.9
+//   K=896 N=4864 M=64: <4,2,1,H> 8.0, <4,2,1> 9.5
+//   K=4864 N=896 M=64: <4,1,1,H> 21.8, <4,2,1,H> 24.4, <4,2,1> 31.8
 // i.e. halves whenever the whole-pair grid leaves CUs short of work, and the
 // deepest per-wave prefetch the registers allow at one or two tokens' rows.
 hipError_t launch_decode_gemm(const swk::DecodeArgs& d, int64_t n_tiled, const Plan& p, hipStream_t s) {
@@ -429,7 +435,7 @@ hipError_t launch_decode_gemm(const swk::DecodeArgs& d, int64_t n_tiled, const P
                                     : launch_decode<1, 1, 8, true>(d, n_tiled, s);
         case 2:
             if (long_k) {
-                return 4 * wg64 >= 3 * p.cus ? launch_decode<2, 4, 1, true>(d, n_tiled, s)
+                return 4 * wg64 >= 3 * p.cus ? launch_decode<2, 8, 1, true, true>(d, n_tiled, s)
                                              : launch_decode<2, 2, 2, true, true>(d, n_tiled, s);
             }
             return 2 * ceil_div(n_tiled, 128) >= p.cus ? launch_decode<2, 8, 1, true>(d, n_tiled, s)

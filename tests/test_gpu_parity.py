@@ -297,8 +297,9 @@ def test_edge_cases(dev):
 @pytest.mark.parametrize("M,K,N,auto_decode", [
     (1, 6144, 24576, True),    # long K, >= 192 column tiles: 8 column groups per workgroup
     (16, 3584, 4096, True),    # short K: one column group, 8 K blocks in flight per wave
-    (32, 6144, 12288, True),   # long K, M <= 32: 4 column groups
-    (32, 512, 16384, True),    # short K, wide N: 8 column groups
+    (32, 6144, 12288, True),   # long K, M <= 32, under two workgroups per CU: 4 column groups
+    (32, 512, 16384, True),    # M <= 32, wide N: 8 column groups
+    (24, 512, 4096, True),     # M <= 32, short K, narrow N: 2 column groups, 2 K blocks in flight
     (48, 6144, 12288, False),  # long K, M <= 64: 4 column groups (AUTO takes the panel schedule)
     (64, 1024, 2048, True),    # short K, M <= 64, few panels: 2 column groups
 ])
@@ -486,7 +487,7 @@ def check_gemm_ulp(got_bits, ref_bits, what):
     (12, 200, 16400),               # <1,1,8> on both halves (wide)
     (3, 6200, 16400),               # <1,4,4> on halves (long K, wide)
     (17, 136, 520), (32, 896, 4864),  # <2,2,2>
-    (24, 6200, 24600),              # <2,4,1> (long K, wide)
+    (24, 6200, 24600),              # <2,8,1> on halves (long K, wide)
     (20, 6200, 1000),               # <2,2,2> on halves (long K, narrow)
     (48, 200, 1032), (64, 72, 136),   # <4,2,1> on halves (short K, few panels)
     (40, 2104, 520),                # <4,1,1> on halves (few panels)
