@@ -383,8 +383,8 @@ def bench_mlp(w, M, steps, warmup, stream, prewarm_s=0.0):
     fused = [(lambda d=d: sw.swiglu_mlp_packed(d["A"], d["Wp"], d["W3g"], N, Y=d["Y"], Z=d["Z"],
                                                workspace=d["ws"])) for d in sets]
     unfused = [(lambda d=d: sw.swiglu_mlp_unfused(d["A"], d["W1g"], d["W2g"], d["W3g"], N, d["G"], d["U"],
-                                                  d["Y"], d["Z"])) for d in sets]
-    down = [(lambda d=d: sw.swiglu_mlp_down(d["Y"], d["W3g"], K, d["Z"])) for d in sets]
+                                                  d["Y"], d["Z"], workspace=d["ws"])) for d in sets]
+    down = [(lambda d=d: sw.swiglu_mlp_down(d["Y"], d["W3g"], K, d["Z"], workspace=d["ws"])) for d in sets]
     tf = time_gpu(fused, steps, warmup, stream, prewarm_s) / steps
     tu = time_gpu(unfused, steps, warmup, stream, prewarm_s) / steps
     td = time_gpu(down, steps, warmup, stream, prewarm_s) / steps

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SWIGLU_ABI_VERSION 2
+#define SWIGLU_ABI_VERSION 3
 
 typedef uint16_t swiglu_bf16;
 
@@ -336,12 +336,23 @@ swiglu_status swiglu_unfused(const swiglu_bf16 *A, const swiglu_bf16 *W1,
  *
  * swiglu_gemm_packed_bytes: size of Wg in bytes (0 for an invalid shape).
  * swiglu_gemm_pack_weight:  W [K,N] -> Wg; Wg must not overlap W.
+ * swiglu_gemm_workspace_bytes: bytes of fp32 partial sums swiglu_gemm_packed
+ *   uses for (M,K,N) when given that much workspace: the fused product's AUTO
+ *   rule on the pack's tiled width (ceil(N/256)*128 columns) asks for split-K
+ *   when its data-parallel tiles would leave most CUs idle; then
+ *   splits * M * 2 * ceil(N/256)*128 * 4 bytes, else 0.
  * swiglu_gemm_packed:       C[M,N] = bf16_RNE(A[M,K] x W), fp32 accumulation
- *   in the fused product's MFMA order; C must not overlap A or Wg.  No
- *   workspace (split-K is never used); products whose activations reach
- *   2 GiB run as row chunks.
+ *   in the fused product's MFMA order; C must not overlap A or Wg.  With a
+ *   workspace of at least swiglu_gemm_workspace_bytes(M,K,N) bytes (16-byte
+ *   aligned device memory, not overlapping A, Wg or C; caller-owned, contents
+ *   on entry irrelevant) a split-K plan runs split (the splits' fp32 partial
+ *   sums of each output added in split order by a second launch, so results
+ *   are deterministic); with less, or workspace NULL, the data-parallel
+ *   schedule runs (no error).  Products whose activations reach 2 GiB run as
+ *   row chunks, data-parallel.
  * swiglu_unfused_packed:    G = gemm_packed(A, W1g); U = gemm_packed(A, W2g);
- *   Y = silu_mul(G, U); G_scratch, U_scratch, Y as in swiglu_unfused.
+ *   Y = silu_mul(G, U); G_scratch, U_scratch, Y as in swiglu_unfused (the two
+ *   GEMMs without workspace, i.e. data-parallel).
  * All: K and N multiples of 8, pointers 16-byte aligned, M == 0 returns
  * SWIGLU_OK without a launch, validation before any launch, work enqueued
  * on `stream` with no synchronisation.
@@ -349,8 +360,10 @@ swiglu_status swiglu_unfused(const swiglu_bf16 *A, const swiglu_bf16 *W1,
 size_t swiglu_gemm_packed_bytes(int64_t K, int64_t N);
 swiglu_status swiglu_gemm_pack_weight(const swiglu_bf16 *W, swiglu_bf16 *Wg,
                                       int64_t K, int64_t N, void *stream);
+size_t swiglu_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 swiglu_status swiglu_gemm_packed(const swiglu_bf16 *A, const swiglu_bf16 *Wg,
                                  swiglu_bf16 *C, int64_t M, int64_t K, int64_t N,
+                                 void *workspace, size_t workspace_bytes,
                                  void *stream);
 swiglu_status swiglu_unfused_packed(const swiglu_bf16 *A, const swiglu_bf16 *W1g,
                                     const swiglu_bf16 *W2g,
@@ -370,23 +383,33 @@ swiglu_status swiglu_unfused_packed(const swiglu_bf16 *A, const swiglu_bf16 *W1g
  * The down projection is a plain GEMM outside the fused product: W3 [N,K]
  * is passed in the single-weight pack (W3g = swiglu_gemm_pack_weight of the
  * [N,K] matrix, swiglu_gemm_packed_bytes(N, K) bytes) and Z =
- * swiglu_gemm_packed(Y, W3g) with N as the depth.
+ * swiglu_gemm_packed(Y, W3g, workspace) with N as the depth.
  *
+ * swiglu_mlp_workspace_bytes: workspace for the fastest schedules of
+ *   swiglu_mlp_packed / swiglu_mlp_unfused / swiglu_mlp_down: the larger of
+ *   swiglu_workspace_bytes(M,K,N,variant) (the fused product) and
+ *   swiglu_gemm_workspace_bytes(M,N,K) (the down projection).
  * swiglu_mlp_packed:  Y = swiglu_fused_packed(A, Wp, ...), then Z = Y x W3.
  *   Y is a caller-owned [M,N] bf16 device buffer and holds the SwiGLU
  *   product on return; workspace, workspace_bytes and variant are those of
- *   swiglu_fused_packed.  Z must not overlap A, Wp, W3g, Y or the workspace;
- *   Y must not overlap W3g (nor the inputs, as in swiglu_fused_packed).
+ *   swiglu_fused_packed, and the same workspace then serves the down
+ *   projection as in swiglu_gemm_packed (split-K only if it is large
+ *   enough).  Z must not overlap A, Wp, W3g, Y or the workspace; Y must not
+ *   overlap W3g (nor the inputs, as in swiglu_fused_packed).
  * swiglu_mlp_unfused: Y = swiglu_unfused_packed(A, W1g, W2g, G, U, ...), then
- *   Z = Y x W3 (W1g, W2g single-weight packs of W1, W2 [K,N]); Z must not
- *   overlap any other buffer, and no scratch may overlap W3g.
+ *   Z = Y x W3 (W1g, W2g single-weight packs of W1, W2 [K,N]), the down
+ *   projection with the workspace as in swiglu_gemm_packed (may be NULL); Z
+ *   must not overlap any other buffer or the workspace, and no scratch may
+ *   overlap W3g.
  * swiglu_mlp_down:    the down projection alone, Z = Y x W3 (the step both
- *   entry points above end with); Z must not overlap Y or W3g.
+ *   entry points above end with), the workspace as in swiglu_gemm_packed;
+ *   Z must not overlap Y or W3g.
  * All: K and N multiples of 8, pointers 16-byte aligned; M == 0 returns
  * SWIGLU_OK without a launch; the validation codes return before any launch;
  * a launch failure returns SWIGLU_ERR_HIP; work is enqueued on `stream`
  * with no synchronisation.
  * ---------------------------------------------------------------------- */
+size_t swiglu_mlp_workspace_bytes(int64_t M, int64_t K, int64_t N, int variant);
 swiglu_status swiglu_mlp_packed(const swiglu_bf16 *A, const swiglu_bf16 *Wp,
                                 const swiglu_bf16 *W3g, swiglu_bf16 *Y,
                                 swiglu_bf16 *Z, int64_t M, int64_t K, int64_t N,
@@ -394,12 +417,14 @@ swiglu_status swiglu_mlp_packed(const swiglu_bf16 *A, const swiglu_bf16 *Wp,
                                 int variant, void *stream);
 swiglu_status swiglu_mlp_down(const swiglu_bf16 *Y, const swiglu_bf16 *W3g,
                              swiglu_bf16 *Z, int64_t M, int64_t K, int64_t N,
+                             void *workspace, size_t workspace_bytes,
                              void *stream);
 swiglu_status swiglu_mlp_unfused(const swiglu_bf16 *A, const swiglu_bf16 *W1g,
                                  const swiglu_bf16 *W2g, const swiglu_bf16 *W3g,
                                  swiglu_bf16 *G_scratch, swiglu_bf16 *U_scratch,
                                  swiglu_bf16 *Y, swiglu_bf16 *Z, int64_t M,
-                                 int64_t K, int64_t N, void *stream);
+                                 int64_t K, int64_t N, void *workspace,
+                                 size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

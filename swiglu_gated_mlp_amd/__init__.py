@@ -56,14 +56,17 @@ SIGNATURES = {
     "swiglu_gemm_bf16": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "swiglu_gemm_packed_bytes": ([_I64, _I64], ctypes.c_size_t),
     "swiglu_gemm_pack_weight": ([_P, _P, _I64, _I64, _P], ctypes.c_int),
-    "swiglu_gemm_packed": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "swiglu_gemm_workspace_bytes": ([_I64, _I64, _I64], ctypes.c_size_t),
+    "swiglu_gemm_packed": ([_P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "swiglu_unfused_packed": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "swiglu_silu_mul": ([_P, _P, _P, _I64, _P], ctypes.c_int),
     "swiglu_unfused": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "swiglu_mlp_packed": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, ctypes.c_int, _P],
                           ctypes.c_int),
-    "swiglu_mlp_unfused": ([_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
-    "swiglu_mlp_down": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "swiglu_mlp_workspace_bytes": ([_I64, _I64, _I64, ctypes.c_int], ctypes.c_size_t),
+    "swiglu_mlp_unfused": ([_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P],
+                           ctypes.c_int),
+    "swiglu_mlp_down": ([_P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P], ctypes.c_int),
     # include/swiglu_probe.h (diagnostic ceilings)
     "swiglu_probe_mfma": ([_P, ctypes.c_int, ctypes.c_int, _P], ctypes.c_int),
     "swiglu_probe_read": ([_P, ctypes.c_size_t, _P, ctypes.c_int, _P], ctypes.c_int),
@@ -325,6 +328,18 @@ def swiglu_workspace_bytes(M: int, K: int, N: int, variant: int = VARIANT_AUTO) 
 _ws_need: dict = {}
 
 
+def _cached_need(kind: str, args: tuple, device: torch.device) -> int:
+    """swiglu_gemm_workspace_bytes ("gemm") or swiglu_mlp_workspace_bytes
+    ("mlp") of args, remembered per device (the plans depend only on the
+    shape and the device's CU count)."""
+    key = (kind, args, device.index)
+    need = _ws_need.get(key)
+    if need is None:
+        fn = swiglu_gemm_workspace_bytes if kind == "gemm" else swiglu_mlp_workspace_bytes
+        need = _ws_need[key] = fn(*args)
+    return need
+
+
 def _workspace_need(M: int, K: int, N: int, variant: int, device: torch.device) -> int:
     """swiglu_workspace_bytes, remembered per (shape, variant, device): the
     plan depends only on these and the device's CU count."""
@@ -333,6 +348,31 @@ def _workspace_need(M: int, K: int, N: int, variant: int, device: torch.device) 
     if need is None:
         need = _ws_need[key] = swiglu_workspace_bytes(M, K, N, variant)
     return need
+
+
+def swiglu_gemm_workspace_bytes(M: int, K: int, N: int) -> int:
+    return int(lib().swiglu_gemm_workspace_bytes(M, K, N))
+
+
+def swiglu_mlp_workspace_bytes(M: int, K: int, N: int, variant: int = VARIANT_AUTO) -> int:
+    return int(lib().swiglu_mlp_workspace_bytes(M, K, N, int(variant)))
+
+
+def _resolve_workspace(workspace, need: int, device: torch.device, s: int):
+    """(pointer-able tensor or None, its bytes) for a call needing `need`
+    bytes: a caller tensor as given, a Workspace grown to `need`, or the
+    cached per-stream Workspace."""
+    if need == 0 and not isinstance(workspace, torch.Tensor):
+        ws = None
+    elif isinstance(workspace, Workspace):
+        ws = workspace.get(need)
+    elif workspace is None:
+        ws = _workspace_for(device, s).get(need)
+    else:
+        ws = workspace
+    if ws is not None and ws.device.type != "cuda":
+        raise ValueError("workspace must be a GPU tensor")
+    return ws, (0 if ws is None else ws.numel() * ws.element_size())
 
 
 def swiglu_choose_variant(M: int, K: int, N: int) -> int:
@@ -382,18 +422,7 @@ def swiglu_fused_packed(A: torch.Tensor, Wp: torch.Tensor, N: int, Y: torch.Tens
     s = _stream(stream)
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
-    need = _workspace_need(M, K, N, int(variant), A.device)
-    if need == 0 and not isinstance(workspace, torch.Tensor):
-        ws = None
-    elif isinstance(workspace, Workspace):
-        ws = workspace.get(need)
-    elif workspace is None:
-        ws = _workspace_for(A.device, s).get(need)
-    else:
-        ws = workspace
-    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    if ws is not None and ws.device.type != "cuda":
-        raise ValueError("workspace must be a GPU tensor")
+    ws, ws_bytes = _resolve_workspace(workspace, _workspace_need(M, K, N, int(variant), A.device), A.device, s)
     st = lib().swiglu_fused_packed(_dev_bf16(A, "A"), _dev_bf16(Wp, "Wp"), _dev_bf16(Y, "Y"), M, K, N,
                                    _ptr(ws), ws_bytes, int(variant), s)
     _check("swiglu_fused_packed", st)
@@ -457,14 +486,18 @@ def swiglu_gemm_pack_weight(W: torch.Tensor, Wg: torch.Tensor | None = None, str
 
 
 def swiglu_gemm_packed(A: torch.Tensor, Wg: torch.Tensor, N: int, C: torch.Tensor | None = None,
-                       stream=None) -> torch.Tensor:
-    """C = bf16(A @ W) with fp32 accumulation from a single-weight pack."""
+                       workspace: torch.Tensor | Workspace | None = None, stream=None) -> torch.Tensor:
+    """C = bf16(A @ W) with fp32 accumulation from a single-weight pack.
+    ``workspace`` as in swiglu_fused_packed (None: the cached per-stream one,
+    so split-K runs where the plan asks for it)."""
     M, K = A.shape
     _gemm_packed_at_least(Wg, K, N)
     _shape(C, (M, N), "C")
     C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device) if C is None else C
+    s = _stream(stream)
+    ws, ws_bytes = _resolve_workspace(workspace, _cached_need("gemm", (M, K, N), A.device), A.device, s)
     st = lib().swiglu_gemm_packed(_dev_bf16(A, "A"), _dev_bf16(Wg, "Wg"), _dev_bf16(C, "C"), M, K, N,
-                                  _stream(stream))
+                                  _ptr(ws), ws_bytes, s)
     _check("swiglu_gemm_packed", st)
     return C
 
@@ -541,14 +574,8 @@ def swiglu_mlp_packed(A: torch.Tensor, Wp: torch.Tensor, W3g: torch.Tensor, N: i
     s = _stream(stream)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=A.device) if Y is None else Y
     Z = torch.empty((M, K), dtype=torch.bfloat16, device=A.device) if Z is None else Z
-    need = swiglu_workspace_bytes(M, K, N, variant)
-    if isinstance(workspace, Workspace):
-        ws = workspace.get(need)
-    elif workspace is None:
-        ws = _workspace_for(A.device, s).get(need)
-    else:
-        ws = workspace
-    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    ws, ws_bytes = _resolve_workspace(workspace, _cached_need("mlp", (M, K, N, int(variant)), A.device),
+                                      A.device, s)
     st = lib().swiglu_mlp_packed(_dev_bf16(A, "A"), _dev_bf16(Wp, "Wp"), _dev_bf16(W3g, "W3g"),
                                  _dev_bf16(Y, "Y"), _dev_bf16(Z, "Z"), M, K, N, _ptr(ws), ws_bytes,
                                  int(variant), s)
@@ -557,24 +584,28 @@ def swiglu_mlp_packed(A: torch.Tensor, Wp: torch.Tensor, W3g: torch.Tensor, N: i
 
 
 def swiglu_mlp_down(Y: torch.Tensor, W3g: torch.Tensor, K: int, Z: torch.Tensor | None = None,
-                    stream=None) -> torch.Tensor:
+                    workspace: torch.Tensor | Workspace | None = None, stream=None) -> torch.Tensor:
     """The MLP block's down projection alone: Z[M,K] = Y[M,N] @ W3[N,K], W3 in
-    the single-weight pack."""
+    the single-weight pack; ``workspace`` as in swiglu_gemm_packed."""
     M, N = Y.shape
     _gemm_packed_at_least(W3g, N, K, "W3g")
     _shape(Z, (M, K), "Z")
     Z = torch.empty((M, K), dtype=torch.bfloat16, device=Y.device) if Z is None else Z
+    s = _stream(stream)
+    ws, ws_bytes = _resolve_workspace(workspace, _cached_need("gemm", (M, N, K), Y.device), Y.device, s)
     st = lib().swiglu_mlp_down(_dev_bf16(Y, "Y"), _dev_bf16(W3g, "W3g"), _dev_bf16(Z, "Z"), M, K, N,
-                               _stream(stream))
+                               _ptr(ws), ws_bytes, s)
     _check("swiglu_mlp_down", st)
     return Z
 
 
 def swiglu_mlp_unfused(A: torch.Tensor, W1g: torch.Tensor, W2g: torch.Tensor, W3g: torch.Tensor, N: int,
                        G: torch.Tensor | None = None, U: torch.Tensor | None = None,
-                       Y: torch.Tensor | None = None, Z: torch.Tensor | None = None, stream=None):
+                       Y: torch.Tensor | None = None, Z: torch.Tensor | None = None,
+                       workspace: torch.Tensor | Workspace | None = None, stream=None):
     """The gated MLP block, unfused, on single-weight packs: G, U through
-    memory, Y = SiLU(G)*U, then Z = Y @ W3.  Returns (Y, Z)."""
+    memory, Y = SiLU(G)*U, then Z = Y @ W3 (``workspace`` as in
+    swiglu_gemm_packed, for the down projection).  Returns (Y, Z)."""
     M, K = A.shape
     _gemm_packed_at_least(W1g, K, N, "W1g")
     _gemm_packed_at_least(W2g, K, N, "W2g")
@@ -586,9 +617,11 @@ def swiglu_mlp_unfused(A: torch.Tensor, W1g: torch.Tensor, W2g: torch.Tensor, W3
     U = mk(M, N) if U is None else U
     Y = mk(M, N) if Y is None else Y
     Z = mk(M, K) if Z is None else Z
+    s = _stream(stream)
+    ws, ws_bytes = _resolve_workspace(workspace, _cached_need("gemm", (M, N, K), A.device), A.device, s)
     st = lib().swiglu_mlp_unfused(_dev_bf16(A, "A"), _dev_bf16(W1g, "W1g"), _dev_bf16(W2g, "W2g"),
                                   _dev_bf16(W3g, "W3g"), _dev_bf16(G, "G"), _dev_bf16(U, "U"),
-                                  _dev_bf16(Y, "Y"), _dev_bf16(Z, "Z"), M, K, N, _stream(stream))
+                                  _dev_bf16(Y, "Y"), _dev_bf16(Z, "Z"), M, K, N, _ptr(ws), ws_bytes, s)
     _check("swiglu_mlp_unfused", st)
     return Y, Z
 

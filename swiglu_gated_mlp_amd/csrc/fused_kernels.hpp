@@ -212,6 +212,42 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
 }
 
+// The single-weight GEMM's split-K reduction: partials [split][M][2*NT] over
+// the NT tiled columns of the pack (the "Gate" sum of tiled column n is output
+// column (n / 128) * 256 + n % 128, the "Up" sum that column + 128), added in
+// split order 0..S-1 and stored as bf16; output columns >= N are skipped.
+__global__ __launch_bounds__(256) void splitk_gemm_reduce_kernel(const float* __restrict__ part,
+                                                                 uint16_t* __restrict__ C, int M, int N, int NT,
+                                                                 int S) {
+    const long long groups = (long long)M * (NT / 4);
+    const size_t split_stride = (size_t)M * 2 * (size_t)NT;
+    for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < groups;
+         t += (long long)gridDim.x * blockDim.x) {
+        const int m = (int)(t / (NT / 4));
+        const int n = (int)(t % (NT / 4)) * 4;
+        const float* src = part + (size_t)m * 2 * (size_t)NT + n;
+        f32x4 g = *reinterpret_cast<const f32x4*>(src);
+        f32x4 u = *reinterpret_cast<const f32x4*>(src + NT);
+        for (int s2 = 1; s2 < S; ++s2) {
+            g += *reinterpret_cast<const f32x4*>(src + s2 * split_stride);
+            u += *reinterpret_cast<const f32x4*>(src + s2 * split_stride + NT);
+        }
+        const int col = (n / PACK_BN) * PACK_ROWS + n % PACK_BN;
+        if (col < N) {
+            u32x2 out;
+            out[0] = pack2(g[0], g[1]);
+            out[1] = pack2(g[2], g[3]);
+            *reinterpret_cast<u32x2*>(C + (size_t)m * N + col) = out;
+        }
+        if (col + PACK_BN < N) {
+            u32x2 out;
+            out[0] = pack2(u[0], u[1]);
+            out[1] = pack2(u[2], u[3]);
+            *reinterpret_cast<u32x2*>(C + (size_t)m * N + col + PACK_BN) = out;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // The fused (DUAL) / single-GEMM (!DUAL) tile kernel.
 //   BM x BN output tile per workgroup, WM x WN waves, each wave owning a
@@ -906,12 +942,13 @@ constexpr int stream_smem_elems() {
 // jt holds W's columns jt*256 + 0..255): the "Gate" accumulators are output
 // columns jt*256 + c, the "Up" ones jt*256 + 128 + c; p.N is C's width.  The
 // Y tile in LDS holds 128 columns, so the epilogue runs in two passes (Gate
-// half, then Up half), each staged, synchronised and stored.
+// half, then Up half), each staged, synchronised and stored.  With SPLIT the
+// partial sums go out over the pack's p.tiles_n * 128 tiled columns instead.
 template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false, bool IL = false, bool F8 = false,
           bool SEQ = false, bool GEMM = false>
 __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_t* smem, int first, int stride,
                                                      int total) {
-    static_assert(!(GEMM && (SPLIT || IL || F8 || SEQ)), "plain GEMM: bf16 single-weight pack, data-parallel");
+    static_assert(!(GEMM && (IL || F8 || SEQ)), "plain GEMM: bf16 single-weight pack");
     static_assert(!(IL && SPLIT), "the interleaved layout has no split-K schedule");
     static_assert(!(F8 && (IL || SPLIT)), "FP8 operands: per-tile layout, data-parallel only");
     static_assert(!(SEQ && (SPLIT || PANELS || IL || F8)), "sequential order: bf16 per-tile tiles only");
@@ -1288,7 +1325,10 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
         __builtin_amdgcn_s_barrier();
 
         if constexpr (SPLIT) {
-            store_partials<TM, 1>(acc, p.part, cur.split, M, N, cur.m0, cur.n0 + wave * 32, lane);
+            // GEMM: the partials cover the pack's tiled columns (both halves
+            // of each packed tile), reduced by splitk_gemm_reduce_kernel
+            store_partials<TM, 1>(acc, p.part, cur.split, M, GEMM ? p.tiles_n * PACK_BN : N, cur.m0,
+                                  cur.n0 + wave * 32, lane);
             break;   // one item per workgroup
         }
 

@@ -851,8 +851,37 @@ swiglu_status swiglu_gemm_pack_weight(const swiglu_bf16* W, swiglu_bf16* Wg, int
     return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
 }
 
+// The single-weight GEMM's plan: the fused product's AUTO rule on the pack's
+// tiled width (128 columns per packed tile), whose split-K needs fp32
+// partials over those tiled columns.  One addition: a compute-bound product
+// (from 1024 rows on) whose data-parallel tiles leave over half the CUs idle
+// -- a narrow output, like the MLP's down projection back to a small model
+// width -- splits K as well: there the idle matrix cores cost more than the
+// partial sums' traffic (measured: 0.5B-width down projection, M=4096
+// K=4864 N=896, 86.6 us data-parallel on 64 tiles).
+Plan gemm_plan(int64_t M, int64_t K, int64_t N) {
+    const int cus = cu_count_now();
+    const int64_t nt = gemm_tiled_cols(N);
+    Plan p = make_plan(M, K, nt, SWIGLU_VARIANT_AUTO, cus);
+    if (p.variant == SWIGLU_VARIANT_DATA_PARALLEL && M >= 1024 && 2 * (int64_t)p.tiles < p.cus) {
+        const Plan q = make_plan(M, K, nt, SWIGLU_VARIANT_SPLIT_K, cus);
+        if (q.splits > 1) p = q;
+    }
+    return p;
+}
+
+size_t gemm_split_bytes(const Plan& p, int64_t M, int64_t N) {
+    return split_workspace_bytes(p, M, gemm_tiled_cols(N));
+}
+
+size_t swiglu_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    if (check_shape(M, K, N) != SWIGLU_OK || M == 0) return 0;
+    if (M > stream_rows_limit(K, 2)) return 0;   // row chunks run data-parallel
+    return gemm_split_bytes(gemm_plan(M, K, N), M, N);
+}
+
 swiglu_status swiglu_gemm_packed(const swiglu_bf16* A, const swiglu_bf16* Wg, swiglu_bf16* C, int64_t M, int64_t K,
-                                 int64_t N, void* stream) {
+                                 int64_t N, void* workspace, size_t workspace_bytes, void* stream) {
     swiglu_status st = check_shape(M, K, N);
     if (st != SWIGLU_OK) return st;
     if (M == 0) return SWIGLU_OK;
@@ -864,17 +893,27 @@ swiglu_status swiglu_gemm_packed(const swiglu_bf16* A, const swiglu_bf16* Wg, sw
     if (M > stream_rows_limit(K, 2)) {
         const int64_t rows = balanced_chunk(M, stream_rows_limit(K, 2));
         for (int64_t m0 = 0; m0 < M; m0 += rows) {
-            st = swiglu_gemm_packed(A + m0 * K, Wg, C + m0 * N, std::min(rows, M - m0), K, N, stream);
+            st = swiglu_gemm_packed(A + m0 * K, Wg, C + m0 * N, std::min(rows, M - m0), K, N, nullptr, 0, stream);
             if (st != SWIGLU_OK) return st;
         }
         return SWIGLU_OK;
     }
-    // the fused product's schedules on the packed tiles' width, without
-    // split-K (no workspace): decode for small M, else the streaming grid
-    const int cus = cu_count_now();
+    // the fused product's schedules on the packed tiles' width: decode for
+    // small M, else the streaming grid, split over K when AUTO asks for it
+    // and the workspace holds the partial sums
     const int64_t nt = gemm_tiled_cols(N);
-    Plan p = make_plan(M, K, nt, SWIGLU_VARIANT_AUTO, cus);
-    if (p.variant == SWIGLU_VARIANT_SPLIT_K) p = make_plan(M, K, nt, SWIGLU_VARIANT_DATA_PARALLEL, cus);
+    Plan p = gemm_plan(M, K, N);
+    const size_t need = gemm_split_bytes(p, M, N);
+    bool split = p.variant == SWIGLU_VARIANT_SPLIT_K && need > 0 && workspace && workspace_bytes >= need;
+    if (split) {
+        if (!aligned16(workspace)) return SWIGLU_ERR_MISALIGNED;
+        const Range w = range_of(workspace, (int64_t)need);
+        if (overlap(w, c) || overlap(w, range_of(A, M * K * 2)) ||
+            overlap(w, range_of(Wg, gemm_packed_elems(K, N) * 2)))
+            return SWIGLU_ERR_ALIASING;
+    } else if (p.variant == SWIGLU_VARIANT_SPLIT_K) {
+        p = make_plan(M, K, nt, SWIGLU_VARIANT_DATA_PARALLEL, p.cus);
+    }
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (p.variant == SWIGLU_VARIANT_DECODE) {
@@ -887,8 +926,26 @@ swiglu_status swiglu_gemm_packed(const swiglu_bf16* A, const swiglu_bf16* Wg, sw
         a.A = A; a.W1 = Wg; a.W2 = nullptr; a.Y = C;
         a.M = (int)M; a.K = (int)K; a.N = (int)N;
         a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n;
-        a.splits = 1; a.kb_per_split = p.KB; a.KB = p.KB;
-        e = launch_stream_dp<false, false, false, true>(a, p, s);
+        a.splits = p.splits; a.kb_per_split = p.kb_per_split; a.KB = p.KB;
+        if (split) {
+            a.part = reinterpret_cast<float*>(workspace);
+            const int grid = p.tiles * p.splits;
+            e = p.t.BM == 128 ? launch_stream<128, true, false, false, false, false, true>(a, grid, grid, s)
+                              : launch_stream<256, true, false, false, false, false, true>(a, grid, grid, s);
+            if (e == hipSuccess) {
+                const long long groups = (long long)M * (nt / 4);
+                const int rgrid = (int)std::max<long long>(
+                    1, std::min<long long>(ceil_div(groups, 256), (long long)p.cus * 8));
+                int Mi = (int)M, Ni = (int)N, NTi = (int)nt, Si = p.splits;
+                const float* part = a.part;
+                uint16_t* cp = C;
+                void* args[] = {(void*)&part, (void*)&cp, &Mi, &Ni, &NTi, &Si};
+                e = hipLaunchKernel(reinterpret_cast<const void*>(&swk::splitk_gemm_reduce_kernel), dim3(rgrid),
+                                    dim3(256), args, 0, s);
+            }
+        } else {
+            e = launch_stream_dp<false, false, false, true>(a, p, s);
+        }
     }
     return e == hipSuccess ? SWIGLU_OK : hip_fail(e);
 }
@@ -908,9 +965,9 @@ swiglu_status swiglu_unfused_packed(const swiglu_bf16* A, const swiglu_bf16* W1g
     for (const Range& r : ins)
         if (overlap(g, r) || overlap(u, r) || overlap(y, r)) return SWIGLU_ERR_ALIASING;
     if (overlap(g, u) || overlap(g, y) || overlap(u, y)) return SWIGLU_ERR_ALIASING;
-    st = swiglu_gemm_packed(A, W1g, G_scratch, M, K, N, stream);
+    st = swiglu_gemm_packed(A, W1g, G_scratch, M, K, N, nullptr, 0, stream);
     if (st != SWIGLU_OK) return st;
-    st = swiglu_gemm_packed(A, W2g, U_scratch, M, K, N, stream);
+    st = swiglu_gemm_packed(A, W2g, U_scratch, M, K, N, nullptr, 0, stream);
     if (st != SWIGLU_OK) return st;
     return swiglu_silu_mul(G_scratch, U_scratch, Y, M * N, stream);
 }
@@ -959,8 +1016,13 @@ swiglu_status swiglu_unfused(const swiglu_bf16* A, const swiglu_bf16* W1, const 
 // GEMM on this library's own kernels, Y as the activations (N deep) and W3 in
 // the single-weight pack (swiglu_gemm_pack_weight of the [N,K] W3).
 // ---------------------------------------------------------------------------
+size_t swiglu_mlp_workspace_bytes(int64_t M, int64_t K, int64_t N, int variant) {
+    if (check_shape(M, K, N) != SWIGLU_OK || M == 0 || !variant_known(variant)) return 0;
+    return std::max(swiglu_workspace_bytes(M, K, N, variant), swiglu_gemm_workspace_bytes(M, N, K));
+}
+
 swiglu_status swiglu_mlp_down(const swiglu_bf16* Y, const swiglu_bf16* W3g, swiglu_bf16* Z, int64_t M, int64_t K,
-                              int64_t N, void* stream) {
+                              int64_t N, void* workspace, size_t workspace_bytes, void* stream) {
     swiglu_status st = check_shape(M, K, N);
     if (st != SWIGLU_OK) return st;
     if (M == 0) return SWIGLU_OK;
@@ -969,7 +1031,7 @@ swiglu_status swiglu_mlp_down(const swiglu_bf16* Y, const swiglu_bf16* W3g, swig
     const Range z = range_of(Z, M * K * 2);
     if (overlap(z, range_of(Y, M * N * 2)) || overlap(z, range_of(W3g, gemm_packed_elems(N, K) * 2)))
         return SWIGLU_ERR_ALIASING;
-    return swiglu_gemm_packed(Y, W3g, Z, M, N, K, stream);
+    return swiglu_gemm_packed(Y, W3g, Z, M, N, K, workspace, workspace_bytes, stream);
 }
 
 swiglu_status swiglu_mlp_packed(const swiglu_bf16* A, const swiglu_bf16* Wp, const swiglu_bf16* W3g,
@@ -990,13 +1052,15 @@ swiglu_status swiglu_mlp_packed(const swiglu_bf16* A, const swiglu_bf16* Wp, con
         return SWIGLU_ERR_ALIASING;
     st = swiglu_fused_packed(A, Wp, Y, M, K, N, workspace, workspace_bytes, variant, stream);
     if (st != SWIGLU_OK) return st;
-    return swiglu_gemm_packed(Y, W3g, Z, M, N, K, stream);
+    // the same workspace then holds the down projection's partial sums (the
+    // fused product's are consumed by then: both run in order on `stream`)
+    return swiglu_gemm_packed(Y, W3g, Z, M, N, K, workspace, workspace_bytes, stream);
 }
 
 swiglu_status swiglu_mlp_unfused(const swiglu_bf16* A, const swiglu_bf16* W1g, const swiglu_bf16* W2g,
                                  const swiglu_bf16* W3g, swiglu_bf16* G_scratch, swiglu_bf16* U_scratch,
                                  swiglu_bf16* Y, swiglu_bf16* Z, int64_t M, int64_t K, int64_t N,
-                                 void* stream) {
+                                 void* workspace, size_t workspace_bytes, void* stream) {
     swiglu_status st = check_shape(M, K, N);
     if (st != SWIGLU_OK) return st;
     if (M == 0) return SWIGLU_OK;
@@ -1011,9 +1075,11 @@ swiglu_status swiglu_mlp_unfused(const swiglu_bf16* A, const swiglu_bf16* W1g, c
         if (overlap(z, r)) return SWIGLU_ERR_ALIASING;
     for (int i = 4; i < 7; ++i)
         if (overlap(others[i], w3)) return SWIGLU_ERR_ALIASING;
+    if (workspace && workspace_bytes > 0 && overlap(z, range_of(workspace, (int64_t)workspace_bytes)))
+        return SWIGLU_ERR_ALIASING;
     st = swiglu_unfused_packed(A, W1g, W2g, G_scratch, U_scratch, Y, M, K, N, stream);
     if (st != SWIGLU_OK) return st;
-    return swiglu_gemm_packed(Y, W3g, Z, M, N, K, stream);
+    return swiglu_gemm_packed(Y, W3g, Z, M, N, K, workspace, workspace_bytes, stream);
 }
 
 swiglu_status swiglu_probe_mfma(float* sink, int blocks, int iters, void* stream) {

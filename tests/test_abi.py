@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert sw.swiglu_abi_version() == 2
+    assert sw.swiglu_abi_version() == 3
     for s in range(9):
         assert sw.status_str(s) and sw.status_str(s) != "unknown status"
     assert sw.status_str(99) == "unknown status"
@@ -135,20 +135,21 @@ def test_mlp_errors():
     assert P(A_, WP_, W3_, Y_, Y_ + 64, 4, 64, 64, None, 0, 0, None) == ALIAS
     assert P(A_, WP_, W3_, W3_ + 4096, Z_, 4, 64, 64, None, 0, 0, None) == ALIAS
     D = L.swiglu_mlp_down
-    assert D(Y_, W3_, Z_, 4, 64, 60, None) == UNSUP
-    assert D(None, None, None, 0, 64, 64, None) == OK
-    assert D(Y_, None, Z_, 4, 64, 64, None) == NULLP
-    assert D(Y_ + 2, W3_, Z_, 4, 64, 64, None) == MISAL
-    assert D(Y_, W3_, Y_ + 128, 4, 64, 64, None) == ALIAS
-    assert D(Y_, W3_, W3_ + 16, 4, 64, 64, None) == ALIAS
+    assert D(Y_, W3_, Z_, 4, 64, 60, None, 0, None) == UNSUP
+    assert D(None, None, None, 0, 64, 64, None, 0, None) == OK
+    assert D(Y_, None, Z_, 4, 64, 64, None, 0, None) == NULLP
+    assert D(Y_ + 2, W3_, Z_, 4, 64, 64, None, 0, None) == MISAL
+    assert D(Y_, W3_, Y_ + 128, 4, 64, 64, None, 0, None) == ALIAS
+    assert D(Y_, W3_, W3_ + 16, 4, 64, 64, None, 0, None) == ALIAS
     U = L.swiglu_mlp_unfused
     G_, U_ = 0x90000000, 0xA0000000
-    assert U(A_, W1_, W2_, W3_, G_, U_, Y_, Z_, 4, 64, 60, None) == UNSUP
-    assert U(None, None, None, None, None, None, None, None, 0, 64, 64, None) == OK
-    assert U(A_, W1_, W2_, W3_, G_, U_, Y_, None, 4, 64, 64, None) == NULLP
-    assert U(A_, W1_, W2_, W3_, G_, U_, Y_, Z_ + 4, 4, 64, 64, None) == MISAL
-    assert U(A_, W1_, W2_, W3_, G_, U_, Y_, G_ + 32, 4, 64, 64, None) == ALIAS
-    assert U(A_, W1_, W2_, W3_, G_, W3_ + 128, Y_, Z_, 4, 64, 64, None) == ALIAS
+    assert U(A_, W1_, W2_, W3_, G_, U_, Y_, Z_, 4, 64, 60, None, 0, None) == UNSUP
+    assert U(None, None, None, None, None, None, None, None, 0, 64, 64, None, 0, None) == OK
+    assert U(A_, W1_, W2_, W3_, G_, U_, Y_, None, 4, 64, 64, None, 0, None) == NULLP
+    assert U(A_, W1_, W2_, W3_, G_, U_, Y_, Z_ + 4, 4, 64, 64, None, 0, None) == MISAL
+    assert U(A_, W1_, W2_, W3_, G_, U_, Y_, G_ + 32, 4, 64, 64, None, 0, None) == ALIAS
+    assert U(A_, W1_, W2_, W3_, G_, W3_ + 128, Y_, Z_, 4, 64, 64, None, 0, None) == ALIAS
+    assert U(A_, W1_, W2_, W3_, G_, U_, Y_, Z_, 4, 64, 64, Z_ + 64, 256, None) == ALIAS
 
 
 def test_gemm_packed_sizes_and_errors():
@@ -160,12 +161,29 @@ def test_gemm_packed_sizes_and_errors():
     assert L.swiglu_gemm_packed_bytes(72, 136) == 1 * 2 * 32768
     assert L.swiglu_gemm_packed_bytes(12, 8) == 0 and L.swiglu_gemm_packed_bytes(8, 0) == 0
     G = L.swiglu_gemm_packed
-    assert G(None, None, None, 0, 64, 64, None) == OK
-    assert G(A_, WP_, Y_, 4, 60, 64, None) == UNSUP
-    assert G(A_, None, Y_, 4, 64, 64, None) == NULLP
-    assert G(A_, WP_, Y_ + 2, 4, 64, 64, None) == MISAL
-    assert G(A_, WP_, WP_ + 1024, 4, 64, 64, None) == ALIAS
-    assert G(A_, WP_, A_ + 16, 4, 64, 64, None) == ALIAS
+    assert G(None, None, None, 0, 64, 64, None, 0, None) == OK
+    assert G(A_, WP_, Y_, 4, 60, 64, None, 0, None) == UNSUP
+    assert G(A_, None, Y_, 4, 64, 64, None, 0, None) == NULLP
+    assert G(A_, WP_, Y_ + 2, 4, 64, 64, None, 0, None) == MISAL
+    assert G(A_, WP_, WP_ + 1024, 4, 64, 64, None, 0, None) == ALIAS
+    assert G(A_, WP_, A_ + 16, 4, 64, 64, None, 0, None) == ALIAS
+    # split-K partials: AUTO's split plan on the pack's tiled width (128
+    # columns per 256-column packed tile), none for decode or full grids
+    assert L.swiglu_gemm_workspace_bytes(1, 3584, 18944) == 0
+    assert L.swiglu_gemm_workspace_bytes(4096, 8192, 29568) == 0
+    need = L.swiglu_gemm_workspace_bytes(128, 18944, 3584)
+    nt = 14 * 128
+    assert need > 0 and need % (128 * 2 * nt * 4) == 0 and need // (128 * 2 * nt * 4) >= 2
+    assert L.swiglu_gemm_workspace_bytes(128, 18940, 3584) == 0     # K not a multiple of 8
+    # a workspace that holds the partials is checked like the fused product's
+    assert G(A_, WP_, Y_, 128, 18944, 3584, WS_ + 8, need, None) == MISAL
+    assert G(A_, WP_, Y_, 128, 18944, 3584, Y_ + 4096, need, None) == ALIAS
+    assert G(A_, WP_, Y_, 128, 18944, 3584, WP_ + 4096, need, None) == ALIAS
+    # the MLP's workspace covers both steps
+    M_, K_, N_ = 128, 3584, 18944
+    assert L.swiglu_mlp_workspace_bytes(M_, K_, N_, 0) == max(L.swiglu_workspace_bytes(M_, K_, N_, 0),
+                                                               L.swiglu_gemm_workspace_bytes(M_, N_, K_)) > 0
+    assert L.swiglu_mlp_workspace_bytes(M_, K_, N_, 9) == 0
     P = L.swiglu_gemm_pack_weight
     assert P(W1_, W1_ + 16, 64, 64, None) == ALIAS
     assert P(W1_, WP_, 64, 63, None) == UNSUP

@@ -346,6 +346,7 @@ def test_panel_schedule(dev, M, K, N):
     (96, 256, 520),       # panel schedule, partial last packed tile
     (16, 3584, 18944),    # 7B decode width: decode schedule, long down-projection reduction
     (256, 896, 4864),     # 0.5B shape, a slice of the prefill rows
+    (128, 1024, 6144),    # down projection split over K (4 column tiles for 256 CUs)
 ])
 def test_mlp_block(dev, M, K, N):
     """The gated MLP block, fused and unfused: the fused Y against the
@@ -362,6 +363,8 @@ def test_mlp_block(dev, M, K, N):
     say("[mlp] M=%d K=%d N=%d" % (M, K, N))
     W3g = sw.swiglu_gemm_pack_weight(W3d)
     W1g, W2g = sw.swiglu_gemm_pack_weight(W1d), sw.swiglu_gemm_pack_weight(W2d)
+    if (M, K, N) == (128, 1024, 6144):
+        assert sw.swiglu_gemm_workspace_bytes(M, N, K) > 0, "down projection expected to take split-K"
     Yf, Zf = sw.swiglu_mlp_packed(Ad, Wp, W3g, N)
     G = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     U = torch.empty_like(G)
@@ -509,6 +512,33 @@ def test_gemm_packed_against_oracle(dev, M, K, N):
     C = sw.swiglu_gemm_packed(A.to(dev), Wg, N)
     torch.cuda.synchronize()
     check_gemm_ulp(gpu_bits(C), oracle.gemm_bf16(A, W), "gemm_packed %s" % ((M, K, N),))
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (128, 4864, 896),     # 0.5B down-projection width: 4 column tiles, 2 splits
+    (100, 6200, 1000),    # ragged M, K and N (half-empty last packed tile), 3 splits
+    (1100, 1000, 520),    # compute-bound, 27 data-parallel tiles: split anyway, 8 splits
+])
+def test_gemm_split_k(dev, M, K, N):
+    """The GEMM's split-K schedule (taken only with a workspace that holds
+    the partial sums): every element within one bf16 flip of the oracle, the
+    same as the data-parallel schedule up to that flip, and bitwise
+    repeatable with a workspace full of NaN or of the previous call's
+    partials."""
+    need = sw.swiglu_gemm_workspace_bytes(M, K, N)
+    assert need > 0, "shape expected to take split-K"
+    A, W, _ = inputs.gaussian_case(M, K, N, seed=5 * M + K + 3 * N)
+    say("[gemm_split] M=%d K=%d N=%d need=%d" % (M, K, N, need))
+    Ad, Wg = A.to(dev), sw.swiglu_gemm_pack_weight(W.to(dev))
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev)
+    C1 = sw.swiglu_gemm_packed(Ad, Wg, N, workspace=ws)
+    C2 = sw.swiglu_gemm_packed(Ad, Wg, N, workspace=ws)
+    C0 = sw.swiglu_gemm_packed(Ad, Wg, N, workspace=torch.empty(16, dtype=torch.uint8, device=dev))
+    torch.cuda.synchronize()
+    ref = oracle.gemm_bf16(A, W)
+    check_gemm_ulp(gpu_bits(C1), ref, "gemm split-K %s" % ((M, K, N),))
+    check_gemm_ulp(gpu_bits(C0), ref, "gemm data-parallel %s" % ((M, K, N),))
+    assert np.array_equal(gpu_bits(C1), gpu_bits(C2)), "split-K GEMM not repeatable"
 
 
 def test_gemm_pack_layout(dev):
