@@ -944,6 +944,10 @@ constexpr int stream_smem_elems() {
 // Y tile in LDS holds 128 columns, so the epilogue runs in two passes (Gate
 // half, then Up half), each staged, synchronised and stored.  With SPLIT the
 // partial sums go out over the pack's p.tiles_n * 128 tiled columns instead.
+// With PANELS each wave takes half a panel -- 32 tiled columns of one weight
+// half, one accumulator set -- so the units are twice the fused product's
+// panels and the CUs share them as evenly (p.panels counts half-panels; the
+// single Y-tile pass maps each wave's 32 columns to its half).
 template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false, bool IL = false, bool F8 = false,
           bool SEQ = false, bool GEMM = false>
 __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_t* smem, int first, int stride,
@@ -960,7 +964,10 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
     constexpr int A_INS = BM / 8 / NW;          // 1 KiB direct loads per wave per stage
     constexpr int ASTAGE = BM * BK;             // elements per activation stage
     constexpr int NBUF = 3;                     // ring slots == weight register sets
-    constexpr int WT = SEQ ? 1 : 2;             // weight halves per stage (Gate and Up, or one)
+    // GEMM on the panel schedule: a wave's unit is half a panel (32 columns of
+    // one weight half), twice the units of the fused product's panels
+    constexpr bool GH = GEMM && PANELS;
+    constexpr int WT = (SEQ || GH) ? 1 : 2;     // weight halves per stage (Gate and Up, or one)
     constexpr int LOADS = A_INS + 4 * WT;       // vector-memory instructions per wave per stage
     constexpr int NST = BM / 16;                // Y stores per wave per tile
     constexpr int GROUP_M = 8;
@@ -1055,7 +1062,8 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
             a_off[i] = (uint32_t)((size_t)min(it.m0 + r, M - 1) * K * EB + 16 * c);
         }
         chunk_x = ((ll & 7) ^ (ll >> 3)) & 7;
-        const int wq = it.n0 / 32 + wave;
+        const int wu = it.n0 / 32 + wave;       // the wave's panel (GH: half-panel)
+        const int wq = GH ? (wu >> 1) : wu;
         if constexpr (F8)
             // FP8 block: [32-row block rb][64-k step][lane][32 bytes]; Gate
             // block wq & 3, Up block 4 + (wq & 3)
@@ -1064,7 +1072,8 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
             w_off = (uint32_t)((((wq & 3) * (IL ? 4 : 2) + ((ll >> 4) & 1)) * 1024 + (ll >> 5) * 128 +
                                 (ll & 15) * 8) * 2);
         w_tile = reinterpret_cast<const char*>(p.W1) + (size_t)(wq >> 2) * KB * (PACK_ROWS * PACK_BK * 2) +
-                 (SEQ && it.up ? 16384 : 0);   // SEQ: the Up half of each packed block
+                 (SEQ && it.up ? 16384 : 0) +   // SEQ: the Up half of each packed block
+                 (GH ? (wu & 1) * 16384 : 0);   // GH: the wave's half
         ld_kb_first = it.kb_first;
         ld_ns = valid ? it.ns : 0;
         ld_ns_w = (!PANELS || wave < it.np) ? ld_ns : 0;
@@ -1220,7 +1229,7 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             acc[0][i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[WS][0][kk], fa[cur][i], acc[0][i][0], 0, 0, 0);
-            if constexpr (!SEQ)
+            if constexpr (WT == 2)
                 acc[1][i][0] =
                     __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[WS][WT - 1][kk], fa[cur][i], acc[1][i][0], 0, 0, 0);
             if constexpr (RD) {
@@ -1460,9 +1469,20 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
             const int r0 = wave * (BM / 4) + (el >> 4);
             const int c = el & 15;
             const int f = cur.n0 + 8 * c;
-            const int n = GEMM ? (f >> 7) * PACK_ROWS + PACK_BN * gh + (f & (PACK_BN - 1)) : f;
-            const bool col_ok = GEMM ? (n < N && (!PANELS || f < cur.n0 + 32 * cur.np))
-                                     : (n < (PANELS ? min(N, cur.n0 + 32 * cur.np) : N));
+            int n;
+            bool col_ok;
+            if constexpr (GH) {
+                // tile columns 32w .. 32w + 31 are wave w's half-panel
+                // u = n0/32 + w: tiled columns 32(u >> 1) + 0..31 of half u & 1
+                const int u = cur.n0 / 32 + (c >> 2);
+                const int tc = (u >> 1) * 32 + 8 * (c & 3);
+                n = (tc >> 7) * PACK_ROWS + PACK_BN * (u & 1) + (tc & (PACK_BN - 1));
+                col_ok = (c >> 2) < cur.np && n < N;
+            } else {
+                n = GEMM ? (f >> 7) * PACK_ROWS + PACK_BN * gh + (f & (PACK_BN - 1)) : f;
+                col_ok = GEMM ? (n < N && (!PANELS || f < cur.n0 + 32 * cur.np))
+                              : (n < (PANELS ? min(N, cur.n0 + 32 * cur.np) : N));
+            }
             const int rows_left = M - cur.m0 - r0;   // rows r0 + 4t < M - m0
             uint16_t* yp = p.Y + (size_t)(cur.m0 + r0) * N + n;
 #pragma unroll
@@ -1474,7 +1494,7 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
             }
         };
         store_tile(0);
-        if constexpr (GEMM) {
+        if constexpr (GEMM && !GH) {
             // every wave has read the Gate half out of the Y tile (its reads
             // fed the stores above); then the Up half goes through it
             __builtin_amdgcn_sched_barrier(0);

@@ -34,21 +34,24 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(float* sink, int iters)
     sink[(size_t)blockIdx.x * blockDim.x + tid] = s;
 }
 
-__global__ __launch_bounds__(256) void probe_read_kernel(const uint4* __restrict__ src, long long n16,
+// Streaming read with non-temporal loads (each byte is read once, as the
+// decode kernels' weights are), four 16-byte loads in flight per lane.
+__global__ __launch_bounds__(256) void probe_read_kernel(const uint4* __restrict__ src4, long long n16,
                                                          uint32_t* sink) {
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const v4u* src = reinterpret_cast<const v4u*>(src4);
     const long long stride = (long long)gridDim.x * blockDim.x;
-    uint32_t x = 0;
+    v4u x = {0u, 0u, 0u, 0u};
     long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
-        x ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.y ^ v1.z ^ v1.w;
-        x ^= v2.x ^ v2.y ^ v2.z ^ v2.w ^ v3.x ^ v3.y ^ v3.z ^ v3.w;
+        const v4u v0 = __builtin_nontemporal_load(src + i);
+        const v4u v1 = __builtin_nontemporal_load(src + i + stride);
+        const v4u v2 = __builtin_nontemporal_load(src + i + 2 * stride);
+        const v4u v3 = __builtin_nontemporal_load(src + i + 3 * stride);
+        x ^= v0 ^ v1 ^ v2 ^ v3;
     }
-    for (; i < n16; i += stride) {
-        const uint4 v = src[i];
-        x ^= v.x ^ v.y ^ v.z ^ v.w;
-    }
-    sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = x;
+    for (; i < n16; i += stride) x ^= __builtin_nontemporal_load(src + i);
+    sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = x[0] ^ x[1] ^ x[2] ^ x[3];
 }
 
 }  // namespace swk

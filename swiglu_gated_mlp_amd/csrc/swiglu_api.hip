@@ -326,10 +326,14 @@ hipError_t launch_stream_dp(const swk::FusedArgs& a, const Plan& p, hipStream_t 
     if (p.t.BM == 128) {
         if constexpr (SEQ) return launch_stream<128, false, false, false, false, true>(a, grid, grid, s);
         if (p.panels > 0) {
+            // the single-weight GEMM's units are half-panels (one weight half
+            // each), as long as no workgroup gets more than its 4 waves
             swk::FusedArgs pa = a;
-            pa.panels = p.panels;
-            const int g = std::min(p.panels, p.cus);
-            return launch_stream<128, false, true, IL, F8, false, GEMM>(pa, g, g, s);
+            pa.panels = GEMM ? 2 * p.panels : p.panels;
+            if (pa.panels <= 4 * p.cus) {
+                const int g = std::min(pa.panels, p.cus);
+                return launch_stream<128, false, true, IL, F8, false, GEMM>(pa, g, g, s);
+            }
         }
         return launch_stream<128, false, false, IL, F8, false, GEMM>(a, grid, grid, s);
     }

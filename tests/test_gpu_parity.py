@@ -494,7 +494,8 @@ def check_gemm_ulp(got_bits, ref_bits, what):
     (20, 6200, 1000),               # <2,2,2> on halves (long K, narrow)
     (48, 200, 1032), (64, 72, 136),   # <4,2,1> on halves (short K, few panels)
     (40, 2104, 520),                # <4,1,1> on halves (few panels)
-    (64, 3584, 18944),                                                     # panel schedule
+    (64, 3584, 18944),                                                     # panel schedule: half-panels
+    (72, 200, 30584),                                                      # 3-4 half-panels per workgroup
     (128, 4864, 896),                                                      # down-projection shape: 3.5 tiles
     (300, 200, 520), (2100, 136, 264),                                     # 128-row tiles
     (2304, 128, 7680),                                                     # 256-row tiles + 128-row tail
