@@ -240,9 +240,9 @@ swiglu_status swiglu_fused_packed_noalloc(const swiglu_bf16 *A,
  *
  * swiglu_packed_bytes_fp8: bytes of the packed FP8 weights (0 for an invalid
  *   or unsupported shape): one 32 KiB block per 128 output columns and 128 k,
- *   [32-row block rb][64-k step][lane][32 bytes] holding packed row
+ *   [32-row block rb][64-k step][half h][lane][16 bytes] holding packed row
  *   rb*32 + (lane & 31) (rows 0-127 W1, 128-255 W2 columns of the tile) at
- *   k = 64*step + 32*(lane >> 5) + 0..31; padding is zero.
+ *   k = 64*step + 32*(lane >> 5) + 16*h + 0..15; padding is zero.
  * swiglu_pack_weights_fp8: W1_8, W2_8 [K,N] bytes -> that layout.
  * swiglu_fused_packed_fp8: Y[M,N] bf16 from A8 [M,K] and the packed weights:
  *   a weight-streaming decode kernel for M <= 32, the data-parallel streaming

@@ -1065,9 +1065,9 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
         const int wu = it.n0 / 32 + wave;       // the wave's panel (GH: half-panel)
         const int wq = GH ? (wu >> 1) : wu;
         if constexpr (F8)
-            // FP8 block: [32-row block rb][64-k step][lane][32 bytes]; Gate
-            // block wq & 3, Up block 4 + (wq & 3)
-            w_off = (uint32_t)((wq & 3) * 4096 + ll * 32);
+            // FP8 block: [32-row block rb][64-k step][half][lane][16 bytes];
+            // Gate block wq & 3, Up block 4 + (wq & 3)
+            w_off = (uint32_t)((wq & 3) * 4096 + ll * 16);
         else
             w_off = (uint32_t)((((wq & 3) * (IL ? 4 : 2) + ((ll >> 4) & 1)) * 1024 + (ll >> 5) * 128 +
                                 (ll & 15) * 8) * 2);
@@ -1171,7 +1171,7 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
             const int t = (j - A_INS) >> 2, kk = (j - A_INS) & 3;
             const char* base = valid ? w_tile + (size_t)(ld_kb_first + ls) * (PACK_ROWS * PACK_BK * 2) +
                                            t * (IL ? 4096 : 16384) +
-                                           (kk >> 1) * (F8 ? 2048 : 1024) + (kk & 1) * (F8 ? 16 : 512)
+                                           (kk >> 1) * (F8 ? 2048 : 1024) + (kk & 1) * (F8 ? 1024 : 512)
                                      : reinterpret_cast<const char*>(g_zero_chunk);
             const bf16x8* wsrc = reinterpret_cast<const bf16x8*>(base + (w_off & keep));
             // panel schedule: each weight byte is read by one wave of the
@@ -1725,9 +1725,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
 // Gate, 4 + rb for Up); its 4 waves take the 128-k blocks round-robin,
 // UNROLL blocks in flight, and each 64-k step is one
 // v_mfma_f32_32x32x64_f8f6f4 per (group, Gate|Up) with the weight fragment
-// as src0 (lane l: packed row l & 31, k 32(l >> 5) + 0..31, read whole from
-// the pack) and the activations as src1 (lane l: token l & 31, the same k,
-// two 16-byte loads).  The four per-wave fp32 sums are added in LDS in wave
+// as src0 (lane l: packed row l & 31, k 32(l >> 5) + 0..31, its two 16-byte
+// halves read with non-temporal loads from the pack's two 1 KiB runs) and the
+// activations as src1 (lane l: token l & 31, the same k, two 16-byte loads).  The four per-wave fp32 sums are added in LDS in wave
 // order 0..3, scaled (p.sg, p.su), and SiLU(Gate) * Up is stored as bf16.
 // ---------------------------------------------------------------------------
 template <int CG, int UNROLL>
@@ -1740,7 +1740,7 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(FusedArgs p) {
     const int M = p.M, K = p.K, N = p.N, KB = p.KB;
     const int n0 = blockIdx.x * (32 * CG);
     const int jt = n0 / PACK_BN, rb0 = (n0 % PACK_BN) / 32;
-    const char* wtile = reinterpret_cast<const char*>(p.W1) + (size_t)jt * KB * 32768 + lane * 32;
+    const char* wtile = reinterpret_cast<const char*>(p.W1) + (size_t)jt * KB * 32768 + lane * 16;
     const char* arow = reinterpret_cast<const char*>(p.A) + (size_t)min(lane & 31, M - 1) * K + 32 * (lane >> 5);
 
     f32x16 acc[CG][2];
@@ -1766,9 +1766,8 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(FusedArgs p) {
                         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                             for (int h = 0; h < 2; ++h)
-                                // (plain loads: non-temporal ones measured 12 % slower here)
-                                wv[u][c][g][ks][h] = *reinterpret_cast<const i32x4*>(
-                                    blk + ((4 * g + rb0 + c) * 2 + ks) * 2048 + 16 * h);
+                                wv[u][c][g][ks][h] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(
+                                    blk + ((4 * g + rb0 + c) * 2 + ks) * 2048 + 1024 * h));
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -1919,11 +1918,13 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint16_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // FP8 weight pack: per (128-column tile jt, 128-k block kb) one 32 KiB block
-// [32-row block rb][64-k step ks][lane][32 bytes], holding packed row
+// [32-row block rb][64-k step ks][half h][lane][16 bytes], holding packed row
 // rb*32 + (lane & 31) (rows 0-127: W1 column jt*128 + row, 128-255: W2 column
-// jt*128 + row - 128) at k = kb*128 + ks*64 + 32*(lane >> 5) + 0..31, the lane
-// order of a v_mfma_f32_32x32x64_f8f6f4 operand.  Padding is zero.  One
-// thread per 16-byte piece (piece index = byte offset / 16).
+// jt*128 + row - 128) at k = kb*128 + ks*64 + 32*(lane >> 5) + 16*h + 0..15:
+// the lane order of a v_mfma_f32_32x32x64_f8f6f4 operand, each half of a
+// lane's 32 bytes in its own 1 KiB run so that one wave load reads 1 KiB
+// contiguous.  Padding is zero.  One thread per 16-byte piece (piece index =
+// byte offset / 16).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void pack_fp8_kernel(const uint8_t* __restrict__ W1,
                                                        const uint8_t* __restrict__ W2,
@@ -1933,7 +1934,7 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const uint8_t* __restrict
     if (q >= npieces) return;
     const long long blk = q >> 11;
     const int within = (int)(q & 2047);
-    const int rb = within >> 8, ks = (within >> 7) & 1, lane = (within >> 1) & 63, half = within & 1;
+    const int rb = within >> 8, ks = (within >> 7) & 1, half = (within >> 6) & 1, lane = within & 63;
     const int kb = (int)(blk % KB), jt = (int)(blk / KB);
     const int prow = rb * 32 + (lane & 31);
     const bool up = prow >= PACK_BN;

@@ -36,8 +36,9 @@ def test_fp8_pack_layout(dev):
         assert P.size == ((N + 127) // 128) * KB * 32768
 
         def pos(jt, kb, prow, k):
+            # [rb][64-k step ks][half of the lane's 32 bytes][lane = 32 h + r][16 bytes]
             rb, r, ks, h, j = prow // 32, prow % 32, k // 64, (k % 64) // 32, k % 32
-            return (jt * KB + kb) * 32768 + ((rb * 2 + ks) * 64 + h * 32 + r) * 32 + j
+            return (jt * KB + kb) * 32768 + (((rb * 2 + ks) * 2 + j // 16) * 64 + h * 32 + r) * 16 + j % 16
 
         w1, w2 = W1.numpy(), W2.numpy()
         rng = np.random.default_rng(K)
