@@ -64,3 +64,40 @@ def test_graph_replay_matches_eager(dev, M, K, N, variant):
         torch.cuda.synchronize()
         assert torch.isfinite(scratch)
         assert np.array_equal(gpu_bits(Yg), gpu_bits(Ye)), "replay %d differs from eager" % rep
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (1, 3584, 1032),      # decode kernel on weight halves
+    (128, 3584, 18944),   # panel schedule on half-panels
+    (128, 4864, 896),     # split-K: partials to the workspace, then the GEMM's reduction
+])
+def test_gemm_graph_replay_matches_eager(dev, M, K, N):
+    """The single-weight GEMM (the unfused pipeline's and the MLP down
+    projection's) under capture, the same way."""
+    A, W, _ = inputs.gaussian_case(M, K, N, seed=13 * M + K + N)
+    A2, _, _ = inputs.gaussian_case(M, K, N, seed=13 * M + K + N + 100)
+    Ad, Wg = A.to(dev), sw.swiglu_gemm_pack_weight(W.to(dev))
+    ws = sw.Workspace(dev)
+    ws.get(sw.swiglu_gemm_workspace_bytes(M, K, N))
+    Cg = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    say("[graph gemm] M=%d K=%d N=%d workspace=%d" % (M, K, N, sw.swiglu_gemm_workspace_bytes(M, K, N)))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sw.swiglu_gemm_packed(Ad, Wg, N, C=Cg, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sw.swiglu_gemm_packed(Ad, Wg, N, C=Cg, workspace=ws)
+    torch.cuda.synchronize()
+    ws_eager = sw.Workspace(dev)
+    for rep, src in enumerate((A, A, A2, A2)):
+        Ad.copy_(src.to(dev))
+        Cg.fill_(0)
+        g.replay()
+        Ce = sw.swiglu_gemm_packed(Ad, Wg, N, workspace=ws_eager)
+        scratch = torch.randn(1 << 16, device=dev).sum()
+        torch.cuda.synchronize()
+        assert torch.isfinite(scratch)
+        assert np.array_equal(gpu_bits(Cg), gpu_bits(Ce)), "replay %d differs from eager" % rep
