@@ -1588,12 +1588,19 @@ struct DecodeArgs {
 // the "Up" rows, jt*256 + 128 + c), so a single-weight product has as many
 // workgroups, each streaming half the bytes, as the fused product on weights
 // of the same width -- finer work units for the CUs to balance.
-template <int MT, int CG, int UNROLL, bool GEMM = false, bool HALF = false>
+// LDSA: each wave stages its K blocks' activations (16*MT rows x 64 k) in its
+// own LDS slots with full-line direct loads (8 rows x 128 bytes per
+// instruction; the 16-byte chunks of row r XOR-ed with r & 7) and reads the
+// MFMA fragments from there, instead of loading each fragment (16 rows x 64
+// bytes, half lines) from global memory.
+template <int MT, int CG, int UNROLL, bool GEMM = false, bool HALF = false, bool LDSA = false>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
     static_assert(GEMM || !HALF, "HALF splits the single-weight product only");
     constexpr int WAVES = 4;
     constexpr int NH = HALF ? 1 : 2;    // weight halves per workgroup
+    constexpr int AROWS = 16 * MT;      // activation rows per K block
     __shared__ f32x4 red[WAVES][MT][CG][NH][64];
+    __shared__ __attribute__((aligned(16))) uint16_t sA[LDSA ? WAVES * UNROLL * AROWS * PACK_BK : 8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1614,6 +1621,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
     const uint16_t* a_row[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) a_row[t] = p.A + (size_t)min(t * 16 + r16, M - 1) * K + 8 * kq;
+    // LDSA: direct load i of a block brings rows 8i + (lane >> 3), lane l's
+    // logical chunk (l & 7) ^ (row & 7), to physical chunk l & 7
+    const uint16_t* a_dma[LDSA ? 2 * MT : 1];
+    int a_chunk[LDSA ? 2 * MT : 1];
+    if constexpr (LDSA) {
+#pragma unroll
+        for (int i = 0; i < 2 * MT; ++i) {
+            const int r = 8 * i + (lane >> 3);
+            a_chunk[i] = (lane & 7) ^ (r & 7);
+            a_dma[i] = p.A + (size_t)min(r, M - 1) * K + 8 * a_chunk[i];
+        }
+    }
+    uint16_t* const sAw = sA + (LDSA ? wave * UNROLL * AROWS * PACK_BK : 0);
 
     f32x4 accg[MT][CG], accu[MT][CG];
 #pragma unroll
@@ -1626,6 +1646,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
 
     for (int kb0 = wave; kb0 < KB; kb0 += WAVES * UNROLL) {
         u32x4 wg[UNROLL][2][CG], wu[UNROLL][2][CG], av[UNROLL][2][MT];
+        if constexpr (LDSA) {
+            // this wave's fragment reads of its slots (previous blocks) are done
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int kb = kb0 + u * WAVES;
+                if (kb < KB) {
+#pragma unroll
+                    for (int i = 0; i < 2 * MT; ++i) {
+                        const uint16_t* src = kb * PACK_BK + 8 * a_chunk[i] < K ? a_dma[i] + (size_t)kb * PACK_BK
+                                                                                : g_zero_chunk;
+                        dma16(src, sAw + (u * AROWS + 8 * i) * PACK_BK);
+                    }
+                }
+            }
+        }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int kb = kb0 + u * WAVES;
@@ -1639,13 +1676,31 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
                         if constexpr (!HALF)
                             wu[u][h][c] = ld16_stream(wtile + boff + (((grp0 + c + 8) * 2 + h) * 64 + lane) * 8);
                     }
-                    const int k = kb * PACK_BK + 32 * h + 8 * kq;
+                    if constexpr (!LDSA) {
+                        const int k = kb * PACK_BK + 32 * h + 8 * kq;
 #pragma unroll
-                    for (int t = 0; t < MT; ++t)
-                        av[u][h][t] = k < K ? ld16(a_row[t] + (size_t)kb * PACK_BK + 32 * h)
-                                            : u32x4{0u, 0u, 0u, 0u};
+                        for (int t = 0; t < MT; ++t)
+                            av[u][h][t] = k < K ? ld16(a_row[t] + (size_t)kb * PACK_BK + 32 * h)
+                                                : u32x4{0u, 0u, 0u, 0u};
+                    }
                 }
             }
+        }
+        if constexpr (LDSA) {
+            // the activations have landed in this wave's slots (the weight
+            // loads issued after them too)
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 63));
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) {
+                        const int r = t * 16 + r16;
+                        av[u][h][t] = *reinterpret_cast<const u32x4*>(
+                            sAw + (u * AROWS + r) * PACK_BK + 8 * ((4 * h + kq) ^ (r & 7)));
+                    }
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {

@@ -286,9 +286,9 @@ hipError_t launch_tile(const swk::FusedArgs& a, int grid, hipStream_t s) {
 // n_tiled: the packed weights' output columns (N for the fused product; 128
 // per packed tile for the single-weight GEMM).  HALF: one workgroup per
 // (column groups, weight half), twice the grid.
-template <int MT, int CG, int UNROLL, bool GEMM = false, bool HALF = false>
+template <int MT, int CG, int UNROLL, bool GEMM = false, bool HALF = false, bool LDSA = false>
 hipError_t launch_decode(const swk::DecodeArgs& a, int64_t n_tiled, hipStream_t s) {
-    const void* fn = reinterpret_cast<const void*>(&swk::decode_kernel<MT, CG, UNROLL, GEMM, HALF>);
+    const void* fn = reinterpret_cast<const void*>(&swk::decode_kernel<MT, CG, UNROLL, GEMM, HALF, LDSA>);
     swk::DecodeArgs args = a;
     void* kargs[] = {&args};
     return hipLaunchKernel(fn, dim3((unsigned)(ceil_div(n_tiled, 16 * CG) * (HALF ? 2 : 1))), dim3(256), kargs, 0,
@@ -393,24 +393,31 @@ hipError_t launch_decode_fp8(const swk::FusedArgs& a, int cus, hipStream_t s) {
 // workgroup per CU.  Measured (us, one call, inputs rotated past the
 // last-level cache):
 //   K=3584 N=18944 M=1 / 16: <1,1,8> 42.9 / 45.8, <1,1,4> 43.0 / 46.3, <1,2,4> 46.1 / 47.5
+//   K=8192 N=29568 M=1 / 16: <1,8,2> 138.4 / 138.0, the same with L 142.3 / 142.0
 //   K=8192 N=29568 M=32: <2,8,1> 140.2, <2,4,1> 147.3, <2,2,2> 170.4
 //   K=3584 N=18944 M=32: <2,8,1> 52.2, <2,2,2> 54.7, <2,4,1> 61.8
 //   K=896 N=4864 M=64: <4,2,1> 9.9, <4,2,2> 10.5, <4,1,1> 11.8
+// With the activations staged through LDS (L = LDSA: one full-line load
+// per 8 rows instead of a half-line per row and fragment), which pays once
+// there are more than 8 distinct rows and the group is narrow:
+//   K=3584 N=18944 M=16: <1,1,8,L> 44.1-44.4 against 45.9-46.3; M=1 / 4 / 8: no gain
+//   K=896 N=4864 M=64: <4,2,1,L> 9.33-9.38 against 9.82-9.90; M=32 with 8 groups: 55.6 against 52.0
 // n_tiled: the packed weights' output columns.
 hipError_t launch_decode_cfg(const swk::DecodeArgs& d, int64_t n_tiled, const Plan& p, hipStream_t s) {
     const bool long_k = p.KB >= 96;
     const int64_t wg64 = ceil_div(n_tiled, 64), wg128 = ceil_div(n_tiled, 128);
     switch (p.decode_mt) {
         case 1:
-            return (long_k && 4 * wg128 >= 3 * p.cus) ? launch_decode<1, 8, 2>(d, n_tiled, s)
-                                                     : launch_decode<1, 1, 8>(d, n_tiled, s);
+            if (long_k && 4 * wg128 >= 3 * p.cus) return launch_decode<1, 8, 2>(d, n_tiled, s);
+            return d.M > 8 ? launch_decode<1, 1, 8, false, false, true>(d, n_tiled, s)
+                           : launch_decode<1, 1, 8>(d, n_tiled, s);
         case 2:
             if (2 * wg128 >= p.cus) return launch_decode<2, 8, 1>(d, n_tiled, s);
             return (long_k && 4 * wg64 >= 3 * p.cus) ? launch_decode<2, 4, 1>(d, n_tiled, s)
                                                     : launch_decode<2, 2, 2>(d, n_tiled, s);
         default:
             return (long_k && 4 * wg64 >= 3 * p.cus) ? launch_decode<4, 4, 1>(d, n_tiled, s)
-                                                    : launch_decode<4, 2, 1>(d, n_tiled, s);
+                                                    : launch_decode<4, 2, 1, false, false, true>(d, n_tiled, s);
     }
 }
 
@@ -426,17 +433,23 @@ hipError_t launch_decode_cfg(const swk::DecodeArgs& d, int64_t n_tiled, const Pl
 //   K=29568 N=8192 M=32: <2,2,2,H> 92.8, <2,2,2> 129.3, <2,4,1,H> 123.9
 //   K=896 N=4864 M=64: <4,2,1,H> 8.0, <4,2,1> 9.5
 //   K=4864 N=896 M=64: <4,1,1,H> 21.8, <4,2,1,H> 24.4, <4,2,1> 31.8
-// i.e. halves whenever the whole-pair grid leaves CUs short of work, and the
-// deepest per-wave prefetch the registers allow at one or two tokens' rows.
+// and with the activations staged through LDS (L, as for the fused product):
+//   K=3584 N=18944 M=16: <1,1,8,H,L> 25.2, <1,1,8,L> 26.3, <1,1,8> 27.0
+//   K=18944 N=3584 M=16: <1,1,8,H,L> 27.4, <1,1,8,H> 30.9; K=4864 N=896 M=16: 7.9 against 9.5
+//   K=8192 N=29568 M=16: <1,4,4,H> 77.7, <1,4,4,H,L> 79.5
+//   K=896 N=4864 M=64: <4,1,1,H,L> 6.8, <4,2,1,H,L> 7.1, <4,2,1,H> 8.0
+//   K=4864 N=896 M=64: <4,1,1,H,L> 17.6, <4,1,1,H> 21.8
+// i.e. halves whenever the whole-pair grid leaves CUs short of work, the
+// deepest per-wave prefetch the registers allow at one or two tokens' rows,
+// and staged activations for narrow groups from 9 rows on.
 hipError_t launch_decode_gemm(const swk::DecodeArgs& d, int64_t n_tiled, const Plan& p, hipStream_t s) {
     const bool long_k = p.KB >= 96;
-    const int64_t wg16 = ceil_div(n_tiled, 16), wg64 = ceil_div(n_tiled, 64);
+    const int64_t wg64 = ceil_div(n_tiled, 64);
     switch (p.decode_mt) {
         case 1:
             if (long_k && 2 * wg64 >= p.cus) return launch_decode<1, 4, 4, true, true>(d, n_tiled, s);
             if (d.M <= 8) return launch_decode<1, 1, 14, true, true>(d, n_tiled, s);
-            return wg16 < 2 * p.cus ? launch_decode<1, 1, 8, true, true>(d, n_tiled, s)
-                                    : launch_decode<1, 1, 8, true>(d, n_tiled, s);
+            return launch_decode<1, 1, 8, true, true, true>(d, n_tiled, s);
         case 2:
             if (long_k) {
                 return 4 * wg64 >= 3 * p.cus ? launch_decode<2, 8, 1, true, true>(d, n_tiled, s)
@@ -446,8 +459,7 @@ hipError_t launch_decode_gemm(const swk::DecodeArgs& d, int64_t n_tiled, const P
                                                        : launch_decode<2, 2, 2, true>(d, n_tiled, s);
         default:
             if (long_k && 4 * wg64 >= 3 * p.cus) return launch_decode<4, 4, 1, true>(d, n_tiled, s);
-            return p.KB >= 32 ? launch_decode<4, 1, 1, true, true>(d, n_tiled, s)
-                              : launch_decode<4, 2, 1, true, true>(d, n_tiled, s);
+            return launch_decode<4, 1, 1, true, true, true>(d, n_tiled, s);
     }
 }
 

@@ -296,12 +296,13 @@ def test_edge_cases(dev):
 
 @pytest.mark.parametrize("M,K,N,auto_decode", [
     (1, 6144, 24576, True),    # long K, >= 192 column tiles: 8 column groups per workgroup
-    (16, 3584, 4096, True),    # short K: one column group, 8 K blocks in flight per wave
+    (16, 3584, 4096, True),    # short K: one column group, 8 K blocks in flight, activations via LDS
+    (8, 1000, 2056, True),     # the same with at most 8 rows: activations from global, ragged K
     (32, 6144, 12288, True),   # long K, M <= 32, under two workgroups per CU: 4 column groups
     (32, 512, 16384, True),    # M <= 32, wide N: 8 column groups
     (24, 512, 4096, True),     # M <= 32, short K, narrow N: 2 column groups, 2 K blocks in flight
     (48, 6144, 12288, False),  # long K, M <= 64: 4 column groups (AUTO takes the panel schedule)
-    (64, 1024, 2048, True),    # short K, M <= 64, few panels: 2 column groups
+    (64, 1024, 2048, True),    # short K, M <= 64, few panels: 2 column groups, activations via LDS
 ])
 def test_decode_configurations(dev, M, K, N, auto_decode):
     """Every decode configuration by M, K and N (column groups per workgroup,
@@ -486,14 +487,14 @@ def check_gemm_ulp(got_bits, ref_bits, what):
 @pytest.mark.parametrize("M,K,N", [
     # decode GEMM, each of its configurations on a 256-CU chip:
     (1, 200, 264),                  # <1,1,14> on weight halves (M <= 8)
-    (16, 3584, 1032),               # <1,1,8> on halves (few column groups)
-    (12, 200, 16400),               # <1,1,8> on both halves (wide)
+    (16, 3584, 1032),               # <1,1,8> on halves, activations via LDS
+    (12, 200, 16400),               # the same, wide, ragged K
     (3, 6200, 16400),               # <1,4,4> on halves (long K, wide)
     (17, 136, 520), (32, 896, 4864),  # <2,2,2>
     (24, 6200, 24600),              # <2,8,1> on halves (long K, wide)
     (20, 6200, 1000),               # <2,2,2> on halves (long K, narrow)
-    (48, 200, 1032), (64, 72, 136),   # <4,2,1> on halves (short K, few panels)
-    (40, 2104, 520),                # <4,1,1> on halves (few panels)
+    (48, 200, 1032), (64, 72, 136),   # <4,1,1> on halves, activations via LDS (short, ragged K)
+    (40, 2104, 520),                # the same, 33 K blocks
     (64, 3584, 18944),                                                     # panel schedule: half-panels
     (72, 200, 30584),                                                      # 3-4 half-panels per workgroup
     (128, 4864, 896),                                                      # down-projection shape: 3.5 tiles
