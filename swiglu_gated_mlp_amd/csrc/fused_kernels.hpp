@@ -1785,10 +1785,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
 // activations as src1 (lane l: token l & 31, the same k, two 16-byte loads).  The four per-wave fp32 sums are added in LDS in wave
 // order 0..3, scaled (p.sg, p.su), and SiLU(Gate) * Up is stored as bf16.
 // ---------------------------------------------------------------------------
-template <int CG, int UNROLL>
+// LDSA: the 32 token rows of each 128-k block go through the wave's own LDS
+// slots (one full-line direct load per 8 rows, chunks XOR-ed with row & 7)
+// instead of four half-filled 16-byte loads per row.
+template <int CG, int UNROLL, bool LDSA = false>
 __global__ __launch_bounds__(256) void decode_fp8_kernel(FusedArgs p) {
     constexpr int WAVES = 4;
     __shared__ f32x16 red[WAVES][CG][2][64];
+    __shared__ __attribute__((aligned(16))) uint8_t sA8[LDSA ? WAVES * UNROLL * 32 * 128 : 16];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -1797,6 +1801,10 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(FusedArgs p) {
     const int jt = n0 / PACK_BN, rb0 = (n0 % PACK_BN) / 32;
     const char* wtile = reinterpret_cast<const char*>(p.W1) + (size_t)jt * KB * 32768 + lane * 16;
     const char* arow = reinterpret_cast<const char*>(p.A) + (size_t)min(lane & 31, M - 1) * K + 32 * (lane >> 5);
+    // LDSA: direct load i of a block brings row 8i + (lane >> 3), logical
+    // 16-byte chunk (lane & 7) ^ (lane >> 3), to physical chunk lane & 7
+    const int a_chunk = (lane & 7) ^ (lane >> 3);
+    uint8_t* const sAw = sA8 + (LDSA ? wave * UNROLL * 32 * 128 : 0);
 
     f32x16 acc[CG][2];
 #pragma unroll
@@ -1808,6 +1816,27 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(FusedArgs p) {
 
     for (int kb0 = wave; kb0 < KB; kb0 += WAVES * UNROLL) {
         i32x4 wv[UNROLL][CG][2][2][2], av[UNROLL][2][2];
+        if constexpr (LDSA) {
+            // this wave's fragment reads of its slots (previous blocks) are done
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int kb = kb0 + u * WAVES;
+                if (kb < KB) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 8 * i + (lane >> 3);
+                        const char* src = kb * 128 + 16 * a_chunk < K
+                                              ? reinterpret_cast<const char*>(p.A) + (size_t)min(r, M - 1) * K +
+                                                    (size_t)kb * 128 + 16 * a_chunk
+                                              : reinterpret_cast<const char*>(g_zero_chunk);
+                        dma16(reinterpret_cast<const uint16_t*>(src),
+                              reinterpret_cast<uint16_t*>(sAw + (u * 32 + 8 * i) * 128));
+                    }
+                }
+            }
+        }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int kb = kb0 + u * WAVES;
@@ -1823,15 +1852,32 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(FusedArgs p) {
                             for (int h = 0; h < 2; ++h)
                                 wv[u][c][g][ks][h] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(
                                     blk + ((4 * g + rb0 + c) * 2 + ks) * 2048 + 1024 * h));
+                if constexpr (!LDSA) {
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const int k = kb * 128 + 64 * ks + 32 * (lane >> 5) + 16 * h;
+                            av[u][ks][h] = k < K ? *reinterpret_cast<const i32x4*>(arow + (size_t)kb * 128 + 64 * ks +
+                                                                                   16 * h)
+                                                 : i32x4{0, 0, 0, 0};
+                        }
+                }
+            }
+        }
+        if constexpr (LDSA) {
+            // the activations have landed (the weight loads issued after them too)
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 63));
+            asm volatile("" ::: "memory");
+            const int r = lane & 31;
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int k = kb * 128 + 64 * ks + 32 * (lane >> 5) + 16 * h;
-                        av[u][ks][h] = k < K ? *reinterpret_cast<const i32x4*>(arow + (size_t)kb * 128 + 64 * ks + 16 * h)
-                                             : i32x4{0, 0, 0, 0};
-                    }
-            }
+                    for (int h = 0; h < 2; ++h)
+                        av[u][ks][h] = *reinterpret_cast<const i32x4*>(
+                            sAw + (u * 32 + r) * 128 + 16 * ((4 * ks + 2 * (lane >> 5) + h) ^ (r & 7)));
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {

@@ -367,22 +367,25 @@ Plan stream_dp_plan(int64_t M, int64_t K, int64_t N, int cus) {
 // 128-k blocks in flight per wave (UNROLL).
 constexpr int64_t kDecodeFp8MaxM = 32;
 
-template <int CG, int UNROLL>
+template <int CG, int UNROLL, bool LDSA = false>
 hipError_t launch_decode_fp8_cfg(const swk::FusedArgs& a, hipStream_t s) {
     swk::FusedArgs args = a;
     void* kargs[] = {&args};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&swk::decode_fp8_kernel<CG, UNROLL>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&swk::decode_fp8_kernel<CG, UNROLL, LDSA>),
                            dim3((unsigned)ceil_div(a.N, 32 * CG)), dim3(256), kargs, 0, s);
 }
 
-// Measured (7B width M=1: <1,2> 27.2 us against 28.5-34.9 for the others;
-// 72B width M=32: <4,1> 83.6 us against 86.4-107): four groups per workgroup
-// when that grid still gives about one workgroup per CU, else one group and
-// two blocks in flight (two workgroups per CU).
+// Measured (7B width M=1: <1,2> 26.1 us against 26.7-32.4 for the others;
+// 72B width M=32: <4,1> 73.7 us against 78.6-112.8): four groups per
+// workgroup when that grid still gives about one workgroup per CU, else one
+// group and two blocks in flight (two workgroups per CU), its activations
+// staged through LDS (L) from 9 rows on (7B width M=16 / 32: <1,2,L> 26.3 /
+// 26.6 us against 27.0 / 31.3; M=1: 26.4 against 26.1; with <4,1> at 72B
+// M=32 78.8 against 73.7).
 hipError_t launch_decode_fp8(const swk::FusedArgs& a, int cus, hipStream_t s) {
     const int64_t wide = ceil_div(a.N, 128);
     if (wide <= cus && 4 * wide >= 3 * (int64_t)cus) return launch_decode_fp8_cfg<4, 1>(a, s);
-    return launch_decode_fp8_cfg<1, 2>(a, s);
+    return a.M > 8 ? launch_decode_fp8_cfg<1, 2, true>(a, s) : launch_decode_fp8_cfg<1, 2>(a, s);
 }
 
 // The decode kernel's configuration for a plan: column groups per workgroup

@@ -58,8 +58,8 @@ def test_fp8_pack_layout(dev):
 
 @pytest.mark.parametrize("M,K,N", [
     (1, 64, 128),         # FP8 decode kernel: one row, half a block
-    (16, 208, 2056),      # FP8 decode: ragged K, a partial last column group
-    (32, 1024, 8192),     # FP8 decode, 32 rows
+    (16, 208, 2056),      # FP8 decode, activations via LDS: ragged K, a partial last column group
+    (32, 1024, 8192),     # FP8 decode, activations via LDS, 32 rows
     (7, 3584, 18944),     # FP8 decode at the 7B width, one column group per workgroup
     (24, 1024, 29568),    # FP8 decode at the 72B width: four column groups per workgroup
     (40, 208, 520),       # panel schedule, ragged K, partial last column tile
