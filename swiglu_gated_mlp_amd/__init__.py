@@ -365,9 +365,9 @@ def _resolve_workspace(workspace, need: int, device: torch.device, s: int):
     if need == 0 and not isinstance(workspace, torch.Tensor):
         ws = None
     elif isinstance(workspace, Workspace):
-        ws = workspace.get(need)
+        ws = workspace.get(need, s)
     elif workspace is None:
-        ws = _workspace_for(device, s).get(need)
+        ws = _workspace_for(device, s).get(need, s)
     else:
         ws = workspace
     if ws is not None and ws.device.type != "cuda":
@@ -388,11 +388,20 @@ class Workspace:
         self.device = torch.device(device or "cuda")
         self.buf: torch.Tensor | None = None
 
-    def get(self, nbytes: int) -> torch.Tensor | None:
+    def get(self, nbytes: int, stream: int | None = None) -> torch.Tensor | None:
+        """A buffer of at least nbytes.  A larger buffer replaces a smaller
+        one; it is allocated on `stream` (a raw handle: the stream of the
+        calls that will use it), so the caching allocator hands the old
+        buffer's memory out again only to work ordered after those calls."""
         if nbytes == 0:
             return None
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            self.buf = None
+            if stream is None or stream == torch.cuda.current_stream(self.device).cuda_stream:
+                self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            else:
+                with torch.cuda.stream(torch.cuda.ExternalStream(stream, device=self.device)):
+                    self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         return self.buf
 
 

@@ -458,6 +458,31 @@ def test_split_workspace_reused_across_shapes(dev):
         ws.buf.fill_(0x7F)      # NaN-patterned leftovers must not matter to the next call
 
 
+def test_split_workspace_grows_on_call_stream(dev):
+    """Split-K calls queued on a stream other than the current one, each
+    needing a larger workspace than the last: the grown buffer is allocated
+    on the calls' stream, so the memory of the buffer it replaces is not
+    handed to the current stream's allocations (filled meanwhile) while the
+    earlier calls still write their partial sums into it."""
+    side = torch.cuda.Stream()
+    ws = sw.Workspace(dev)
+    cases = []
+    for i, (M, K, N) in enumerate([(128, 1024, 1024), (128, 2048, 4864), (128, 2048, 18944)]):
+        A, W1, W2 = inputs.gaussian_case(M, K, N, seed=400 + i)
+        cases.append((A.to(dev), sw.swiglu_pack_weights(W1.to(dev), W2.to(dev)), N))
+    torch.cuda.synchronize()
+    say("[side stream] split-K with a growing workspace")
+    outs, junk = [], []
+    for Ad, Wp, N in cases:
+        outs.append(sw.swiglu_fused_packed(Ad, Wp, N, workspace=ws, variant=SPLIT, stream=side))
+        junk.append(torch.full((4 << 20,), 0x7F, dtype=torch.uint8, device=dev))
+    torch.cuda.synchronize()
+    for (Ad, Wp, N), Y in zip(cases, outs):
+        ref = sw.swiglu_fused_packed(Ad, Wp, N, variant=SPLIT)
+        torch.cuda.synchronize()
+        assert np.array_equal(gpu_bits(Y), gpu_bits(ref)), "side-stream split-K call differs (N=%d)" % N
+
+
 @pytest.mark.parametrize("M,K,N", [(1, 200, 264), (17, 136, 520), (32, 896, 4864), (33, 72, 264),
                                    (48, 200, 1032), (64, 896, 4864),
                                    (65, 72, 264), (300, 200, 520), (1024, 896, 4864), (2100, 136, 256),
