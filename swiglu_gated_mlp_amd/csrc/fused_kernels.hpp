@@ -1791,7 +1791,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
 template <int CG, int UNROLL, bool LDSA = false>
 __global__ __launch_bounds__(256) void decode_fp8_kernel(FusedArgs p) {
     constexpr int WAVES = 4;
-    __shared__ f32x16 red[WAVES][CG][2][64];
+    // per-wave sums in 16-byte quarters, lane-contiguous (conflict-free LDS
+    // stores and loads: 64 lanes x 16 bytes per instruction)
+    __shared__ f32x4 red[WAVES][CG][2][4][64];
     __shared__ __attribute__((aligned(16))) uint8_t sA8[LDSA ? WAVES * UNROLL * 32 * 128 : 16];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1903,26 +1905,30 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(FusedArgs p) {
 #pragma unroll
     for (int c = 0; c < CG; ++c)
 #pragma unroll
-        for (int g = 0; g < 2; ++g) red[wave][c][g][lane] = acc[c][g];
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                red[wave][c][g][j][lane] =
+                    f32x4{acc[c][g][4 * j], acc[c][g][4 * j + 1], acc[c][g][4 * j + 2], acc[c][g][4 * j + 3]};
     __syncthreads();
     // epilogue: wave w finishes groups w, w + 4, ...; lane l holds token
     // m = l & 31 and columns n0 + 32c + 8(r/4) + 4(l >> 5) + r%4
     for (int c = wave; c < CG; c += WAVES) {
-        f32x16 g = red[0][c][0][lane], u = red[0][c][1][lane];
-#pragma unroll
-        for (int w = 1; w < WAVES; ++w) {
-            g += red[w][c][0][lane];
-            u += red[w][c][1][lane];
-        }
         const int m = lane & 31;
         if (m < M) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
+                f32x4 g = red[0][c][0][q][lane], u = red[0][c][1][q][lane];
+#pragma unroll
+                for (int w = 1; w < WAVES; ++w) {
+                    g += red[w][c][0][q][lane];
+                    u += red[w][c][1][q][lane];
+                }
                 const int n = n0 + 32 * c + 8 * q + 4 * (lane >> 5);
                 if (n < N) {
                     float v[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = silu_f(g[4 * q + e] * p.sg) * (u[4 * q + e] * p.su);
+                    for (int e = 0; e < 4; ++e) v[e] = silu_f(g[e] * p.sg) * (u[e] * p.su);
                     u32x2 out;
                     out[0] = pack2(v[0], v[1]);
                     out[1] = pack2(v[2], v[3]);
