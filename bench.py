@@ -310,6 +310,30 @@ def bench_point(w, M, steps, warmup, variant, stream, prewarm_s=0.0, layout="per
     return out
 
 
+def bench_rowmajor(w, M, steps, warmup, stream, prewarm_s=0.0):
+    """The fused product from row-major W1, W2 (swiglu_fused, no pack) and
+    the one-time pack of those weights (swiglu_pack_weights), each over
+    rotated sets; returns per-call seconds of both."""
+    import torch
+    import swiglu_gated_mlp_amd as sw
+    from swiglu_gated_mlp_amd import inputs
+    dev = torch.device("cuda:0")
+    K, N = w.K, w.N
+    A, W1, W2 = inputs.workload_tensors(w, M)
+    R = rotation_count(M, K, N)
+    sets = []
+    for _ in range(R):
+        W1d, W2d = W1.to(dev), W2.to(dev)
+        sets.append((A.to(dev), W1d, W2d, torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                     torch.empty(sw.swiglu_packed_bytes(K, N) // 2, dtype=torch.bfloat16, device=dev)))
+    torch.cuda.synchronize()
+    fused = [(lambda s=s: sw.swiglu_fused(s[0], s[1], s[2], Y=s[3])) for s in sets]
+    pack = [(lambda s=s: sw.swiglu_pack_weights(s[1], s[2], Wp=s[4])) for s in sets]
+    tr = time_gpu(fused, steps, warmup, stream, prewarm_s) / steps
+    tp = time_gpu(pack, max(3, steps // 4), 2, stream) / max(3, steps // 4)
+    return tr, tp
+
+
 def bench_unfused(w, M, steps, warmup, stream, prewarm_s=0.0):
     """The unfused pipeline on the library's fastest GEMM: W1 and W2 in the
     single-weight pack (packed once, like the fused weights), two GEMM calls
@@ -571,6 +595,11 @@ def main():
                 if "graph_per_launch_s" in r:
                     line["graph_us"] = round(r["graph_per_launch_s"] * 1e6, 2)
                 line.update(bench_gemm(ww, mm, max(10, args.steps // 2), 5, stream, args.prewarm))
+                # the unpacked entry point (row-major weights) and the one-time
+                # pack, reported beside the packed path they stand for
+                tr, tp = bench_rowmajor(ww, mm, max(10, args.steps // 4), 3, stream, args.prewarm)
+                line.update(rowmajor_us=round(tr * 1e6, 2), rowmajor_tflops=round(flops(mm, ww.K, ww.N) / tr / 1e12, 2),
+                            pack_us=round(tp * 1e6, 2))
                 log("POINT " + json.dumps(line))
                 extra.setdefault("points", []).append(line)
                 if args.mlp:

@@ -211,7 +211,7 @@ def swiglu_packed_bytes(K: int, N: int) -> int:
 
 def swiglu_pack_weights(W1: torch.Tensor, W2: torch.Tensor, Wp: torch.Tensor | None = None,
                         stream=None) -> torch.Tensor:
-    """Pack W1, W2 [K,N] into the per-128-column-tile interleaved layout."""
+    """Pack W1, W2 [K,N] into the per-128-column-tile [W1 | W2] layout."""
     K, N = W1.shape
     _shape(W2, (K, N), "W2")
     nbytes = swiglu_packed_bytes(K, N)
