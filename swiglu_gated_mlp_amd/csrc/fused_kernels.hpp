@@ -1940,7 +1940,7 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(FusedArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Row-major decode (swiglu_fused, M <= 32): the weight-streaming shape of
+// Row-major decode (swiglu_fused, M <= 64): the weight-streaming shape of
 // decode_kernel on W1, W2 as they lie in memory ([K,N], N-contiguous).  Each
 // workgroup owns CW output columns (64 or 32); its 4 waves take the 64-deep K
 // blocks round-robin, UNROLL blocks at a time.  A wave brings each block's 64
@@ -1948,9 +1948,10 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(FusedArgs p) {
 // loads -- slot row k holds 2*CW columns, W1's then W2's, its 16-byte chunks
 // XOR-swizzled by rmd_swz(k) -- and reads the MFMA weight fragments back with
 // the transposing LDS read (8 K-consecutive values of one column per lane).
-// The activations (32 token rows, rows past M repeating row M - 1) are
-// 16-byte loads straight to registers.  One v_mfma_f32_32x32x16_bf16 per
-// (Gate|Up, 32-column piece, 16-deep step); the four per-wave fp32 sums are
+// The activations (MT tiles of 32 token rows, rows past M repeating row
+// M - 1) are 16-byte loads straight to registers.  One
+// v_mfma_f32_32x32x16_bf16 per (Gate|Up, 32-column piece, token tile, 16-deep
+// step); the four per-wave fp32 sums are
 // added in LDS in wave order 0..3, then SiLU(Gate) * Up in fp32 and bf16
 // stores.  With CW = 32 a row of W1 (or W2) per block is half a cache line,
 // the other half belonging to the neighbouring workgroup, which the XCD-aware
@@ -1965,9 +1966,10 @@ __device__ __forceinline__ int rmd_off(int k, int col) {
     return k * (2 * CW) + ((((col >> 3) ^ rmd_swz<CW>(k))) << 3) + (col & 7);
 }
 
-template <int CW, int UNROLL>
+template <int CW, int UNROLL, int MT>
 __global__ __launch_bounds__(256) void rowmajor_decode_kernel(FusedArgs p) {
     static_assert(CW == 64 || CW == 32, "64 or 32 columns per workgroup");
+    static_assert(MT == 1 || MT == 2, "one or two 32-token tiles");
     constexpr int WAVES = 4;
     constexpr int NB = 2 * CW;               // LDS row: CW W1 columns, then CW W2 columns
     constexpr int CH = NB / 8;               // 16-byte chunks per LDS row
@@ -1975,7 +1977,7 @@ __global__ __launch_bounds__(256) void rowmajor_decode_kernel(FusedArgs p) {
     constexpr int KBLK = 64;                 // K rows per block
     constexpr int SLOT = KBLK * NB;          // elements per block slot
     constexpr int NJ = CW / 32;              // 32-column pieces per weight
-    constexpr int RED = WAVES * 2 * NJ * 4 * 64 * 4;   // floats of the per-wave sums
+    constexpr int RED = WAVES * 2 * NJ * MT * 4 * 64 * 4;   // floats of the per-wave sums
     constexpr int SW = WAVES * UNROLL * SLOT > 2 * RED ? WAVES * UNROLL * SLOT : 2 * RED;
     __shared__ __attribute__((aligned(16))) uint16_t sW[SW];
     const int tid = threadIdx.x;
@@ -1997,25 +1999,29 @@ __global__ __launch_bounds__(256) void rowmajor_decode_kernel(FusedArgs p) {
     const uint16_t* const wsrc = (lchunk >= CH / 2 ? p.W2 : p.W1) + (col_ok ? ncol : 0);
     // activation rows: token lane & 31 (rows past M repeat row M - 1), the
     // 8 k at 8 (lane >> 5) of each 16-deep step
-    const uint16_t* const arow = p.A + (size_t)min(lane & 31, M - 1) * K + 8 * (lane >> 5);
+    const uint16_t* arow[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) arow[t] = p.A + (size_t)min(t * 32 + (lane & 31), M - 1) * K + 8 * (lane >> 5);
     // transposing reads: lane l gets W[16kk + 8(l >> 5) + 0..7][column l & 31
     // of the 32-column piece]
     const int kr0 = 8 * (lane >> 5) + ((lane & 15) >> 2);
     const int cl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    f32x16 acc[2][NJ];
+    f32x16 acc[2][NJ][MT];
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[g][j][r] = 0.0f;
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[g][j][t][r] = 0.0f;
 
     for (int kb0 = wave; kb0 < KB; kb0 += WAVES * UNROLL) {
         // this wave's fragment reads of its slots (previous blocks) are done
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
         asm volatile("" ::: "memory");
-        u32x4 av[UNROLL][4];
+        u32x4 av[UNROLL][4][MT];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int kb = kb0 + u * WAVES;
@@ -2029,7 +2035,9 @@ __global__ __launch_bounds__(256) void rowmajor_decode_kernel(FusedArgs p) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     const int k = kb * KBLK + 16 * kk + 8 * (lane >> 5);
-                    av[u][kk] = k < K ? ld16(arow + (size_t)kb * KBLK + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int t = 0; t < MT; ++t)
+                        av[u][kk][t] = k < K ? ld16(arow[t] + (size_t)kb * KBLK + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
                 }
             }
         }
@@ -2042,7 +2050,6 @@ __global__ __launch_bounds__(256) void rowmajor_decode_kernel(FusedArgs p) {
             if (kb < KB) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    const bf16x8 a8 = __builtin_bit_cast(bf16x8, av[u][kk]);
 #pragma unroll
                     for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -2051,8 +2058,11 @@ __global__ __launch_bounds__(256) void rowmajor_decode_kernel(FusedArgs p) {
                             const s16x4 lo = ds_read_tr16(sWw + u * SLOT + rmd_off<CW>(16 * kk + kr0, col));
                             const s16x4 hi = ds_read_tr16(sWw + u * SLOT + rmd_off<CW>(16 * kk + kr0 + 4, col));
                             const s16x4 both[2] = {lo, hi};
-                            acc[g][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), a8,
-                                                                                acc[g][j], 0, 0, 0);
+                            const bf16x8 w8 = __builtin_bit_cast(bf16x8, both);
+#pragma unroll
+                            for (int t = 0; t < MT; ++t)
+                                acc[g][j][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                    w8, __builtin_bit_cast(bf16x8, av[u][kk][t]), acc[g][j][t], 0, 0, 0);
                         }
                 }
             }
@@ -2060,31 +2070,36 @@ __global__ __launch_bounds__(256) void rowmajor_decode_kernel(FusedArgs p) {
     }
 
     // per-wave sums in 16-byte quarters, lane-contiguous, in the slots' LDS
-    // once every wave is done with them: red[wave][g][j][q][lane]
+    // once every wave is done with them: red[wave][g][j][t][q][lane]
     __syncthreads();
     f32x4* red = reinterpret_cast<f32x4*>(sW);
-    auto ridx = [&](int w, int g, int j, int q) { return (((w * 2 + g) * NJ + j) * 4 + q) * 64 + lane; };
+    auto ridx = [&](int w, int g, int j, int t, int q) {
+        return ((((w * 2 + g) * NJ + j) * MT + t) * 4 + q) * 64 + lane;
+    };
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                red[ridx(wave, g, j, q)] =
-                    f32x4{acc[g][j][4 * q], acc[g][j][4 * q + 1], acc[g][j][4 * q + 2], acc[g][j][4 * q + 3]};
-    __syncthreads();
-    // wave w finishes the (32-column piece j, row quad q) pieces j * 4 + q = w, w + 4, ...
-    const int m = lane & 31;
+            for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int t = 0; t < NJ; ++t) {
-        const int jq = wave + 4 * t;
-        const int j = jq >> 2, q = jq & 3;
-        f32x4 g = red[ridx(0, 0, j, q)], u = red[ridx(0, 1, j, q)];
+                for (int q = 0; q < 4; ++q)
+                    red[ridx(wave, g, j, t, q)] = f32x4{acc[g][j][t][4 * q], acc[g][j][t][4 * q + 1],
+                                                        acc[g][j][t][4 * q + 2], acc[g][j][t][4 * q + 3]};
+    __syncthreads();
+    // wave w finishes the (32-column piece j, token tile t, row quad q)
+    // pieces (j * MT + t) * 4 + q = w, w + 4, ...
+#pragma unroll
+    for (int x = 0; x < NJ * MT; ++x) {
+        const int jtq = wave + 4 * x;
+        const int q = jtq & 3, t = (jtq >> 2) % MT, j = (jtq >> 2) / MT;
+        f32x4 g = red[ridx(0, 0, j, t, q)], u = red[ridx(0, 1, j, t, q)];
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) {
-            g += red[ridx(w, 0, j, q)];
-            u += red[ridx(w, 1, j, q)];
+            g += red[ridx(w, 0, j, t, q)];
+            u += red[ridx(w, 1, j, t, q)];
         }
+        const int m = t * 32 + (lane & 31);
         const int n = n0 + 32 * j + 8 * q + 4 * (lane >> 5);
         if (m < M && n < N) {
             u32x2 out;

@@ -699,22 +699,29 @@ swiglu_status swiglu_fused(const swiglu_bf16* A, const swiglu_bf16* W1, const sw
     a.splits = 1; a.kb_per_split = a.KB;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    // M <= 32: the row-major decode kernel; M <= 64: register-transposing tile
-    // kernel on 64-column tiles (128-byte weight rows; twice the workgroups of
-    // 128-column tiles); above: direct loads of the row-major weight tiles,
-    // fragments through the transposing LDS read
-    if (M <= 32) {
-        // the weight-streaming row-major decode kernel: 64-column workgroups
-        // when they are at least 1.5 per CU, else 32-column workgroups with
-        // two K blocks in flight per wave (measured: 72B-width 195 -> 165 us
-        // at M=1 with 64 columns, 7B-width 80.6 -> 67.7 us with 32)
-        const int cus = std::max(1, cu_count_now());
-        const bool wide = 2 * ceil_div(N, 64) >= 3 * (int64_t)cus;
+    // small M: the row-major decode kernel (or, for 32 < M <= 64 when
+    // 32-column workgroups would number more than the CUs, the
+    // register-transposing tile kernel on 64-column tiles); above 64 rows:
+    // direct loads of the row-major weight tiles, fragments through the
+    // transposing LDS read
+    const int cus = std::max(1, cu_count_now());
+    // the weight-streaming row-major decode kernel: 64-column workgroups when
+    // they are at least 1.5 per CU, else 32-column ones (measured:
+    // 72B-width 195 -> 165 us at M=1 with 64 columns, 7B-width 80.6 -> 67.7 us
+    // with 32 and two K blocks in flight); two 32-token tiles above 32 rows,
+    // as long as the narrow grid stays within one workgroup per CU (every
+    // workgroup reads all the activation rows: 7B-width M=64 keeps the tile
+    // kernel, 91 against 111 us; the tiny point's M=64 21.9 -> 13.4 us)
+    const bool wide = 2 * ceil_div(N, 64) >= 3 * (int64_t)cus;
+    const bool two = M > 32;
+    if (M <= 32 || (M <= 64 && (wide || ceil_div(N, 32) <= cus))) {
+        const void* fn = wide ? (two ? reinterpret_cast<const void*>(&swk::rowmajor_decode_kernel<64, 1, 2>)
+                                     : reinterpret_cast<const void*>(&swk::rowmajor_decode_kernel<64, 1, 1>))
+                              : (two ? reinterpret_cast<const void*>(&swk::rowmajor_decode_kernel<32, 1, 2>)
+                                     : reinterpret_cast<const void*>(&swk::rowmajor_decode_kernel<32, 2, 1>));
         swk::FusedArgs args = a;
         void* kargs[] = {&args};
-        e = hipLaunchKernel(wide ? reinterpret_cast<const void*>(&swk::rowmajor_decode_kernel<64, 1>)
-                                 : reinterpret_cast<const void*>(&swk::rowmajor_decode_kernel<32, 2>),
-                            dim3((unsigned)ceil_div(N, wide ? 64 : 32)), dim3(256), kargs, 0, s);
+        e = hipLaunchKernel(fn, dim3((unsigned)ceil_div(N, wide ? 64 : 32)), dim3(256), kargs, 0, s);
     } else if (M <= 64) {
         a.tiles_m = 1; a.tiles_n = (int)ceil_div(N, 64);
         e = launch_tile<64, 64, 2, 1, true, false, false>(a, a.tiles_m * a.tiles_n, s);

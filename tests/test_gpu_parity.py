@@ -319,18 +319,20 @@ def test_decode_configurations(dev, M, K, N, auto_decode):
     check_close(gpu_bits(Ya), ref, "auto %s" % ((M, K, N),))
 
 
-@pytest.mark.parametrize("wide", [False, True])
-@pytest.mark.parametrize("M,K", [(1, 136), (7, 72), (32, 200), (17, 1000)])
-def test_rowmajor_decode_widths(dev, M, K, wide):
-    """swiglu_fused at M <= 32 (the row-major decode kernel) on both of its
-    workgroup widths: 32 columns with two K blocks in flight while 64-column
-    workgroups would number under 1.5 per CU, else 64 columns; ragged K and a
+@pytest.mark.parametrize("grid", ["one-per-cu", "narrow", "wide"])
+@pytest.mark.parametrize("M,K", [(1, 136), (7, 72), (32, 200), (17, 1000), (33, 136), (64, 328)])
+def test_rowmajor_decode_widths(dev, M, K, grid):
+    """swiglu_fused at M <= 64 on each of its small-M schedules: the row-major
+    decode kernel with 32-column workgroups (two K blocks in flight for one
+    token tile, one for two) while 64-column ones would number under 1.5 per
+    CU, with 64-column ones above that, and for 32 < M <= 64 with more
+    32-column workgroups than CUs the 64x64 tile kernel; ragged K and a
     partial last workgroup of columns, every element against the oracle."""
     cus = sw.swiglu_device_cu_count()
     wide_min = 64 * ((3 * cus + 1) // 2)          # the narrowest N with 64-column workgroups
-    N = wide_min + 40 if wide else wide_min - 64 * 3 - 24
+    N = {"one-per-cu": 32 * cus - 24, "narrow": wide_min - 64 * 3 - 24, "wide": wide_min + 40}[grid]
     A, W1, W2 = inputs.gaussian_case(M, K, N, seed=5 * M + K + N)
-    say("[rowmajor decode] M=%d K=%d N=%d wide=%s" % (M, K, N, wide))
+    say("[rowmajor decode] M=%d K=%d N=%d grid=%s" % (M, K, N, grid))
     Y = sw.swiglu_fused(A.to(dev), W1.to(dev), W2.to(dev))
     torch.cuda.synchronize()
     check_close(gpu_bits(Y), oracle.swiglu(A, W1, W2), "rowmajor decode %s" % ((M, K, N),))
