@@ -339,6 +339,24 @@ def test_rowmajor_decode_widths(dev, M, K, grid):
 
 
 @pytest.mark.parametrize("M,K,N", [
+    (128, 200, 9000),     # 71 tiles of 128 columns: 141 of 64 columns, one round
+    (100, 136, 30000),    # 235 tiles of 128 columns: 469 of 64 columns; M tail
+    (300, 72, 8200),      # 3 x 65 tiles of 128 columns: 3 x 129 = 387 of 64 columns
+    (130, 64, 18944),     # 2 x 148 tiles of 128 columns fill the CUs: stays on 128
+])
+def test_rowmajor_prefill_tiles(dev, M, K, N):
+    """swiglu_fused for 64 < M <= 2048 on 128x64 tiles (when 128x128 tiles
+    leave CUs idle and the 64-column grid fits one round or fills one and a
+    half) and on 128x128 tiles; ragged K and N, every element against the
+    oracle."""
+    A, W1, W2 = inputs.gaussian_case(M, K, N, seed=3 * M + K + N)
+    say("[rowmajor prefill] M=%d K=%d N=%d" % (M, K, N))
+    Y = sw.swiglu_fused(A.to(dev), W1.to(dev), W2.to(dev))
+    torch.cuda.synchronize()
+    check_close(gpu_bits(Y), oracle.swiglu(A, W1, W2), "rowmajor prefill %s" % ((M, K, N),))
+
+
+@pytest.mark.parametrize("M,K,N", [
     (100, 256, 8192),     # 256 panels: one per workgroup
     (72, 64, 12040),      # one or two panels per workgroup; the last panel partly past N
     (128, 200, 24576),    # three panels per workgroup, across packed-tile borders; ragged K
