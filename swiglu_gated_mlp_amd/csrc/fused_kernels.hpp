@@ -1532,7 +1532,7 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
 template <int BM, bool SPLIT, bool RAGGED, bool PANELS = false, bool IL = false, bool F8 = false,
           bool SEQ = false, bool GEMM = false>
 __global__ __launch_bounds__(256) void stream_prefill_kernel(FusedArgs p, int total) {
-    static_assert(!PANELS || (BM == 128 && !SPLIT), "panel schedule: one 128-row tile, data-parallel");
+    static_assert(!PANELS || !SPLIT, "panel schedule: one row tile, data-parallel");
     __shared__ __attribute__((aligned(16))) uint16_t smem[stream_smem_elems<BM>()];
     stream_prefill_tiles<BM, SPLIT, RAGGED, PANELS, IL, F8, SEQ, GEMM>(p, smem, blockIdx.x, gridDim.x, total);
 }

@@ -168,13 +168,23 @@ struct TileCfg {
 // Split-K keeps small row tiles for small M; the data-parallel schedule is
 // the streaming kernel at every M (one row of 128-row tiles for M <= 128, on
 // the panel schedule when its column tiles leave CUs idle).
-TileCfg packed_tile_for(int64_t M, int variant) {
+// Data-parallel tiles: 256 x 128 (persistent, with the 128-row tail of the
+// mixed launch) above 512 rows, and from 385 rows when the last row tile is
+// at least three quarters full and the 256-row grid fills the CUs; else
+// 128 x 128 (measured against 128-row tiles everywhere up to 2048 rows:
+// 7B width M=512 152 -> 141 us, M=768 201 -> 178 us, M=2048 479 -> 422 us,
+// 72B width M=1024 865 -> 751 us; 0.5B width M=1024 29.4 -> 25.0 us).
+TileCfg packed_tile_for(int64_t M, int variant, int64_t N, int cus) {
     if (variant == SWIGLU_VARIANT_SPLIT_K) {
         if (M <= 32) return {32, 128};
         if (M <= 64) return {64, 128};
         return {128, 128};
     }
-    if (M <= 2048) return {128, 128};
+    if (M <= 512) {
+        if (M > 384 && (M % 256 == 0 || M % 256 >= 192) && ceil_div(M, 256) * ceil_div(N, 128) >= cus)
+            return {256, 128};
+        return {128, 128};
+    }
     return {256, 128};
 }
 
@@ -223,7 +233,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int variant, int cus) {
             // most K / (16 M) splits (extra traffic <= a quarter of the
             // weights).  A data-parallel grid that fills half the CUs streams
             // the weights faster than split-K does.
-            const TileCfg dp = packed_tile_for(M, SWIGLU_VARIANT_DATA_PARALLEL);
+            const TileCfg dp = packed_tile_for(M, SWIGLU_VARIANT_DATA_PARALLEL, N, cus);
             const int64_t dp_tiles = ceil_div(M, dp.BM) * ceil_div(N, dp.BN);
             auto_split_cap = (int)std::min<int64_t>(K / (16 * M), 1 << 20);
             v = (2 * dp_tiles >= cus || p.KB < 4 || auto_split_cap < 2) ? SWIGLU_VARIANT_DATA_PARALLEL
@@ -234,7 +244,7 @@ Plan make_plan(int64_t M, int64_t K, int64_t N, int variant, int cus) {
     p.decode_mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     // the sequential order runs on the data-parallel tiles (no panel schedule)
     const bool dp_tiles = v == SWIGLU_VARIANT_DATA_PARALLEL || v == SWIGLU_VARIANT_SEQUENTIAL;
-    p.t = packed_tile_for(M, dp_tiles ? SWIGLU_VARIANT_DATA_PARALLEL : v);
+    p.t = packed_tile_for(M, dp_tiles ? SWIGLU_VARIANT_DATA_PARALLEL : v, N, cus);
     p.tiles_m = (int)ceil_div(M, p.t.BM);
     p.tiles_n = (int)ceil_div(N, p.t.BN);
     p.tiles = p.tiles_m * p.tiles_n;
@@ -325,6 +335,20 @@ hipError_t launch_stream_dp(const swk::FusedArgs& a, const Plan& p, hipStream_t 
     const int grid = p.tiles;
     if (p.t.BM == 128) {
         if constexpr (SEQ) return launch_stream<128, false, false, false, false, true>(a, grid, grid, s);
+        if constexpr (!GEMM && !IL && !F8) {
+            // two rows of 128-row tiles that leave CUs idle on a wide product:
+            // one row of 256-row tiles on the panel schedule instead, the
+            // weights streamed once (7B width M=192 98.6 -> 84.2 us, 72B width
+            // M=256 259 -> 226 us; the 0.5B width's few short panels lose,
+            // 13.5 against 24 us, and keep the 128-row tiles)
+            if (p.tiles_m == 2 && a.M <= 256 && p.tiles_n < p.cus && 2 * p.tiles_n >= p.cus) {
+                swk::FusedArgs pa = a;
+                pa.tiles_m = 1;
+                pa.panels = 4 * p.tiles_n;
+                const int g = std::min(pa.panels, p.cus);
+                return launch_stream<256, false, true, false, false, false, false>(pa, g, g, s);
+            }
+        }
         if (p.panels > 0) {
             // the single-weight GEMM's units are half-panels (one weight half
             // each), as long as no workgroup gets more than its 4 waves

@@ -71,6 +71,10 @@ SMALL_SHAPES = [
     # the smallest legal K and N (one 16-byte chunk of k; one 8-column piece of
     # a 128-column tile) on the decode, 128-row and 256-row schedules
     (3, 8, 8), (70, 8, 24), (300, 24, 8), (2100, 8, 8),
+    # 256-row tiles below 2048 rows: from 385 rows with a last row tile at
+    # least three quarters full and a 256-row grid that fills the CUs (with the
+    # 128-row tail), and above 512 rows; 416 rows stays on 128-row tiles
+    (450, 136, 18000), (512, 64, 16384), (600, 136, 2000), (416, 200, 18944),
 ]
 
 
@@ -357,16 +361,20 @@ def test_rowmajor_prefill_tiles(dev, M, K, N):
 
 
 @pytest.mark.parametrize("M,K,N", [
+    # two rows of 128-row tiles on a wide product: one row of 256-row tiles on
+    # the panel schedule (ragged K, partial last packed tile, M tail)
+    (200, 136, 16392), (256, 72, 30000), (129, 64, 24576),
     (100, 256, 8192),     # 256 panels: one per workgroup
     (72, 64, 12040),      # one or two panels per workgroup; the last panel partly past N
     (128, 200, 24576),    # three panels per workgroup, across packed-tile borders; ragged K
     (96, 136, 30000),     # three or four panels; a partial last packed tile
 ])
 def test_panel_schedule(dev, M, K, N):
-    """One row of 128-row tiles with fewer column tiles than CUs: the
-    32-column weight panels are spread over the workgroups (data-parallel and
-    AUTO), all elements against the oracle and bitwise against the row-major
-    entry point (same MFMA chain per element)."""
+    """One row of 128-row tiles (or, for two rows on a wide product, one row
+    of 256-row tiles) with fewer column tiles than CUs: the 32-column weight
+    panels are spread over the workgroups (data-parallel and AUTO), all
+    elements against the oracle and bitwise against the row-major entry point
+    (same MFMA chain per element)."""
     A, W1, W2 = inputs.gaussian_case(M, K, N, seed=M + 3 * K + N)
     Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
     Wp = sw.swiglu_pack_weights(W1d, W2d)
