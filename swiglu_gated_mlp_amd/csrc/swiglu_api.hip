@@ -335,18 +335,20 @@ hipError_t launch_stream_dp(const swk::FusedArgs& a, const Plan& p, hipStream_t 
     const int grid = p.tiles;
     if (p.t.BM == 128) {
         if constexpr (SEQ) return launch_stream<128, false, false, false, false, true>(a, grid, grid, s);
-        if constexpr (!GEMM && !IL && !F8) {
+        if constexpr (!GEMM && !IL) {
             // two rows of 128-row tiles that leave CUs idle on a wide product:
             // one row of 256-row tiles on the panel schedule instead, the
             // weights streamed once (7B width M=192 98.6 -> 84.2 us, 72B width
-            // M=256 259 -> 226 us; the 0.5B width's few short panels lose,
-            // 13.5 against 24 us, and keep the 128-row tiles)
+            // M=256 259 -> 226 us; FP8 72B width M=192 144 -> 127 us; the 0.5B
+            // width's few short panels lose, 13.5 against 24 us, and keep the
+            // 128-row tiles, as does the interleaved layout, 95 against 107 us
+            // at the 7B width)
             if (p.tiles_m == 2 && a.M <= 256 && p.tiles_n < p.cus && 2 * p.tiles_n >= p.cus) {
                 swk::FusedArgs pa = a;
                 pa.tiles_m = 1;
                 pa.panels = 4 * p.tiles_n;
                 const int g = std::min(pa.panels, p.cus);
-                return launch_stream<256, false, true, false, false, false, false>(pa, g, g, s);
+                return launch_stream<256, false, true, IL, F8, false, false>(pa, g, g, s);
             }
         }
         if (p.panels > 0) {

@@ -64,6 +64,7 @@ def test_fp8_pack_layout(dev):
     (24, 1024, 29568),    # FP8 decode at the 72B width: four column groups per workgroup
     (40, 208, 520),       # panel schedule, ragged K, partial last column tile
     (128, 512, 4096),     # panel schedule, 2-3 panels per workgroup
+    (200, 256, 16392),    # two rows of 128-row tiles, wide: one row of 256-row tiles on the panel schedule
     (300, 144, 264),      # 128-row tiles, ragged K
     (2100, 128, 256),     # persistent 256-row tiles, M tail
     (4000, 256, 2696),    # mixed 256/128-row launch, partial last column tile

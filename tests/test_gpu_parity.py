@@ -470,6 +470,7 @@ def test_interleaved_pack_roundtrip_and_layout(dev):
 @pytest.mark.parametrize("M,K,N", [
     (1, 64, 128), (40, 200, 520), (128, 512, 4096), (300, 136, 264),
     (2100, 72, 256), (4000, 200, 2696),
+    (200, 136, 16392),    # one row of 256-row tiles on the panel schedule
 ])
 def test_interleaved_layout_matches(dev, M, K, N):
     """The interleaved-layout path against the oracle and bitwise against the
