@@ -1642,6 +1642,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
         for (int c = 0; c < CG; ++c) {
             accg[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
             accu[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // opaque zeros: with one shared zero register as every sum's
+            // start, the allocator gave the loop-carried sums different
+            // registers at the loop's entry and back edge and copied them at
+            // every step (80 copies per 32 MFMAs at 64 rows; tiny-width
+            // M=64 9.4 -> 8.8 us, bitwise equal)
+            asm volatile("" : "+a"(accg[t][c]), "+a"(accu[t][c]));
         }
 
     for (int kb0 = wave; kb0 < KB; kb0 += WAVES * UNROLL) {
@@ -2013,9 +2019,11 @@ __global__ __launch_bounds__(256) void rowmajor_decode_kernel(FusedArgs p) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int t = 0; t < MT; ++t)
+            for (int t = 0; t < MT; ++t) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[g][j][t][r] = 0.0f;
+                asm volatile("" : "+a"(acc[g][j][t]));   // opaque zeros, as in decode_kernel
+            }
 
     for (int kb0 = wave; kb0 < KB; kb0 += WAVES * UNROLL) {
         // this wave's fragment reads of its slots (previous blocks) are done
