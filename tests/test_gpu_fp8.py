@@ -78,11 +78,12 @@ def test_fp8_parity(dev, M, K, N):
     check_close(Y, ref, "fp8 %s" % ((M, K, N),))
 
 
-@pytest.mark.parametrize("name,M", [("qwen2.5-0.5B-prefill", 4096), ("qwen2.5-7B-decode", 128),
-                                    ("qwen2.5-7B-prefill", 8192)])
+@pytest.mark.parametrize("name,M", [(w.name, m) for w in inputs.WORKLOADS for m in w.ms],
+                         ids=["%s-M%d" % (w.name, m) for w in inputs.WORKLOADS for m in w.ms])
 def test_fp8_workload_shapes(dev, name, M):
-    """The workload's own tensors quantised per tensor; every element against
-    the oracle."""
+    """The workload's own tensors quantised per tensor, at every workload
+    point (decode kernel up to 32 rows, the tiny point's panel schedule, the
+    mixed prefill launch); every element against the oracle."""
     w = inputs.BY_NAME[name]
     A, W1, W2 = inputs.workload_tensors(w, M)
     A8, sa = inputs.quantize_e4m3(A)

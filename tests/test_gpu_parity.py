@@ -488,6 +488,25 @@ def test_interleaved_layout_matches(dev, M, K, N):
         assert np.array_equal(Yi, Yp), "interleaved != per-tile layout bitwise"
 
 
+@pytest.mark.parametrize("point", POINTS, ids=[_points_id(p) for p in POINTS])
+def test_interleaved_workload_shapes(dev, point):
+    """The interleaved-layout path at the workload points: every element
+    against the whole oracle output (the same inputs and cached result as
+    test_gaussian_workloads), and bitwise equal to the per-tile layout on the
+    same streaming schedule."""
+    w = inputs.WORKLOADS[point[0]]
+    M = point[1]
+    A, W1, W2 = inputs.workload_tensors(w, M)
+    Ad, W1d, W2d = A.to(dev), W1.to(dev), W2.to(dev)
+    say("[interleaved-workload] %s M=%d" % (w.name, M))
+    Yi = gpu_bits(sw.swiglu_fused_packed_interleaved(Ad, sw.swiglu_pack_weights_interleaved(W1d, W2d), w.N))
+    Yp = gpu_bits(sw.swiglu_fused_packed(Ad, sw.swiglu_pack_weights(W1d, W2d), w.N, variant=DP))
+    ref, _ = cached_oracle("gauss-%s-M%d" % (w.name, M), lambda: oracle.swiglu(A, W1, W2, want_p=True),
+                           want_p=True)
+    check_close_all(Yi, ref, "interleaved %s M=%d" % (w.name, M))
+    assert np.array_equal(Yi, Yp), "interleaved != per-tile layout bitwise"
+
+
 def test_split_workspace_reused_across_shapes(dev):
     """One workspace serves split-K calls of different shapes in a row, and
     its earlier contents (partials of another shape, or garbage) never leak
