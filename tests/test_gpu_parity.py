@@ -298,6 +298,35 @@ def test_edge_cases(dev):
     assert np.all((gpu_bits(Y) & 0x7FFF) == 0)
 
 
+@pytest.mark.parametrize("M,K,N", [
+    (16, 136, 520),       # decode schedule
+    (100, 136, 520),      # panel schedule
+    (300, 136, 1032),     # 128-row tiles
+    (2100, 72, 264),      # persistent 256-row tiles with the 128-row tail
+])
+def test_nonfinite_inputs(dev, M, K, N):
+    """IEEE special values pass through every schedule as the oracle's
+    definition gives them: a NaN activation makes its whole output row NaN;
+    +Inf in a row gives Gate and Up of +-Inf (SiLU(+Inf) = +Inf, and
+    SiLU(-Inf) = -Inf / Inf = NaN); an Inf weight does the same to its output
+    column.  The NaN pattern must match exactly, and finite and infinite values
+    as everywhere (the last activation K column, in the ragged block, too)."""
+    A, W1, W2 = inputs.gaussian_case(M, K, N, seed=M + 11 * K + N)
+    nan, inf = float("nan"), float("inf")
+    A[1, 5] = nan
+    A[2, 7] = inf
+    A[3, 9] = -inf
+    A[M - 1, K - 1] = nan
+    W1[3, 10] = inf
+    W2[K - 1, N - 2] = -inf
+    outs = run_all_variants(dev, A, W1, W2, "nonfinite")
+    ref = oracle.swiglu(A, W1, W2)
+    r = f32(ref)
+    assert np.isnan(r[1]).all() and np.isnan(r[M - 1]).all() and np.isinf(r[2]).any()
+    for name, y in outs.items():
+        check_close(y, ref, "nonfinite/%s %s" % (name, (M, K, N)))
+
+
 @pytest.mark.parametrize("M,K,N,auto_decode", [
     (1, 6144, 24576, True),    # long K, >= 192 column tiles: 8 column groups per workgroup
     (16, 3584, 4096, True),    # short K: one column group, 8 K blocks in flight, activations via LDS
