@@ -751,13 +751,19 @@ swiglu_status swiglu_fused(const swiglu_bf16* A, const swiglu_bf16* W1, const sw
     } else if (M <= 64) {
         a.tiles_m = 1; a.tiles_n = (int)ceil_div(N, 64);
         e = launch_tile<64, 64, 2, 1, true, false, false>(a, a.tiles_m * a.tiles_n, s);
-    } else if (M <= 512) {
-        // 128x64 tiles when 128x128 ones leave CUs idle and the 64-column grid
-        // fits one round or fills at least one and a half (72B-width M=128
-        // 298 -> 237 us, 0.5B-width 29.2 -> 22.9 us; the 7B width's 296 tiles
-        // of 64 columns, a round and a sixth, stay on 128 columns); 256-row
-        // tiles above 512 rows (7B-width M=2048 899 -> 631 us, 72B-width
-        // M=1024 1742 -> 1199 us)
+    } else if (M <= 512 && 4 * ceil_div(ceil_div(M, 256) * ceil_div(N, 128), (int64_t)cus) >=
+                               3 * ceil_div(ceil_div(M, 128) * ceil_div(N, 128), (int64_t)cus)) {
+        // 128-row tiles up to 512 rows unless 256-row ones need fewer rounds
+        // of workgroups over the CUs by more than their 4/3 cost per tile
+        // (7B-width M=192 177 -> 128 us, M=448 251 -> 242 us, 72B-width
+        // M=256 408 -> 336 us, M=512 780 -> 589 us; 7B-width M=300 and the
+        // 0.5B width up to 512 rows stay on 128 rows: 178 against 233 us and
+        // 15.3 against 29.4 us at M=256).  128x64 tiles when 128x128 ones
+        // leave CUs idle and the 64-column grid fits one round or fills at
+        // least one and a half (72B-width M=128 298 -> 237 us, 0.5B-width
+        // 29.2 -> 22.9 us; the 7B width's 296 tiles of 64 columns, a round
+        // and a sixth, stay on 128 columns); 256-row tiles above 512 rows
+        // (7B-width M=2048 899 -> 631 us, 72B-width M=1024 1742 -> 1199 us)
         a.tiles_m = (int)ceil_div(M, 128); a.tiles_n = (int)ceil_div(N, 128);
         const int64_t t64 = (int64_t)a.tiles_m * ceil_div(N, 64);
         if ((int64_t)a.tiles_m * a.tiles_n < cus && (t64 <= cus || 2 * t64 >= 3 * (int64_t)cus)) {

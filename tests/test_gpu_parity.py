@@ -375,13 +375,16 @@ def test_rowmajor_decode_widths(dev, M, K, grid):
     (128, 200, 9000),     # 71 tiles of 128 columns: 141 of 64 columns, one round
     (100, 136, 30000),    # 235 tiles of 128 columns: 469 of 64 columns; M tail
     (300, 72, 8200),      # 3 x 65 tiles of 128 columns: 3 x 129 = 387 of 64 columns
-    (130, 64, 18944),     # 2 x 148 tiles of 128 columns fill the CUs: stays on 128
+    (130, 64, 18944),     # 2 x 148 tiles of 128 columns: one round of 148 256-row tiles instead
+    (300, 136, 18944),    # 3 x 148 128-row tiles against 2 x 148 256-row ones: stays on 128 rows
+    (450, 200, 30000),    # 2 x 235 256-row tiles (two rounds) against 4 x 235 128-row ones (four)
 ])
 def test_rowmajor_prefill_tiles(dev, M, K, N):
-    """swiglu_fused for 64 < M <= 2048 on 128x64 tiles (when 128x128 tiles
+    """swiglu_fused for 64 < M <= 512 on 128x64 tiles (when 128x128 tiles
     leave CUs idle and the 64-column grid fits one round or fills one and a
-    half) and on 128x128 tiles; ragged K and N, every element against the
-    oracle."""
+    half), on 128x128 tiles, and on 256x128 tiles where they need fewer rounds
+    over the CUs by more than their 4/3 cost; ragged K and N, every element
+    against the oracle."""
     A, W1, W2 = inputs.gaussian_case(M, K, N, seed=3 * M + K + N)
     say("[rowmajor prefill] M=%d K=%d N=%d" % (M, K, N))
     Y = sw.swiglu_fused(A.to(dev), W1.to(dev), W2.to(dev))
