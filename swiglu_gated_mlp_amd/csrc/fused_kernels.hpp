@@ -1180,20 +1180,23 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
     };
     constexpr int LPS = LOADS / 4;                // loads per sub-step
     static_assert(LOADS % 4 == 0, "loads split over four sub-steps");
-    constexpr int LPI = (LPS + TM - 1) / TM;      // loads per 32-row step
     constexpr int RPI = TM >= 2 ? 2 : 1;          // next-sub-step reads per step
     // One 16-deep sub-step on fragment set CUR, in a fixed order (each step
     // fenced): for each 32-row tile, its Gate and Up MFMAs, then the next
     // sub-step's fragments (RD: from slot offset rso, sub-step rkk; two per
-    // step, so they are all issued in the first half), then (LD) LPI loads of
-    // stage ls.  The reads go to the other fragment set, so any wait for
+    // step, so they are all issued in the first half), then (LD) its share of
+    // the sub-step's loads of stage ls (LPS of them, or all LOADS with ALL).
+    // The reads go to the other fragment set, so any wait for
     // them lands at the start of the next sub-step, long after they were
     // issued.
     auto substep = [&](auto wsetc, int kk, int cur, auto rdc, uint32_t rso, int rkk, auto ldc, int ls, int lbuf,
-                       auto lsetc, int lq) {
+                       auto lsetc, int lq, auto allc) {
         constexpr int WS = decltype(wsetc)::value;
         constexpr bool RD = decltype(rdc)::value;
         constexpr bool LD = decltype(ldc)::value;
+        constexpr bool ALL = decltype(allc)::value;   // all LOADS loads of the stage in this sub-step
+        constexpr int NLD = ALL ? LOADS : LPS;
+        constexpr int LPIX = (NLD + TM - 1) / TM;
         // this sub-step's fragments were all read during the first half of
         // the previous one: wait for them here, before any new read, so no
         // later wait in this sub-step has to cover the new reads
@@ -1238,8 +1241,8 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
             }
             if constexpr (LD) {
 #pragma unroll
-                for (int j = i * LPI; j < (i + 1) * LPI; ++j)
-                    if (j < LPS) issue_one(lq * LPS + j, ls, lbuf, lsetc);
+                for (int j = i * LPIX; j < (i + 1) * LPIX; ++j)
+                    if (j < NLD) issue_one(ALL ? j : lq * LPS + j, ls, lbuf, lsetc);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1250,7 +1253,11 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
     // One 64-deep stage s in ring slot / register set P = s % 3: issues
     // stage s+2's loads (slot and set (P+2) % 3, freed by the previous
     // stage's barrier), LPS per sub-step, and reads stage s+1's first
-    // fragments during its last sub-step.
+    // fragments during its last sub-step.  The single-weight GEMM's panel
+    // schedule (one accumulator set, half-panels) issues all of them in the
+    // first sub-step instead (7B-width M=128 GEMM 43.8 -> 39.8 us, M=64
+    // 42.0 -> 34.9 us, 0.5B-width M=128 12.5 -> 11.1 us; the fused product's
+    // panels were slower that way, 7B-width M=128 56.7 -> 58.5 us).
     auto stage = [&](auto pc, int s) {
         constexpr int P = decltype(pc)::value;
         constexpr int PN = (P + 1) % NBUF, PL = (P + 2) % NBUF;
@@ -1258,18 +1265,22 @@ __device__ __forceinline__ void stream_prefill_tiles(const FusedArgs& p, uint16_
         using WL = std::integral_constant<int, PL>;
         const uint32_t so = slot_off(P);
         __builtin_amdgcn_sched_barrier(0);
-        substep(WP{}, 0, 0, T{}, so, 1, T{}, s + 2, PL, WL{}, 0);
-        substep(WP{}, 1, 1, T{}, so, 2, T{}, s + 2, PL, WL{}, 1);
-        substep(WP{}, 2, 0, T{}, so, 3, T{}, s + 2, PL, WL{}, 2);
+        constexpr bool EARLY = PANELS && GEMM && !F8;
+        using EA = std::integral_constant<bool, EARLY>;
+        using LR = std::integral_constant<bool, !EARLY>;
+        substep(WP{}, 0, 0, T{}, so, 1, T{}, s + 2, PL, WL{}, 0, EA{});
+        substep(WP{}, 1, 1, T{}, so, 2, LR{}, s + 2, PL, WL{}, 1, F{});
+        substep(WP{}, 2, 0, T{}, so, 3, LR{}, s + 2, PL, WL{}, 2, F{});
         const uint32_t son = slot_off(PN);
         // stage s+1 (activations and this wave's weights) has landed once at
-        // most the 3*LPS loads of stage s+2 issued so far are in flight (every
-        // stage issues all LOADS loads, also past the end: see below); after
-        // the barrier every wave is done reading slot P
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * LPS, 0));
+        // most the loads of stage s+2 issued so far (3*LPS, or all LOADS when
+        // EARLY) are in flight (every stage issues all LOADS loads, also past
+        // the end: see below); after the barrier every wave is done reading
+        // slot P
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(EARLY ? LOADS : 3 * LPS, 0));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        substep(WP{}, 3, 1, T{}, son, 0, T{}, s + 2, PL, WL{}, 3);
+        substep(WP{}, 3, 1, T{}, son, 0, LR{}, s + 2, PL, WL{}, 3, F{});
         __builtin_amdgcn_sched_barrier(0);
     };
 
