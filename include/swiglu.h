@@ -137,7 +137,11 @@ int swiglu_device_cu_count(void);
  *   A  [M,K] bf16, W1 [K,N] bf16, W2 [K,N] bf16 (inputs, device)
  *   Y  [M,N] bf16 (output, device; must not overlap A, W1, W2)
  * Needs no workspace; always uses the data-parallel schedule.  The weights are
- * transposed to K-contiguous order on the fly, tile by tile, in registers.
+ * transposed to K-contiguous order on the fly, tile by tile: their tiles are
+ * loaded into LDS as they lie in memory and the transposing LDS read forms
+ * the matrix-core fragments (for 32 < M <= 64 on products wider than the CU
+ * count allows in 32-column workgroups, a tile kernel transposes them in
+ * registers instead).
  * ---------------------------------------------------------------------- */
 swiglu_status swiglu_fused(const swiglu_bf16 *A, const swiglu_bf16 *W1,
                            const swiglu_bf16 *W2, swiglu_bf16 *Y, int64_t M,
